@@ -1,0 +1,37 @@
+"""Every planted mistake in the oracle is caught by at least one pin.
+
+Each ORC_MUTATE value in oracle/gqa_oracle.c plants one plausible mistake
+(a wrong KV-head index, a dropped scale, a flipped RoPE sign, a strict `own`
+comparison, an off-by-one window, a scaled sink, a strict `seen`, a swapped
+page index, a wrong inv_freq denominator, truncating rounding). The oracle is
+rebuilt with each one into a temporary directory; the pins must reject it.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+from tests import oracle_pins
+
+MUTATIONS = {
+    1: "kv head h % KvHeads instead of floor(h / G)",
+    2: "softmax scale dropped",
+    3: "rope sign flipped in the low half",
+    4: "own mask strict (<) on positions",
+    5: "window keeps W + 1 keys",
+    6: "sink multiplied by the scale",
+    7: "decode seen strict (<)",
+    8: "paged page/offset swapped",
+    9: "inv_freq uses D/2 in the exponent",
+    10: "rounding truncates",
+}
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_mutation_is_caught(tmp_path, mutation):
+    lib = obuild.build(str(tmp_path / f"liboracle_m{mutation}.so"), mutation=mutation)
+    o = oracle.Oracle(lib)
+    assert o.mutation() == mutation
+    bad = oracle_pins.failing_pins(o)
+    assert bad, f"mutation {mutation} ({MUTATIONS[mutation]}) passed every pin"
