@@ -1,0 +1,127 @@
+// Device-side helpers shared by the gfx950 kernels of the attention library:
+// bf16 <-> f32 conversion, exact rounding of fp64 results to T, wavefront
+// shuffles, and the MFMA operand vector types. Nothing here is visible
+// through the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPageSize = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// bf16 storage is raw 16-bit patterns (uint16_t); arithmetic is f32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// f32 -> bf16, nearest-even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// fp64 -> f32 with round-to-odd: truncate toward zero, then force the last
+// bit to 1 when inexact. A second rounding of that value to any format with
+// at most 22 significant bits (bf16 has 8) is then the correctly rounded
+// (nearest-even) result of the original fp64 value.
+__device__ __forceinline__ float f64_to_f32_round_odd(double x) {
+  float f = (float)x;
+  double back = (double)f;
+  if (back != x && !__builtin_isnan(x)) {
+    uint32_t u = __float_as_uint(f);
+    if (__builtin_fabs(back) > __builtin_fabs(x)) u -= 1u;  // step toward zero
+    u |= 1u;
+    f = __uint_as_float(u);
+  }
+  return f;
+}
+
+// fp64 -> bf16, nearest-even, exactly (single rounding).
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  return f32_to_bf16(f64_to_f32_round_odd(x));
+}
+
+// ---------------------------------------------------------------------------
+// Element traits: 16-byte vectors of T and their f32 view.
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<uint16_t> {  // bf16
+  static constexpr int kPer16B = 8;
+  __device__ __forceinline__ static void to_f32(const u32x4& w, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = bf16_lo(w[i]);
+      out[2 * i + 1] = bf16_hi(w[i]);
+    }
+  }
+  __device__ __forceinline__ static float load1(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static void store1(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+template <>
+struct Elem<float> {
+  static constexpr int kPer16B = 4;
+  __device__ __forceinline__ static void to_f32(const u32x4& w, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+  }
+  __device__ __forceinline__ static float load1(const float* p) { return *p; }
+  __device__ __forceinline__ static void store1(float* p, float v) { *p = v; }
+};
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store16(void* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront (64-lane) reductions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Key range [lo, hi] a decode query at `pos` attends in a cache of `cap`
+// logical slots: seen = slot <= pos, window W > 0 keeps pos - slot < W.
+// Empty when hi < lo.
+__device__ __forceinline__ void decode_key_range(int pos, int cap, int window, int& lo,
+                                                 int& hi) {
+  hi = pos < cap - 1 ? pos : cap - 1;
+  long long l = 0;
+  if (window > 0) {
+    long long w0 = (long long)pos - (long long)window + 1;
+    l = w0 > 0 ? w0 : 0;
+  }
+  lo = (int)(l < (long long)cap ? l : (long long)cap);
+}
+
+}  // namespace gqa

@@ -1,0 +1,280 @@
+// C ABI of the attention library: host-side validation (the `where` clause of
+// the GroupedQueryAttention block on the Linnet "examples/01-llama" page,
+// plus what this build supports) and dispatch to the kernel launchers. No
+// C++ exception crosses this boundary; nothing here allocates or
+// synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+
+#include "gqa.h"
+#include "internal.h"
+
+namespace {
+
+std::atomic<int32_t> g_dry_run{0};
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool supported_dim(int32_t d) { return d == 64 || d == 128; }
+bool valid_dtype(int32_t t) { return t == GQA_BF16 || t == GQA_F32; }
+
+// where Heads > 0, KvHeads > 0, Heads % KvHeads == 0, (H / Heads) % 2 == 0.
+int check_heads(int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype) {
+  if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0) return GQA_ERR_INVALID_ARG;
+  if (head_dim <= 0 || head_dim % 2 != 0) return GQA_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return GQA_ERR_INVALID_ARG;
+  if (!supported_dim(head_dim)) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+float effective_scale_log2(float scale, int32_t head_dim) {
+  // rsqrt(cast<f32>(H / Heads)) as the correctly rounded f32 value.
+  const float s = scale != 0.0f ? scale : (float)(1.0 / std::sqrt((double)head_dim));
+  return s * kLog2e;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t gqa_abi_version(void) { return 1; }
+
+int32_t gqa_set_dry_run(int32_t on) { return g_dry_run.exchange(on ? 1 : 0); }
+
+const char* gqa_status_string(int32_t status) {
+  switch (status) {
+    case GQA_OK:
+      return "ok";
+    case GQA_ERR_INVALID_ARG:
+      return "invalid argument";
+    case GQA_ERR_UNSUPPORTED:
+      return "unsupported dtype / head dim / operation";
+    case GQA_ERR_WORKSPACE:
+      return "workspace missing or too small";
+    case GQA_ERR_HIP:
+      return "HIP runtime error";
+    default:
+      return "unknown status";
+  }
+}
+
+int gqa_rope_table(int32_t head_dim, int32_t max_pos, float theta, int32_t dtype, void* table,
+                   void* stream) {
+  if (head_dim <= 0 || head_dim % 2 != 0 || max_pos <= 0 || !valid_dtype(dtype))
+    return GQA_ERR_INVALID_ARG;
+  if (!(theta > 0.0f) || !std::isfinite(theta)) return GQA_ERR_INVALID_ARG;
+  if (table == nullptr) return GQA_ERR_INVALID_ARG;
+  if (!supported_dim(head_dim)) return GQA_ERR_UNSUPPORTED;
+  if (g_dry_run.load()) return GQA_OK;
+  return hip_status(gqa::launch_rope_table(head_dim, max_pos, theta, dtype, table,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int gqa_rope_write_kv(int32_t n, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                      int32_t dtype, void* q, void* k, const void* v,
+                      const int32_t* positions, const void* rope_table, int32_t rope_max_pos,
+                      int32_t cache_kind, void* cache_k, void* cache_v, int32_t cache_dim0,
+                      int32_t cache_seq, const int32_t* rows, const int32_t* slots,
+                      const int32_t* table, int32_t table_rows, int32_t table_pages,
+                      void* stream) {
+  if (n < 0) return GQA_ERR_INVALID_ARG;
+  int st = check_heads(heads, kv_heads, head_dim, dtype);
+  if (st != GQA_OK) return st;
+  if (cache_kind < GQA_CACHE_NONE || cache_kind > GQA_CACHE_PAGED_SLOTS) return GQA_ERR_INVALID_ARG;
+  if (rope_table != nullptr && rope_max_pos <= 0) return GQA_ERR_INVALID_ARG;
+  const bool needs_pos = rope_table != nullptr || cache_kind == GQA_CACHE_CONTIGUOUS ||
+                         cache_kind == GQA_CACHE_PAGED_TABLE;
+  if (needs_pos && positions == nullptr) return GQA_ERR_INVALID_ARG;
+  if (cache_kind != GQA_CACHE_NONE) {
+    if (k == nullptr || cache_k == nullptr) return GQA_ERR_INVALID_ARG;
+    if (v != nullptr && cache_v == nullptr) return GQA_ERR_INVALID_ARG;
+    if (cache_dim0 <= 0) return GQA_ERR_INVALID_ARG;
+    if (cache_kind == GQA_CACHE_CONTIGUOUS && cache_seq <= 0) return GQA_ERR_INVALID_ARG;
+    if (cache_kind != GQA_CACHE_CONTIGUOUS && cache_seq != GQA_PAGE_SIZE)
+      return GQA_ERR_INVALID_ARG;
+    if (cache_kind == GQA_CACHE_PAGED_TABLE &&
+        (table == nullptr || table_rows <= 0 || table_pages <= 0))
+      return GQA_ERR_INVALID_ARG;
+    if (cache_kind == GQA_CACHE_PAGED_SLOTS && slots == nullptr) return GQA_ERR_INVALID_ARG;
+  } else if (rope_table == nullptr || (q == nullptr && k == nullptr)) {
+    return GQA_ERR_INVALID_ARG;  // nothing to do is a caller error
+  }
+  if (n == 0 || g_dry_run.load()) return GQA_OK;
+  gqa::RopeWriteArgs a;
+  a.n = n;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.head_dim = head_dim;
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.positions = positions;
+  a.rope_table = rope_table;
+  a.rope_max_pos = rope_max_pos;
+  a.cache_kind = cache_kind;
+  a.cache_k = cache_k;
+  a.cache_v = cache_v;
+  a.cache_dim0 = cache_dim0;
+  a.cache_seq = cache_seq;
+  a.rows = rows;
+  a.slots = slots;
+  a.table = table;
+  a.table_rows = table_rows;
+  a.table_pages = table_pages;
+  return hip_status(gqa::launch_rope_write(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t gqa_prefill_packed_workspace(int32_t p, int32_t heads, int32_t kv_heads,
+                                    int32_t head_dim) {
+  if (p <= 0) return 0;
+  return gqa::prefill_workspace_bytes(p, heads, kv_heads, head_dim);
+}
+
+int gqa_prefill_packed(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                       int32_t dtype, float scale, int32_t window, const void* sinks,
+                       const void* q, const void* k, const void* v,
+                       const int32_t* positions, const int32_t* segments, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (p < 0 || window < 0) return GQA_ERR_INVALID_ARG;
+  int st = check_heads(heads, kv_heads, head_dim, dtype);
+  if (st != GQA_OK) return st;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (q == nullptr || k == nullptr || v == nullptr || positions == nullptr ||
+      segments == nullptr || out == nullptr)
+    return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  if (p == 0) return GQA_OK;
+  const size_t need = gqa::prefill_workspace_bytes(p, heads, kv_heads, head_dim);
+  if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GQA_ERR_WORKSPACE;
+  if (g_dry_run.load()) return GQA_OK;
+  gqa::PrefillArgs a;
+  a.p = p;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.head_dim = head_dim;
+  a.dtype = dtype;
+  a.scale_log2 = effective_scale_log2(scale, head_dim);
+  a.window = window;
+  a.sinks = sinks;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.positions = positions;
+  a.segments = segments;
+  a.out = out;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  return hip_status(gqa::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+static size_t decode_ws(int rows, int heads, int kv_heads, int head_dim, int dtype, int paged,
+                        int cap) {
+  size_t ws = 0;
+  gqa::decode_plan(rows, heads, kv_heads, head_dim, dtype, paged, cap, nullptr, nullptr, &ws);
+  return ws;
+}
+
+size_t gqa_decode_rows_workspace(int32_t batch, int32_t heads, int32_t kv_heads,
+                                 int32_t head_dim, int32_t max_seq) {
+  if (batch <= 0 || heads <= 0 || max_seq <= 0) return 0;
+  // The plan does not depend on dtype for the contiguous cache.
+  return decode_ws(batch, heads, kv_heads, head_dim, GQA_F32, 0, max_seq);
+}
+
+size_t gqa_decode_paged_workspace(int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
+                                  int32_t head_dim) {
+  if (rows <= 0 || pages <= 0 || heads <= 0) return 0;
+  if ((long long)pages * GQA_PAGE_SIZE > 0x7fffffffLL) return 0;
+  const size_t a = decode_ws(rows, heads, kv_heads, head_dim, GQA_BF16, 1, pages * GQA_PAGE_SIZE);
+  const size_t b = decode_ws(rows, heads, kv_heads, head_dim, GQA_F32, 1, pages * GQA_PAGE_SIZE);
+  return a > b ? a : b;
+}
+
+static int decode_common(gqa::DecodeArgs& a, size_t workspace_bytes, void* workspace,
+                         hipStream_t stream) {
+  const size_t need =
+      decode_ws(a.rows, a.heads, a.kv_heads, a.head_dim, a.dtype, a.paged, a.cap);
+  if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GQA_ERR_WORKSPACE;
+  if (g_dry_run.load()) return GQA_OK;
+  a.ws = static_cast<float*>(workspace);
+  return hip_status(gqa::launch_decode(a, stream));
+}
+
+int gqa_decode_rows(int32_t batch, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                    int32_t dtype, float scale, int32_t window, const void* sinks,
+                    const void* q, const void* cache_k, const void* cache_v, int32_t max_seq,
+                    const int32_t* positions, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (batch < 0 || window < 0 || max_seq <= 0) return GQA_ERR_INVALID_ARG;
+  int st = check_heads(heads, kv_heads, head_dim, dtype);
+  if (st != GQA_OK) return st;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (q == nullptr || cache_k == nullptr || cache_v == nullptr || positions == nullptr ||
+      out == nullptr)
+    return GQA_ERR_INVALID_ARG;
+  if (batch == 0) return GQA_OK;
+  gqa::DecodeArgs a{};
+  a.rows = batch;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.head_dim = head_dim;
+  a.dtype = dtype;
+  a.scale_log2 = effective_scale_log2(scale, head_dim);
+  a.window = window;
+  a.sinks = sinks;
+  a.q = q;
+  a.k = cache_k;
+  a.v = cache_v;
+  a.positions = positions;
+  a.table = nullptr;
+  a.paged = 0;
+  a.cap = max_seq;
+  a.pages = 0;
+  a.num_pages = 0;
+  a.out = out;
+  return decode_common(a, workspace_bytes, workspace, static_cast<hipStream_t>(stream));
+}
+
+int gqa_decode_paged(int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
+                     int32_t head_dim, int32_t dtype, float scale, int32_t window,
+                     const void* sinks, const void* q, const void* pool_k, const void* pool_v,
+                     int32_t num_pages, const int32_t* positions, const int32_t* table,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 0 || pages <= 0 || num_pages <= 0 || window < 0) return GQA_ERR_INVALID_ARG;
+  if ((long long)pages * GQA_PAGE_SIZE > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
+  int st = check_heads(heads, kv_heads, head_dim, dtype);
+  if (st != GQA_OK) return st;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (q == nullptr || pool_k == nullptr || pool_v == nullptr || positions == nullptr ||
+      table == nullptr || out == nullptr)
+    return GQA_ERR_INVALID_ARG;
+  if (rows == 0) return GQA_OK;
+  gqa::DecodeArgs a{};
+  a.rows = rows;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.head_dim = head_dim;
+  a.dtype = dtype;
+  a.scale_log2 = effective_scale_log2(scale, head_dim);
+  a.window = window;
+  a.sinks = sinks;
+  a.q = q;
+  a.k = pool_k;
+  a.v = pool_v;
+  a.positions = positions;
+  a.table = table;
+  a.paged = 1;
+  a.cap = pages * GQA_PAGE_SIZE;
+  a.pages = pages;
+  a.num_pages = num_pages;
+  a.out = out;
+  return decode_common(a, workspace_bytes, workspace, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Launcher interface between the C ABI (gqa_api.cpp) and the kernels. Host
+// code only: argument structs passed by value to kernels, and the launchers
+// each kernel file provides. All pointers are device pointers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqa {
+
+constexpr int kDtypeBf16 = 0;
+constexpr int kDtypeF32 = 1;
+
+struct RopeWriteArgs {
+  int n, heads, kv_heads, head_dim, dtype;
+  void* q;
+  void* k;
+  const void* v;
+  const int32_t* positions;
+  const void* rope_table;
+  int rope_max_pos;
+  int cache_kind;  // 0 none, 1 contiguous, 2 paged table, 3 paged slots
+  void* cache_k;
+  void* cache_v;
+  int cache_dim0;  // batch (contiguous) or num_pages (paged)
+  int cache_seq;   // max_seq (contiguous) or page size (paged)
+  const int32_t* rows;
+  const int32_t* slots;
+  const int32_t* table;
+  int table_rows, table_pages;
+};
+
+// One decode call, contiguous or paged.
+struct DecodeArgs {
+  int rows;          // batch rows / table rows
+  int heads, kv_heads, head_dim, dtype;
+  float scale_log2;  // scale * log2(e)
+  int window;
+  const void* sinks;  // [heads] of T or null
+  const void* q;      // [rows, heads, D]
+  const void* k;      // contiguous [rows, kvh, cap, D] or pool [num_pages, kvh, 64, D]
+  const void* v;
+  const int32_t* positions;  // [rows]
+  const int32_t* table;      // [rows, pages] or null (contiguous)
+  int paged;
+  int cap;        // max_seq (contiguous) or pages * 64 (paged)
+  int pages;      // table width (paged)
+  int num_pages;  // pool size (paged)
+  void* out;      // [rows, heads, D]
+  float* ws;      // split partials
+  int split_len;  // tokens per split
+  int nsplit;     // splits per row
+};
+
+struct PrefillArgs {
+  int p, heads, kv_heads, head_dim, dtype;
+  float scale_log2;
+  int window;
+  const void* sinks;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* positions;
+  const int32_t* segments;
+  void* out;
+  void* ws;
+  size_t ws_bytes;
+};
+
+hipError_t launch_rope_table(int head_dim, int max_pos, float theta, int dtype, void* table,
+                             hipStream_t stream);
+hipError_t launch_rope_write(const RopeWriteArgs& a, hipStream_t stream);
+
+// Decode: split length / split count the launcher will use, the workspace
+// bytes that needs, and the launch itself.
+void decode_plan(int rows, int heads, int kv_heads, int head_dim, int dtype, int paged, int cap,
+                 int* split_len, int* nsplit, size_t* ws_bytes);
+hipError_t launch_decode(DecodeArgs a, hipStream_t stream);
+
+size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace gqa

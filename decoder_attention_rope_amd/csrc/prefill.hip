@@ -1,0 +1,462 @@
+// Packed prefill attention on bf16 matrix cores (gfx950).
+//
+// `packed<P>` of the Linnet "examples/01-llama" page (src/attention.linnet)
+// lets token i attend key j iff own[i, j] = segments[i] == segments[j] &&
+// positions[j] <= positions[i]; prefill_packed of the Nest
+// llama-3.1-8b-instruct card uses the same mask, and SinkAttention of the
+// Nest gpt-oss-20b card adds a window and a per-head sink logit.
+//
+// Design (flash-style, one pass over the keys, online softmax):
+// * A workgroup owns one KV head and a tile of queries: 4 wavefronts, each
+//   with 32 query tokens of one query head. With G = Heads / KvHeads >= 4 the
+//   four waves are four query heads of the group over the same 32 tokens, so
+//   every K/V tile staged in LDS serves four heads.
+// * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//   K rows (keys) are the A operand read from LDS, Q^T the B operand held in
+//   registers. In the 32x32 accumulator layout a lane owns one query column,
+//   so the softmax max/sum of a query needs one cross-lane exchange (lanes l
+//   and l ^ 32) per tile.
+// * The key order inside a 32-key block is permuted (bits 2 and 3 of the row
+//   index swapped) so that the probabilities a lane holds after the softmax
+//   are exactly the B operand of the P.V product O^T = V^T P^T; no data moves
+//   between lanes. V is written to LDS transposed (dimension-major, XOR
+//   swizzled) while it is staged, so the A operand V^T is one 16-byte LDS
+//   read per lane.
+// * K/V tiles of 64 keys are double-buffered in LDS: the global loads of the
+//   next tile are in flight while the current tile is on the matrix cores.
+// * Tiles that cannot hold an allowed key are skipped using per-tile
+//   [min, max] summaries of segments and positions; tiles in which every pair
+//   is allowed skip the per-element mask. The exact `own` predicate is
+//   evaluated everywhere else, so any segment order or id is handled.
+// * A single-workgroup prep kernel computes the summaries, each query tile's
+//   visited key-tile range and its cost, and orders the query tiles longest
+//   first; workgroup index i * n_groups + g maps KV head g to the
+//   round-robin XCD g % 8, keeping one head's K/V in one XCD's L2.
+#include "common.h"
+#include "internal.h"
+
+namespace gqa {
+
+namespace {
+constexpr int kBK = 64;       // keys per tile
+constexpr int kPrepThreads = 1024;
+constexpr int kSortMax = 4096;  // query tiles sorted by cost in LDS
+constexpr float kNegInf = -__builtin_huge_valf();
+
+struct TileSum {
+  int seg_min, seg_max, pos_min, pos_max;
+};
+
+struct Plan {
+  TileSum* ksum;  // [n_kt]
+  TileSum* qsum;  // [n_qt]
+  int2* qrange;   // [n_qt] first / last key tile to visit
+  int* order;     // [n_qt] query tiles, costliest first
+  int n_kt, n_qt, tq, head_groups, gw;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__device__ __forceinline__ bool tiles_meet(const TileSum& q, const TileSum& k, int window) {
+  if (k.seg_max < q.seg_min || k.seg_min > q.seg_max) return false;
+  if (k.pos_min > q.pos_max) return false;
+  if (window > 0 && (long long)q.pos_min - (long long)k.pos_max >= window) return false;
+  return true;
+}
+
+__device__ __forceinline__ TileSum summarize(const int32_t* pos, const int32_t* seg, int lo, int hi) {
+  TileSum s{0x7fffffff, (int)0x80000000, 0x7fffffff, (int)0x80000000};
+  for (int t = lo; t < hi; ++t) {
+    const int sg = seg[t], ps = pos[t];
+    s.seg_min = min(s.seg_min, sg);
+    s.seg_max = max(s.seg_max, sg);
+    s.pos_min = min(s.pos_min, ps);
+    s.pos_max = max(s.pos_max, ps);
+  }
+  return s;
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Prep: summaries, visited ranges, longest-first order (one workgroup).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(PrefillArgs a, Plan pl) {
+  __shared__ int cost[kSortMax];
+  __shared__ int idx[kSortMax];
+  const int tid = threadIdx.x;
+  for (int kt = tid; kt < pl.n_kt; kt += kPrepThreads)
+    pl.ksum[kt] = summarize(a.positions, a.segments, kt * kBK, min(a.p, (kt + 1) * kBK));
+  for (int qt = tid; qt < pl.n_qt; qt += kPrepThreads)
+    pl.qsum[qt] = summarize(a.positions, a.segments, qt * pl.tq, min(a.p, (qt + 1) * pl.tq));
+  __syncthreads();
+  const bool sort = pl.n_qt <= kSortMax;
+  for (int qt = tid; qt < pl.n_qt; qt += kPrepThreads) {
+    const TileSum q = pl.qsum[qt];
+    int first = pl.n_kt, last = -1, cnt = 0;
+    for (int kt = 0; kt < pl.n_kt; ++kt) {
+      if (tiles_meet(q, pl.ksum[kt], a.window)) {
+        first = min(first, kt);
+        last = kt;
+        ++cnt;
+      }
+    }
+    pl.qrange[qt] = make_int2(first, last);
+    if (sort) {
+      cost[qt] = cnt;
+      idx[qt] = qt;
+    } else {
+      pl.order[qt] = qt;
+    }
+  }
+  if (!sort) return;
+  int n2 = 1;
+  while (n2 < pl.n_qt) n2 <<= 1;
+  for (int i = pl.n_qt + tid; i < n2; i += kPrepThreads) {
+    cost[i] = -1;
+    idx[i] = 0x7fffffff;
+  }
+  __syncthreads();
+  // Bitonic sort: cost descending, then tile index ascending.
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < n2; i += kPrepThreads) {
+        const int l = i ^ j;
+        if (l > i) {
+          const bool desc = (i & k) == 0;
+          const int ci = cost[i], cl = cost[l];
+          const bool i_before_l = ci > cl || (ci == cl && idx[i] < idx[l]);
+          if (desc != i_before_l) {
+            cost[i] = cl;
+            cost[l] = ci;
+            const int t = idx[i];
+            idx[i] = idx[l];
+            idx[l] = t;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < pl.n_qt; i += kPrepThreads) pl.order[i] = idx[i];
+}
+
+// ---------------------------------------------------------------------------
+// LDS layouts.
+//   K tile  [64 keys][D]: 16-byte granule g of row r stored at granule
+//           g ^ swk(r); the 8 rows a group of 8 lanes reads at once land in
+//           8 distinct bank groups.
+//   V^T tile [D][64 keys]: granule g (8 keys) of row d stored at g ^ swv(d).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swk(int row) { return (row & 3) | ((row >> 1) & 4); }
+__device__ __forceinline__ int swv(int d) { return (d + (d >> 3)) & 7; }
+// Key row feeding accumulator row m of a 32-key block: bits 2 and 3 swapped.
+__device__ __forceinline__ int kappa(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+template <int D, int GW>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl) {
+  constexpr int SUB = 4 / GW;   // query sub-tiles of 32 per workgroup
+  constexpr int TQ = 32 * SUB;  // query tokens per workgroup
+  constexpr int KS = D / 16;    // k-steps of QK^T over the head dim
+  constexpr int MD = D / 32;    // 32-row blocks of O^T
+  constexpr int LPR = D / 8;    // staging threads per key row (16 B each)
+  constexpr int RPT = D / 32;   // key rows staged per thread
+  static_assert(LPR * (kBK / RPT) == 256, "staging covers the tile");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * kBK];
+  __shared__ __attribute__((aligned(16))) int sPos[2][kBK];
+  __shared__ __attribute__((aligned(16))) int sSeg[2][kBK];
+
+  const int G = a.heads / a.kv_heads;
+  const int n_groups = a.kv_heads * pl.head_groups;
+  const int wi = blockIdx.x / n_groups;
+  const int grp = blockIdx.x % n_groups;
+  const int kh = grp / pl.head_groups;
+  const int hg = grp % pl.head_groups;
+  const int qt = pl.order[wi];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hl = wave % GW;
+  const int st = wave / GW;
+  const int h = kh * G + hg * GW + hl;
+  const int qn = lane & 31;
+  const int hf = lane >> 5;
+  const int P = a.p;
+  const int q_tok = qt * TQ + st * 32 + qn;
+  const bool q_valid = q_tok < P;
+  const int my_pos = q_valid ? a.positions[q_tok] : 0;
+  const int my_seg = q_valid ? a.segments[q_tok] : 0;
+  const int window = a.window;
+
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k);
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v);
+
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (q_valid) w = load16(qg + ((long long)q_tok * a.heads + h) * D + ks * 16 + hf * 8);
+    qf[ks] = __builtin_bit_cast(bf16x8, w);
+  }
+
+  f32x16 o[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[md][r] = 0.f;
+  float m_run = kNegInf;
+  float l_run = 0.f;
+
+  const int2 rng = pl.qrange[qt];
+  const TileSum qs = pl.qsum[qt];
+
+  // Staging of one K/V tile: thread (c, ar) loads 16-byte chunk c of key rows
+  // ar * RPT .. ar * RPT + RPT - 1 (LPR threads cover a row, so a wavefront
+  // reads whole rows).
+  const int sc_c = tid % LPR;
+  const int sc_a = tid / LPR;
+  u32x4 kreg[RPT], vreg[RPT];
+  int pos_reg = 0, seg_reg = 0;
+
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int key = kt * kBK + sc_a * RPT + i;
+      if (key < P) {
+        const long long off = ((long long)key * a.kv_heads + kh) * D + sc_c * 8;
+        kreg[i] = load16(kg + off);
+        vreg[i] = load16(vg + off);
+      } else {
+        kreg[i] = u32x4{0u, 0u, 0u, 0u};
+        vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (tid < kBK) {
+      const int key = kt * kBK + tid;
+      pos_reg = key < P ? a.positions[key] : 0;
+      seg_reg = key < P ? a.segments[key] : 0;
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    uint16_t* k_s = sK[buf];
+    uint16_t* v_s = sV[buf];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = sc_a * RPT + i;
+      store16(k_s + row * D + ((sc_c ^ swk(row)) * 8), kreg[i]);
+    }
+    const int key0 = sc_a * RPT;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = sc_c * 8 + e;
+      const int w = e >> 1;
+      const int sh = (e & 1) * 16;
+      uint16_t* dst = v_s + d * kBK + ((((key0 >> 3) ^ swv(d)) << 3) | (key0 & 7));
+      if (RPT == 4) {
+        u32x2 pk;
+        pk[0] = ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[1 % RPT][w] >> sh) & 0xffffu) << 16);
+        pk[1] = ((vreg[2 % RPT][w] >> sh) & 0xffffu) | (((vreg[3 % RPT][w] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<u32x2*>(dst) = pk;
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) =
+            ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[1 % RPT][w] >> sh) & 0xffffu) << 16);
+      }
+    }
+    if (tid < kBK) {
+      sPos[buf][tid] = pos_reg;
+      sSeg[buf][tid] = seg_reg;
+    }
+  };
+
+  auto visit = [&](int kt) { return tiles_meet(qs, pl.ksum[kt], window); };
+  auto next_visit = [&](int kt) {
+    while (kt <= rng.y && !visit(kt)) ++kt;
+    return kt;
+  };
+
+  // QK^T, mask, online-softmax update; leaves the bf16 probabilities in pw
+  // (the B operand of the P.V product) and rescales the O accumulator.
+  u32x4 pw[4];
+  auto qk_softmax = [&](int buf, int kt) {
+    const TileSum ks_ = pl.ksum[kt];
+    const bool full = (kt + 1) * kBK <= P && qs.seg_min == qs.seg_max &&
+                      ks_.seg_min == ks_.seg_max && ks_.seg_min == qs.seg_min &&
+                      ks_.pos_max <= qs.pos_min &&
+                      (window <= 0 || (long long)qs.pos_max - (long long)ks_.pos_min < window);
+    const uint16_t* k_s = sK[buf];
+    f32x16 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
+      const int row = kappa(qn) + 32 * mb;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(
+            k_s + row * D + (((2 * ks + hf) ^ swk(row)) * 8));
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], s[mb], 0, 0, 0);
+      }
+    }
+    if (!full) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = 32 * mb + 16 * (r >> 3) + 8 * hf + (r & 7);
+          const int kp = sPos[buf][j];
+          const bool ok = kt * kBK + j < P && sSeg[buf][j] == my_seg && kp <= my_pos &&
+                          (window <= 0 || (uint32_t)my_pos - (uint32_t)kp < (uint32_t)window);
+          if (!ok) s[mb][r] = kNegInf;
+        }
+      }
+    }
+    float tmax = kNegInf;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[mb][r] *= a.scale_log2;
+        tmax = fmaxf(tmax, s[mb][r]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = exp2f(s[mb][r] - m_use);
+        const float p1 = exp2f(s[mb][r + 1] - m_use);
+        psum += p0 + p1;
+        pw[2 * mb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
+  };
+
+  // O^T += V^T P^T over the tile's 64 keys.
+  auto pv = [&](int buf) {
+    const uint16_t* v_s = sV[buf];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const int d = 32 * md + qn;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(
+            v_s + d * kBK + (((2 * ks + hf) ^ swv(d)) * 8));
+        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, pw[ks]),
+                                                        o[md], 0, 0, 0);
+      }
+    }
+  };
+
+  int cur = next_visit(rng.x);
+  if (cur <= rng.y) {
+    load_tile(cur);
+    store_tile(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  while (cur <= rng.y) {
+    const int nxt = next_visit(cur + 1);
+    // The next tile's global loads fly during QK^T and the softmax; its LDS
+    // buffer was last read before the previous barrier.
+    if (nxt <= rng.y) load_tile(nxt);
+    qk_softmax(buf, cur);
+    if (nxt <= rng.y) store_tile(buf ^ 1);
+    pv(buf);
+    __syncthreads();
+    buf ^= 1;
+    cur = nxt;
+  }
+
+  // Normalize; the sink logit joins the denominator.
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  float f = 1.f, den = l_tot;
+  if (a.sinks != nullptr) {
+    const float s2 = bf16_to_f32(static_cast<const uint16_t*>(a.sinks)[h]) * kLog2e;
+    const float M = fmaxf(m_run, s2);
+    f = exp2f(m_run - M);
+    den = l_tot * f + exp2f(s2 - M);
+  }
+  const float inv = den > 0.f ? f / den : 0.f;
+  if (q_valid) {
+    uint16_t* og = static_cast<uint16_t*>(a.out) + ((long long)q_tok * a.heads + h) * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[md][4 * g] * inv, o[md][4 * g + 1] * inv);
+        w[1] = pack_bf16x2(o[md][4 * g + 2] * inv, o[md][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(og + 32 * md + 8 * g + 4 * hf) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+static int group_width(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
+
+size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim) {
+  (void)heads;
+  (void)kv_heads;
+  (void)head_dim;
+  const size_t n_kt = (size_t)(p + kBK - 1) / kBK;
+  const size_t n_qt = (size_t)(p + 31) / 32;  // the smallest query tile
+  return align256(n_kt * sizeof(TileSum)) + align256(n_qt * sizeof(TileSum)) +
+         align256(n_qt * sizeof(int2)) + align256(n_qt * sizeof(int));
+}
+
+template <int D, int GW>
+static void launch_main(const PrefillArgs& a, const Plan& pl, hipStream_t stream) {
+  const int n_groups = a.kv_heads * pl.head_groups;
+  prefill_kernel<D, GW><<<dim3(pl.n_qt * n_groups), dim3(256), 0, stream>>>(a, pl);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  const int G = a.heads / a.kv_heads;
+  Plan pl;
+  pl.gw = group_width(G);
+  pl.head_groups = G / pl.gw;
+  pl.tq = 32 * (4 / pl.gw);
+  pl.n_kt = (a.p + kBK - 1) / kBK;
+  pl.n_qt = (a.p + pl.tq - 1) / pl.tq;
+  const size_t n_kt_b = align256((size_t)pl.n_kt * sizeof(TileSum));
+  const size_t n_qt_max = (size_t)(a.p + 31) / 32;
+  const size_t q_b = align256(n_qt_max * sizeof(TileSum));
+  const size_t r_b = align256(n_qt_max * sizeof(int2));
+  char* ws = static_cast<char*>(a.ws);
+  pl.ksum = reinterpret_cast<TileSum*>(ws);
+  pl.qsum = reinterpret_cast<TileSum*>(ws + n_kt_b);
+  pl.qrange = reinterpret_cast<int2*>(ws + n_kt_b + q_b);
+  pl.order = reinterpret_cast<int*>(ws + n_kt_b + q_b + r_b);
+
+  prefill_prep_kernel<<<1, kPrepThreads, 0, stream>>>(a, pl);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.head_dim == 64) {
+    if (pl.gw == 4) launch_main<64, 4>(a, pl, stream);
+    else if (pl.gw == 2) launch_main<64, 2>(a, pl, stream);
+    else launch_main<64, 1>(a, pl, stream);
+  } else {
+    if (pl.gw == 4) launch_main<128, 4>(a, pl, stream);
+    else if (pl.gw == 2) launch_main<128, 2>(a, pl, stream);
+    else launch_main<128, 1>(a, pl, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -1,0 +1,203 @@
+/*
+ * gqa.h -- C ABI of the MI355X (gfx950) grouped-query attention library.
+ *
+ * The library computes grouped-query causal attention with rotary positions
+ * over a KV cache, as the GroupedQueryAttention block of the Linnet
+ * "examples/01-llama" page defines it (src/attention.linnet: `forward`,
+ * `packed`, `decode`; src/rope.linnet: `tables`), with the serving entries of
+ * the Nest llama-3.1-8b-instruct card (decode_rows, prefill_slots,
+ * prefill_packed, decode_paged, prefill_paged; PageSize = 64) and the
+ * sliding-window / sink-logit variant of the Nest gpt-oss-20b card
+ * (SinkAttention: `window: i32`, `param sinks: Tensor[Heads; T]`).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every buffer pointer is a DEVICE pointer owned by the caller. The library
+ *   keeps no pointer after a call returns, allocates no memory, holds no
+ *   per-call state and never synchronizes: work is enqueued on `stream` (a
+ *   hipStream_t; NULL is the default stream) and the call returns.
+ * - dtype (T): GQA_BF16 or GQA_F32. q, k, v, caches, out, sinks and the rotary
+ *   table all have type T. Scores, softmax statistics and accumulators are
+ *   f32 on the device.
+ * - Layouts are row-major, token-major for activations: q [n, heads, D],
+ *   k/v [n, kv_heads, D] (the [B, S, N*D] layout before split_heads' permute).
+ *   Contiguous cache: [batch, kv_heads, max_seq, D] (state cache_k/cache_v).
+ *   Paged pool: [num_pages, kv_heads, GQA_PAGE_SIZE, D] for K and for V; a
+ *   page table [rows, pages] of int32 page ids maps logical position t of row
+ *   r to page table[r, t / 64], offset t % 64.
+ * - GQA: query head h reads KV head floor(h / (heads / kv_heads)).
+ * - scale: 0 selects rsqrt(f32(D)) (the pages' rsqrt(cast<f32>(H / Heads)));
+ *   otherwise the given value multiplies q.k.
+ * - window: 0 is no window; W > 0 keeps key position p_k for query position
+ *   p_q iff 0 <= p_q - p_k < W (W keys including the query's own).
+ * - sinks: NULL, or [heads] of T; exp(sinks[h]) is added to head h's softmax
+ *   denominator (a logit with no value vector, not multiplied by the scale).
+ * - A query with no allowed key produces 0.
+ * - Errors: every call validates its arguments on the host before enqueuing
+ *   anything and returns a GQA_ERR_* code without touching device memory if
+ *   they are invalid (the block's `where` clause: heads > 0, kv_heads > 0,
+ *   heads % kv_heads == 0, D even; here also D in {64, 128}). n == 0 is
+ *   GQA_OK and enqueues nothing. A HIP launch failure returns GQA_ERR_HIP.
+ *   Index values held in device memory (positions, rows, slots, table
+ *   entries, segments) are not checked on the host; the kernels give every
+ *   value a defined, memory-safe meaning, stated per entry point below.
+ * - Determinism: identical inputs give bitwise identical outputs (no float
+ *   atomics; the split schedule depends only on the shapes).
+ * - Thread safety: calls may be made from any host thread.
+ * - Dry run: after gqa_set_dry_run(1), calls validate and return without any
+ *   HIP call (for hosts without a GPU).
+ */
+#ifndef GQA_H_
+#define GQA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define GQA_OK 0
+#define GQA_ERR_INVALID_ARG 1 /* null pointer, negative size, violated where clause */
+#define GQA_ERR_UNSUPPORTED 2 /* valid, but this dtype / head dim / op is not built */
+#define GQA_ERR_WORKSPACE 3   /* workspace missing or smaller than required */
+#define GQA_ERR_HIP 4         /* a HIP runtime call or kernel launch failed */
+
+/* Element types. */
+#define GQA_BF16 0
+#define GQA_F32 1
+
+/* Cache kinds of gqa_rope_write_kv. */
+#define GQA_CACHE_NONE 0        /* rotate only */
+#define GQA_CACHE_CONTIGUOUS 1  /* [batch, kv_heads, max_seq, D] */
+#define GQA_CACHE_PAGED_TABLE 2 /* pool + page table, logical positions */
+#define GQA_CACHE_PAGED_SLOTS 3 /* pool + physical slots */
+
+/* PageSize generic of the GroupedQueryAttention block. */
+#define GQA_PAGE_SIZE 64
+
+/*
+ * gqa_rope_table -- the rotary tables of rope.linnet `tables<S, D, T>(theta)`.
+ *   inv_freq[i] = exp(-(f32(i) * 2 / f32(D)) * log(theta)), i < D/2, in f32;
+ *   angle[s, i] = f32(s) * inv_freq[i] (f32 product);
+ *   table[0, s, i] = cast<T>(cos(angle)), table[1, s, i] = cast<T>(sin(angle)).
+ * Each f32 step is the correctly rounded f32 result (evaluated in fp64 on the
+ * device and rounded), cos/sin rounded to f32 and then to T, nearest-even.
+ * The page's [S, D] tables repeat every frequency in both halves of the head
+ * dimension; only the first half is stored: table is [2, max_pos, D/2] of T.
+ *   head_dim: D (64 or 128); max_pos: S > 0; theta > 0.
+ */
+int gqa_rope_table(int32_t head_dim, int32_t max_pos, float theta, int32_t dtype,
+                   void* table, void* stream);
+
+/*
+ * gqa_rope_write_kv -- rope on q and k at each token's position, then the KV
+ * write (`decode`: rope(q), rope(k), write_at(cache_k, k, pos),
+ * write_at(cache_v, v, pos); prefill_slots / prefill_packed / prefill_paged /
+ * decode_paged do the same at rows / slots / table pages).
+ *   n tokens; q [n, heads, D] and k [n, kv_heads, D] are rotated IN PLACE
+ *   (q may be NULL: not rotated; k may be NULL only when rope_table is NULL
+ *   or cache_kind is NONE and there is nothing to rotate).
+ *   Rotation (rotate-half on the pairs (i, i + D/2)) at position
+ *   positions[t] with the table of gqa_rope_table:
+ *     y_lo = x_lo * c - x_hi * s,  y_hi = x_hi * c + x_lo * s,
+ *   evaluated exactly and rounded once to T (nearest-even). A position
+ *   outside [0, rope_max_pos) reads the nearest table row.
+ *   rope_table == NULL: no rotation (learned positions, as in GPT-2).
+ *   v [n, kv_heads, D] is copied bit for bit into cache_v (NULL: K only).
+ *   cache_kind selects the write target of token t:
+ *     NONE          nothing written.
+ *     CONTIGUOUS    cache[r, :, positions[t], :] with r = rows[t] (rows NULL:
+ *                   0); cache_dim0 = batch, cache_seq = max_seq.
+ *     PAGED_TABLE   logical position positions[t] of table row r = rows[t]
+ *                   (NULL: 0): page table[r, pos / 64], offset pos % 64;
+ *                   cache_dim0 = num_pages, cache_seq = 64; table is
+ *                   [table_rows, table_pages].
+ *     PAGED_SLOTS   physical slot slots[t] = page * 64 + offset;
+ *                   cache_dim0 = num_pages, cache_seq = 64.
+ *   A target outside the cache (row, position, slot or page id out of range)
+ *   drops that token's write: write_at is a masked select. Two tokens with
+ *   the same target race (one of them lands).
+ */
+int gqa_rope_write_kv(int32_t n, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                      int32_t dtype, void* q, void* k, const void* v,
+                      const int32_t* positions, const void* rope_table, int32_t rope_max_pos,
+                      int32_t cache_kind, void* cache_k, void* cache_v, int32_t cache_dim0,
+                      int32_t cache_seq, const int32_t* rows, const int32_t* slots,
+                      const int32_t* table, int32_t table_rows, int32_t table_pages,
+                      void* stream);
+
+/*
+ * gqa_prefill_packed -- attention of `packed<P>` / prefill_packed: token i
+ * attends key j iff segments[i] == segments[j] && positions[j] <=
+ * positions[i] (the `own` mask, literal: any segment ids, any order) and the
+ * window keeps it; grouped_attention then softmax-weights v.
+ *   q [p, heads, D] and k, v [p, kv_heads, D] already rotated (see
+ *   gqa_rope_write_kv); out [p, heads, D] of T.
+ *   Built for T = bf16, D in {64, 128}; bf16 matrix cores, f32 softmax.
+ *   workspace: device memory of at least gqa_prefill_packed_workspace(...)
+ *   bytes (tile summaries and the schedule), 256-byte aligned.
+ */
+int gqa_prefill_packed(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                       int32_t dtype, float scale, int32_t window, const void* sinks,
+                       const void* q, const void* k, const void* v,
+                       const int32_t* positions, const int32_t* segments, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+size_t gqa_prefill_packed_workspace(int32_t p, int32_t heads, int32_t kv_heads,
+                                    int32_t head_dim);
+
+/*
+ * gqa_decode_rows -- `decode` / decode_rows: row b's query attends every slot
+ * s of its cache row with s <= positions[b] (seen = iota(MaxSeq) <= pos) and
+ * inside the window; slots past positions[b] are never read. A position at or
+ * past max_seq attends the whole row; a negative position attends nothing.
+ *   q [batch, heads, D]; cache_k, cache_v [batch, kv_heads, max_seq, D];
+ *   positions [batch]; out [batch, heads, D].
+ *   The query's own key must already be in the cache (gqa_rope_write_kv
+ *   enqueued before on the same stream).
+ *   workspace: at least gqa_decode_rows_workspace(...) bytes (split partials).
+ */
+int gqa_decode_rows(int32_t batch, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                    int32_t dtype, float scale, int32_t window, const void* sinks,
+                    const void* q, const void* cache_k, const void* cache_v, int32_t max_seq,
+                    const int32_t* positions, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+size_t gqa_decode_rows_workspace(int32_t batch, int32_t heads, int32_t kv_heads,
+                                 int32_t head_dim, int32_t max_seq);
+
+/*
+ * gqa_decode_paged -- decode_paged<Rows, Pages>: row r's logical key t,
+ * 0 <= t < pages * 64, is attended iff t <= positions[r] and the window keeps
+ * it; it lives at page table[r, t / 64], offset t % 64 of the pool. A page id
+ * outside [0, num_pages) contributes no keys (its entries are never used to
+ * address memory), so tables may carry -1 past a row's last page.
+ *   q [rows, heads, D]; pool_k, pool_v [num_pages, kv_heads, 64, D];
+ *   positions [rows]; table [rows, pages]; out [rows, heads, D].
+ *   workspace: at least gqa_decode_paged_workspace(...) bytes.
+ */
+int gqa_decode_paged(int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
+                     int32_t head_dim, int32_t dtype, float scale, int32_t window,
+                     const void* sinks, const void* q, const void* pool_k, const void* pool_v,
+                     int32_t num_pages, const int32_t* positions, const int32_t* table,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t gqa_decode_paged_workspace(int32_t rows, int32_t pages, int32_t heads,
+                                  int32_t kv_heads, int32_t head_dim);
+
+/* Human-readable name of a status code (static storage). */
+const char* gqa_status_string(int32_t status);
+
+/* Dry-run switch (process-wide); returns the previous setting. */
+int32_t gqa_set_dry_run(int32_t on);
+
+/* ABI version of this header. */
+int32_t gqa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H_ */

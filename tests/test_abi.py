@@ -1,0 +1,175 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/gqa.h declares, and its host-side validation accepts the shapes the
+pages bind and rejects what the `where` clause forbids (dry-run mode: the
+library validates and returns before any HIP call)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "decoder_attention_rope_amd", "libgqa.so")
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+
+def _build_if_missing():
+    """Build the library when nothing is built yet (build.py is loaded by path:
+    the package itself refuses to import without the library)."""
+    if os.path.exists(LIB):
+        return
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_gqa_build", os.path.join(ROOT, "decoder_attention_rope_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod.build()
+
+
+@pytest.fixture(scope="module")
+def g():
+    _build_if_missing()
+    import decoder_attention_rope_amd as mod
+    prev = mod.gqa_set_dry_run(1)
+    yield mod
+    mod.gqa_set_dry_run(prev)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(g):
+    names = declared_functions()
+    assert {"gqa_rope_write_kv", "gqa_prefill_packed", "gqa_decode_paged",
+            "gqa_decode_rows"} <= set(names)
+    cdll = ctypes.CDLL(LIB)
+    missing = [n for n in names if not hasattr(cdll, n)]
+    assert not missing, f"declared but not exported: {missing}"
+    assert g.gqa_abi_version() == 1
+
+
+def _codes(g):
+    return g.GQA_ERR_INVALID_ARG, g.GQA_ERR_UNSUPPORTED, g.GQA_ERR_WORKSPACE
+
+
+def _expect(g, status, fn, *args):
+    if status == g.GQA_OK:
+        fn(*args)
+        return
+    with pytest.raises(g.GQAError) as e:
+        fn(*args)
+    assert e.value.status == status
+
+
+def _decode_rows(g, heads, kvh, d, dtype=0, batch=2, max_seq=64, window=0, ws=True, scale=0.0):
+    nb = g.gqa_decode_rows_workspace(max(batch, 1), heads, kvh, d, max_seq) if ws else 0
+    return (g.gqa_decode_rows, batch, heads, kvh, d, dtype, scale, window, None, 8, 8, 8, max_seq,
+            8, 8, 256 if ws else None, nb)
+
+
+def test_page_shapes_accepted(g):
+    pages = json.load(open(os.path.join(ROOT, "tests", "golden", "page_generics.json")))
+    llama, gpt2, oss, tiny = (pages["llama-3.1-8b-instruct"], pages["gpt2"], pages["gpt-oss-20b"],
+                              pages["01-llama-bind"])
+    shapes = [
+        (llama["Heads"], llama["KvHeads"], llama["H"] // llama["Heads"], g.GQA_BF16),
+        (gpt2["Heads"], gpt2["Heads"], gpt2["H"] // gpt2["Heads"], g.GQA_F32),
+        (oss["Heads"], oss["KvHeads"], oss["HeadDim"], g.GQA_BF16),
+        (tiny["Heads"], tiny["KvHeads"], tiny["H"] // tiny["Heads"], g.GQA_BF16),
+    ]
+    for heads, kvh, d, dt in shapes:
+        fn, *args = _decode_rows(g, heads, kvh, d, dt)
+        fn(*args)
+        g.gqa_rope_write_kv(4, heads, kvh, d, dt, 8, 8, 8, 8, 8, 16, g.GQA_CACHE_CONTIGUOUS, 8, 8,
+                            2, 16, None, None, None, 0, 0)
+        nbp = g.gqa_decode_paged_workspace(3, 4, heads, kvh, d)
+        g.gqa_decode_paged(3, 4, heads, kvh, d, dt, 0.0, oss["Window"], 8, 8, 8, 8, 10, 8, 8, 8,
+                           256, nbp)
+        if dt == g.GQA_BF16:
+            nb = g.gqa_prefill_packed_workspace(100, heads, kvh, d)
+            g.gqa_prefill_packed(100, heads, kvh, d, dt, 0.0, 0, None, 8, 8, 8, 8, 8, 8, 256, nb)
+        g.gqa_rope_table(d, 64, pages["THETA"], dt, 8)
+    # the workloads use the cards' shapes
+    import workloads as W
+    assert (W.LLAMA8B_PAGED.heads, W.LLAMA8B_PAGED.kv_heads, W.LLAMA8B_PAGED.head_dim) == \
+        (llama["Heads"], llama["KvHeads"], llama["H"] // llama["Heads"])
+    assert W.LLAMA8B_PAGED.extra["page_size"] == llama["PageSize"]
+    assert (W.GPT2_DECODE_ROWS.heads, W.GPT2_DECODE_ROWS.head_dim) == \
+        (gpt2["Heads"], gpt2["H"] // gpt2["Heads"])
+    assert W.GPT2_DECODE_ROWS.extra["max_seq"] == gpt2["MaxSeq"]
+    assert (W.GPT_OSS_SINK.heads, W.GPT_OSS_SINK.kv_heads, W.GPT_OSS_SINK.head_dim) == \
+        (oss["Heads"], oss["KvHeads"], oss["HeadDim"])
+    assert W.GPT_OSS_SINK.extra["windows"][0] == oss["Window"]
+    assert (W.TINY_LLAMA.heads, W.TINY_LLAMA.kv_heads, W.TINY_LLAMA.extra["max_seq"]) == \
+        (tiny["Heads"], tiny["KvHeads"], tiny["MaxSeq"])
+
+
+def test_where_clause_violations(g):
+    bad_arg, unsup, ws_err = _codes(g)
+    cases = [
+        (bad_arg, dict(heads=0, kvh=1, d=64)),
+        (bad_arg, dict(heads=8, kvh=0, d=64)),
+        (bad_arg, dict(heads=8, kvh=3, d=64)),     # Heads % KvHeads != 0
+        (bad_arg, dict(heads=8, kvh=8, d=63)),     # odd head dim
+        (unsup, dict(heads=8, kvh=8, d=96)),       # valid, not built
+        (bad_arg, dict(heads=8, kvh=8, d=64, dtype=7)),
+        (bad_arg, dict(heads=8, kvh=8, d=64, window=-1)),
+        (bad_arg, dict(heads=8, kvh=8, d=64, batch=-1)),
+        (bad_arg, dict(heads=8, kvh=8, d=64, max_seq=0)),
+        (ws_err, dict(heads=8, kvh=8, d=64, ws=False)),
+        (bad_arg, dict(heads=8, kvh=8, d=64, scale=float("nan"))),
+        (g.GQA_OK, dict(heads=8, kvh=8, d=64, batch=0)),  # empty is fine
+    ]
+    for status, kw in cases:
+        fn, *args = _decode_rows(g, **kw)
+        _expect(g, status, fn, *args)
+
+
+def test_entry_point_argument_checks(g):
+    bad_arg, unsup, ws_err = _codes(g)
+    # null pointers
+    _expect(g, bad_arg, g.gqa_decode_paged, 2, 4, 8, 8, 64, 0, 0.0, 0, None, None, 8, 8, 10, 8, 8,
+            8, 256, 10 ** 6)
+    _expect(g, bad_arg, g.gqa_prefill_packed, 10, 8, 8, 64, 0, 0.0, 0, None, 8, 8, 8, None, 8, 8,
+            256, 10 ** 6)
+    # prefill is built for bf16 only
+    _expect(g, unsup, g.gqa_prefill_packed, 10, 8, 8, 64, 1, 0.0, 0, None, 8, 8, 8, 8, 8, 8, 256,
+            10 ** 6)
+    # workspace: too small, misaligned
+    _expect(g, ws_err, g.gqa_prefill_packed, 10, 8, 8, 64, 0, 0.0, 0, None, 8, 8, 8, 8, 8, 8, 256,
+            16)
+    _expect(g, ws_err, g.gqa_prefill_packed, 10, 8, 8, 64, 0, 0.0, 0, None, 8, 8, 8, 8, 8, 8, 257,
+            10 ** 6)
+    _expect(g, g.GQA_OK, g.gqa_prefill_packed, 0, 8, 8, 64, 0, 0.0, 0, None, 8, 8, 8, 8, 8, 8,
+            None, 0)
+    # paged writes need the page size; table writes need a table
+    _expect(g, bad_arg, g.gqa_rope_write_kv, 4, 8, 8, 64, 0, 8, 8, 8, 8, 8, 16,
+            g.GQA_CACHE_PAGED_SLOTS, 8, 8, 10, 32, None, 8, None, 0, 0)
+    _expect(g, bad_arg, g.gqa_rope_write_kv, 4, 8, 8, 64, 0, 8, 8, 8, 8, 8, 16,
+            g.GQA_CACHE_PAGED_TABLE, 8, 8, 10, 64, None, None, None, 0, 0)
+    _expect(g, g.GQA_OK, g.gqa_rope_write_kv, 4, 8, 8, 64, 0, 8, 8, 8, 8, 8, 16,
+            g.GQA_CACHE_PAGED_TABLE, 8, 8, 10, 64, None, None, 8, 3, 2)
+    _expect(g, bad_arg, g.gqa_rope_write_kv, 4, 8, 8, 64, 0, 8, 8, 8, 8, 8, 16, 9, 8, 8, 10, 64,
+            None, None, None, 0, 0)
+    _expect(g, bad_arg, g.gqa_rope_write_kv, -1, 8, 8, 64, 0, 8, 8, 8, 8, 8, 16,
+            g.GQA_CACHE_NONE, None, None, 0, 0, None, None, None, 0, 0)
+    # rope table
+    _expect(g, bad_arg, g.gqa_rope_table, 64, 0, 1e4, 0, 8)
+    _expect(g, bad_arg, g.gqa_rope_table, 64, 10, -1.0, 0, 8)
+    _expect(g, unsup, g.gqa_rope_table, 32, 10, 1e4, 0, 8)
+    # paged decode: pages * 64 must fit int32
+    _expect(g, bad_arg, g.gqa_decode_paged, 2, 2 ** 26, 8, 8, 64, 0, 0.0, 0, None, 8, 8, 8, 10, 8,
+            8, 8, 256, 10 ** 12)
+
+
+def test_workspace_sizes(g):
+    assert g.gqa_decode_rows_workspace(0, 8, 8, 64, 10) == 0
+    a = g.gqa_decode_paged_workspace(64, 128, 32, 8, 128)
+    b = g.gqa_decode_paged_workspace(64, 256, 32, 8, 128)
+    assert 0 < a < b
+    assert g.gqa_prefill_packed_workspace(16384, 32, 8, 128) > g.gqa_prefill_packed_workspace(
+        1024, 32, 8, 128) > 0
