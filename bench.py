@@ -1,0 +1,270 @@
+#!/usr/bin/env python
+"""Benchmark of the grouped-query attention hot path on one MI355X.
+
+One step is one pass over every stage of the path on the two headline
+workloads, with all inputs resident in HBM:
+
+  1. gqa_rope_table     rotary tables, D = 128, theta = 500000, 8192 positions
+  2. gqa_rope_write_kv  rope + paged KV write of 64 new tokens (Llama-3.1-8B
+                        shapes, page table into a 9000-page pool)
+  3. gqa_decode_paged   paged decode, 64 rows, context lengths U[512, 8192]
+  4. gqa_rope_write_kv  rope + KV write of 16384 packed tokens (cache row =
+                        segment)
+  5. gqa_prefill_packed packed prefill, 16384 tokens, segments U[64, 4096]
+
+Each stage is bracketed by HIP events on the stream it is launched on. The
+JSON line reports the paged-decode KV bandwidth as `value` (GB/s), the
+packed-prefill throughput (TFLOP/s), both against the MI355X peaks, the
+oracle timed on the host cores on a bounded sample, and the per-stage times.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged GQA decode KV GB/s + packed prefill TFLOP/s (% of MI355X peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+SEED_DECODE, SEED_PREFILL = 3, 4
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=16)
+    ap.add_argument("--cpu-sample-queries", type=int, default=256)
+    return ap.parse_args()
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "decoder_attention_rope_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, sources):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel)
+    if not ent or ent.get("source_sha") != source_sha(*sources):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention path is measured on one MI355X, see DESIGN.md for how it would "
+              "shard)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import decoder_attention_rope_amd as gqa
+    import workloads as W
+
+    dev = "cuda"
+    bf16 = torch.bfloat16
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    # ---------------- decode workload (Llama-3.1-8B paged) ----------------
+    wd = W.LLAMA8B_PAGED
+    ed = wd.extra
+    H, KVH, D = wd.heads, wd.kv_heads, wd.head_dim
+    gi = W.streams(SEED_DECODE)
+    lengths, dpos, table = W.paged_layout(ed["rows"], ed["len_lo"], ed["len_hi"],
+                                          ed["num_pages"], ed["page_size"], gi["index"])
+    rows, pages, num_pages = ed["rows"], table.shape[1], ed["num_pages"]
+    pool_k = W.device_normal((num_pages, KVH, 64, D), SEED_DECODE, "pool_k", bf16)
+    pool_v = W.device_normal((num_pages, KVH, 64, D), SEED_DECODE, "pool_v", bf16)
+    dq = W.device_normal((rows, H, D), SEED_DECODE, "q", bf16)
+    dk = W.device_normal((rows, KVH, D), SEED_DECODE, "k", bf16)
+    dv = W.device_normal((rows, KVH, D), SEED_DECODE, "v", bf16)
+    d_pos = torch.from_numpy(dpos).to(dev)
+    d_table = torch.from_numpy(table).to(dev)
+    d_rows = torch.arange(rows, dtype=torch.int32, device=dev)
+    d_out = torch.empty((rows, H, D), dtype=bf16, device=dev)
+    dws_n = gqa.gqa_decode_paged_workspace(rows, pages, H, KVH, D)
+    d_ws = torch.empty(dws_n, dtype=torch.uint8, device=dev)
+    theta = wd.theta
+    max_pos = 8192
+    rope_tab = torch.empty((2, max_pos, D // 2), dtype=bf16, device=dev)
+
+    # ---------------- prefill workload (Llama-3.1-8B packed) ----------------
+    wp = W.LLAMA8B_PACKED
+    P = wp.extra["p"]
+    gp = W.streams(SEED_PREFILL)
+    seg_len, ppos, pseg = W.segment_layout(P, wp.extra["seg_lo"], wp.extra["seg_hi"], gp["index"])
+    nseg = len(seg_len)
+    pq = W.device_normal((P, H, D), SEED_PREFILL, "q", bf16)
+    pk = W.device_normal((P, KVH, D), SEED_PREFILL, "k", bf16)
+    pv = W.device_normal((P, KVH, D), SEED_PREFILL, "v", bf16)
+    p_pos = torch.from_numpy(ppos).to(dev)
+    p_seg = torch.from_numpy(pseg).to(dev)
+    cache_len = int(max(seg_len))
+    p_cache_k = torch.empty((nseg, KVH, cache_len, D), dtype=bf16, device=dev)
+    p_cache_v = torch.empty((nseg, KVH, cache_len, D), dtype=bf16, device=dev)
+    p_out = torch.empty((P, H, D), dtype=bf16, device=dev)
+    pws_n = gqa.gqa_prefill_packed_workspace(P, H, KVH, D)
+    p_ws = torch.empty(max(pws_n, 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    # Host snapshots for the CPU baseline, taken before any library call so
+    # the oracle never sees data the library wrote.
+    snap = None
+    if not args.no_cpu_baseline:
+        srows = np.arange(min(args.cpu_sample_rows, rows))
+        used = sorted({int(p) for r in srows for p in table[r] if p >= 0})
+        remap = {p: i for i, p in enumerate(used)}
+        st = np.array([[remap.get(int(p), -1) if p >= 0 else -1 for p in table[r]]
+                       for r in srows], dtype=np.int32)
+        idx = torch.tensor(used, dtype=torch.long, device=dev)
+        sel = W.sample_indices(P, args.cpu_sample_queries, gp["extra"])
+        snap = dict(
+            rows=srows, table=st,
+            pk=pool_k[idx].to(torch.float64).cpu().numpy(),
+            pv=pool_v[idx].to(torch.float64).cpu().numpy(),
+            q=dq[torch.from_numpy(srows).to(dev)].to(torch.float64).cpu().numpy(),
+            pq=pq.to(torch.float64).cpu().numpy(), pk_=pk.to(torch.float64).cpu().numpy(),
+            pv_=pv.to(torch.float64).cpu().numpy(), sel=sel)
+
+    # ---------------- one step ----------------
+    names = ["rope_table", "rope_write_decode", "decode_paged", "rope_write_prefill",
+             "prefill_packed"]
+
+    def step(ev):
+        ev[0].record(stream)
+        gqa.gqa_rope_table(D, max_pos, theta, gqa.GQA_BF16, rope_tab)
+        ev[1].record(stream)
+        gqa.gqa_rope_write_kv(rows, H, KVH, D, gqa.GQA_BF16, dq, dk, dv, d_pos, rope_tab, max_pos,
+                              gqa.GQA_CACHE_PAGED_TABLE, pool_k, pool_v, num_pages, 64, d_rows,
+                              None, d_table, rows, pages)
+        ev[2].record(stream)
+        gqa.gqa_decode_paged(rows, pages, H, KVH, D, gqa.GQA_BF16, 0.0, 0, None, dq, pool_k,
+                             pool_v, num_pages, d_pos, d_table, d_out, d_ws, dws_n)
+        ev[3].record(stream)
+        gqa.gqa_rope_write_kv(P, H, KVH, D, gqa.GQA_BF16, pq, pk, pv, p_pos, rope_tab, max_pos,
+                              gqa.GQA_CACHE_CONTIGUOUS, p_cache_k, p_cache_v, nseg, cache_len,
+                              p_seg, None, None, 0, 0)
+        ev[4].record(stream)
+        gqa.gqa_prefill_packed(P, H, KVH, D, gqa.GQA_BF16, 0.0, 0, None, pq, pk, pv, p_pos, p_seg,
+                               p_out, p_ws, pws_n)
+        ev[5].record(stream)
+
+    def new_events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+
+    for _ in range(args.warmup):
+        step(new_events())
+    torch.cuda.synchronize()
+    evs = [new_events() for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_op_ms = {n: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in evs]))
+                 for i, n in enumerate(names)}
+    step_ms = float(np.mean([ev[0].elapsed_time(ev[5]) for ev in evs]))
+
+    # ---------------- algorithmic work ----------------
+    kv_bytes = int(np.sum(lengths)) * KVH * D * 2 * 2          # K + V of attended keys
+    qo_bytes = 2 * rows * H * D * 2                              # q in, out
+    decode_bytes = kv_bytes + qo_bytes
+    pairs = int(np.sum(seg_len * (seg_len + 1) // 2))
+    prefill_flops = 4 * D * H * pairs                            # QK^T + PV, unmasked pairs
+    dec_s = per_op_ms["decode_paged"] * 1e-3
+    pre_s = per_op_ms["prefill_packed"] * 1e-3
+    decode_gbs = decode_bytes / dec_s / 1e9
+    prefill_tflops = prefill_flops / pre_s / 1e12
+
+    dec_roof = {"bound": "hbm", "achieved": decode_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": decode_gbs / HBM_PEAK_GBS,
+                "traffic": traffic_for("decode_paged", ["decode.hip", "common.h"]),
+                "algorithmic_bytes": decode_bytes, "avg_us": dec_s * 1e6}
+    pre_roof = {"bound": "mfma", "achieved": prefill_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": prefill_tflops / MFMA_BF16_PEAK_TFLOPS,
+                "traffic": traffic_for("prefill_packed", ["prefill.hip", "common.h"]),
+                "algorithmic_flops": prefill_flops, "avg_us": pre_s * 1e6}
+    dominant = "prefill_packed" if pre_s >= dec_s else "decode_paged"
+    roof = dict(pre_roof if dominant == "prefill_packed" else dec_roof)
+    roof["kernel"] = dominant
+
+    # ---------------- CPU baseline: the oracle on a bounded sample ----------------
+    cpu = None
+    if snap is not None:
+        import oracle
+        o = oracle.default()
+        t = time.perf_counter()
+        o.decode_paged(snap["q"], snap["pk"], snap["pv"], dpos[snap["rows"]], snap["table"])
+        cpu_dec_s = time.perf_counter() - t
+        s_bytes = int(np.sum(lengths[snap["rows"]])) * KVH * D * 2 * 2 + 2 * len(snap["rows"]) * H * D * 2
+        t = time.perf_counter()
+        o.packed(snap["pq"], snap["pk_"], snap["pv_"], ppos, pseg, sel=snap["sel"])
+        cpu_pre_s = time.perf_counter() - t
+        s_pairs = int(np.sum(ppos[snap["sel"]].astype(np.int64) + 1))
+        s_flops = 4 * D * H * s_pairs
+        cpu = {"value": s_bytes / cpu_dec_s / 1e9, "unit": "GB/s", "cores": o.num_threads(),
+               "kind": "oracle",
+               "sample": (f"decode_paged on {len(snap['rows'])} of {rows} rows "
+                          f"({int(np.sum(lengths[snap['rows']]))} keys, {cpu_dec_s:.2f} s); "
+                          f"packed prefill on {len(snap['sel'])} of {P} queries "
+                          f"({s_pairs} attended pairs/head, {cpu_pre_s:.2f} s)"),
+               "prefill_tflops": s_flops / cpu_pre_s / 1e12,
+               "seconds": cpu_dec_s + cpu_pre_s}
+
+    result = {
+        "metric": METRIC,
+        "value": decode_gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) q/k/v and page pool, seeded page table and segment layout",
+        "config": {
+            "workload": "llama-3.1-8b paged decode (64 rows, L~U[512,8192], 9000-page pool, "
+                        "PageSize 64) + packed prefill (P=16384, segments U[64,4096]); "
+                        "Heads 32, KvHeads 8, D 128, theta 5e5",
+            "decode_rows": rows, "decode_keys": int(np.sum(lengths)),
+            "prefill_tokens": P, "prefill_segments": nseg, "prefill_pairs_per_head": pairs,
+        },
+        "prefill_tflops": prefill_tflops,
+        "decode_frac_of_hbm_peak": decode_gbs / HBM_PEAK_GBS,
+        "prefill_frac_of_mfma_peak": prefill_tflops / MFMA_BF16_PEAK_TFLOPS,
+        "roofline": roof,
+        "rooflines": {"decode_paged": dec_roof, "prefill_packed": pre_roof},
+        "per_op_us": {k: v * 1e3 for k, v in per_op_ms.items()},
+        "wall_s_timed": wall,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -25,17 +25,30 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// f32 -> bf16, nearest-even; NaN stays a quiet NaN.
+// f32 -> bf16, round to nearest, ties to even, computed on the integer
+// pattern (select, no branch); NaN stays a quiet NaN. Used wherever the
+// result is compared bit for bit.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t q = (u >> 16) | 0x0040u;
+  return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? q : r);
 }
 
+// Two f32 -> packed bf16 with the hardware converter (v_cvt_pk_bf16_f32), for
+// matrix-core operands where the last-bit rounding choice on exact ties does
+// not matter.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  bf16x2_t r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
 }
+
+// 2^x on the transcendental unit (v_exp_f32); the attention kernels only
+// evaluate it for x <= 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // fp64 -> f32 with round-to-odd: truncate toward zero, then force the last
 // bit to 1 when inexact. A second rounding of that value to any format with
@@ -91,6 +104,11 @@ struct Elem<float> {
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+// Streaming load (nontemporal hint): for data read once, such as the KV cache
+// in decode.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 __device__ __forceinline__ void store16(void* p, const u32x4& v) {
   *reinterpret_cast<u32x4*>(p) = v;

@@ -175,42 +175,82 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Combine the split partials of one (row, query head); the sink logit joins
-// the denominator here.
+// Combine the split partials of one (row, KV head): the G query heads' split
+// weights exp2(m_s - M) go to LDS, then every (head, dimension) output is one
+// coalesced pass over the splits. The sink logit joins the denominator here.
+constexpr int kMergeMaxW = 4096;
+
 template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
-  const int h = blockIdx.x;
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  __shared__ float w[kMergeMaxW];
+  __shared__ float inv_l[64];
+  const int kh = blockIdx.x;
   const int r = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int G = a.heads / a.kv_heads;
+  const int h0 = kh * G;
   int lo, hi;
   decode_key_range(a.positions[r], a.cap, a.window, lo, hi);
-  int s_first = 0, s_last = -1;
+  int s_first = 0, ns = 0;
   if (hi >= lo) {
     s_first = lo / a.split_len;
-    s_last = hi / a.split_len;
+    ns = hi / a.split_len - s_first + 1;
   }
-  const float* part = a.ws + ((long long)r * a.heads + h) * a.nsplit * (D + 2);
   const bool has_sink = a.sinks != nullptr;
-  const float sink2 =
-      has_sink ? Elem<T>::load1(static_cast<const T*>(a.sinks) + h) * kLog2e : kNegInf;
-  float M = sink2;
-  for (int s = s_first; s <= s_last; ++s) M = fmaxf(M, part[(long long)s * (D + 2)]);
-  T* out = static_cast<T*>(a.out) + ((long long)r * a.heads + h) * D;
-  for (int d = lane; d < D; d += 64) {
-    float num = 0.f, den = 0.f;
-    for (int s = s_first; s <= s_last; ++s) {
-      const float* ps = part + (long long)s * (D + 2);
-      const float ms = ps[0];
-      if (ms == kNegInf) continue;
-      const float w = exp2f(ms - M);
-      num += w * ps[2 + d];
-      den += w * ps[1];
+  auto part = [&](int h, int s) {
+    return a.ws + (((long long)r * a.heads + h0 + h) * a.nsplit + s_first + s) * (D + 2);
+  };
+  auto sink2 = [&](int h) {
+    return has_sink ? Elem<T>::load1(static_cast<const T*>(a.sinks) + h0 + h) * kLog2e : kNegInf;
+  };
+  T* out = static_cast<T*>(a.out) + ((long long)r * a.heads + h0) * D;
+  if (G * ns > kMergeMaxW || G > 64) {
+    // Serial fallback for very long caches: one thread per output.
+    for (int x = tid; x < G * D; x += blockDim.x) {
+      const int h = x / D, d = x % D;
+      float M = sink2(h);
+      for (int s = 0; s < ns; ++s) M = fmaxf(M, part(h, s)[0]);
+      float num = 0.f, den = (has_sink && M != kNegInf) ? fast_exp2(sink2(h) - M) : 0.f;
+      for (int s = 0; s < ns; ++s) {
+        const float ms = part(h, s)[0];
+        if (ms == kNegInf) continue;
+        const float ws = fast_exp2(ms - M);
+        num += ws * part(h, s)[2 + d];
+        den += ws * part(h, s)[1];
+      }
+      Elem<T>::store1(out + (long long)h * D + d, den > 0.f ? num / den : 0.f);
     }
-    if (has_sink && M != kNegInf) den += exp2f(sink2 - M);
-    Elem<T>::store1(out + d, den > 0.f ? num / den : 0.f);
+    return;
+  }
+  for (int x = tid; x < G * ns; x += blockDim.x) w[x] = part(x / ns, x % ns)[0];
+  __syncthreads();
+  if (tid < G) {
+    float M = sink2(tid);
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, w[tid * ns + s]);
+    float L = (has_sink && M != kNegInf) ? fast_exp2(sink2(tid) - M) : 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float ms = w[tid * ns + s];
+      const float ws = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
+      w[tid * ns + s] = ws;
+      L += ws * part(tid, s)[1];
+    }
+    inv_l[tid] = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+  for (int x = tid; x < G * D; x += blockDim.x) {
+    const int h = x / D, d = x % D;
+    float acc = 0.f;
+    const float* ws = w + h * ns;
+    for (int s = 0; s < ns; ++s) {
+      const float wt = ws[s];
+      if (wt != 0.f) acc += wt * part(h, s)[2 + d];
+    }
+    Elem<T>::store1(out + (long long)h * D + d, acc * inv_l[h]);
   }
 }
 
+// Vector-ALU split plan; its 256-key splits are the shortest of both paths,
+// so its workspace bound covers the matrix-core path too.
 void decode_plan(int rows, int heads, int kv_heads, int head_dim, int dtype, int paged, int cap,
                  int* split_len, int* nsplit, size_t* ws_bytes) {
   (void)kv_heads;
@@ -251,11 +291,24 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = a.paged ? launch_split_t<T, D, true>(a, gc, stream)
                          : launch_split_t<T, D, false>(a, gc, stream);
   if (e != hipSuccess) return e;
-  decode_merge_kernel<T, D><<<dim3(a.heads, a.rows), 64, 0, stream>>>(a);
+  decode_merge_kernel<T, D><<<dim3(a.kv_heads, a.rows), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
+  if (decode_mfma_supported(a)) {
+    // Matrix-core split kernel, then (with more than one split) the merge.
+    a.split_len = decode_mfma_split_len(a.rows, a.kv_heads, a.cap);
+    a.nsplit = (a.cap + a.split_len - 1) / a.split_len;
+    hipError_t e = launch_decode_mfma(a, stream);
+    if (e != hipSuccess) return e;
+    if (a.nsplit == 1) return hipSuccess;  // the split kernel wrote the output
+    if (a.head_dim == 64)
+      decode_merge_kernel<uint16_t, 64><<<dim3(a.kv_heads, a.rows), 256, 0, stream>>>(a);
+    else
+      decode_merge_kernel<uint16_t, 128><<<dim3(a.kv_heads, a.rows), 256, 0, stream>>>(a);
+    return hipGetLastError();
+  }
   decode_plan(a.rows, a.heads, a.kv_heads, a.head_dim, a.dtype, a.paged, a.cap, &a.split_len,
               &a.nsplit, nullptr);
   if (a.dtype == kDtypeBf16) {

@@ -142,7 +142,7 @@ int gqa_prefill_packed(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_
   if (p < 0 || window < 0) return GQA_ERR_INVALID_ARG;
   int st = check_heads(heads, kv_heads, head_dim, dtype);
   if (st != GQA_OK) return st;
-  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || scale < 0.0f) return GQA_ERR_INVALID_ARG;
   if (q == nullptr || k == nullptr || v == nullptr || positions == nullptr ||
       segments == nullptr || out == nullptr)
     return GQA_ERR_INVALID_ARG;
@@ -214,7 +214,7 @@ int gqa_decode_rows(int32_t batch, int32_t heads, int32_t kv_heads, int32_t head
   if (batch < 0 || window < 0 || max_seq <= 0) return GQA_ERR_INVALID_ARG;
   int st = check_heads(heads, kv_heads, head_dim, dtype);
   if (st != GQA_OK) return st;
-  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || scale < 0.0f) return GQA_ERR_INVALID_ARG;
   if (q == nullptr || cache_k == nullptr || cache_v == nullptr || positions == nullptr ||
       out == nullptr)
     return GQA_ERR_INVALID_ARG;
@@ -250,7 +250,7 @@ int gqa_decode_paged(int32_t rows, int32_t pages, int32_t heads, int32_t kv_head
   if ((long long)pages * GQA_PAGE_SIZE > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
   int st = check_heads(heads, kv_heads, head_dim, dtype);
   if (st != GQA_OK) return st;
-  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || scale < 0.0f) return GQA_ERR_INVALID_ARG;
   if (q == nullptr || pool_k == nullptr || pool_v == nullptr || positions == nullptr ||
       table == nullptr || out == nullptr)
     return GQA_ERR_INVALID_ARG;

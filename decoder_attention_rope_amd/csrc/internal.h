@@ -77,6 +77,9 @@ hipError_t launch_rope_write(const RopeWriteArgs& a, hipStream_t stream);
 void decode_plan(int rows, int heads, int kv_heads, int head_dim, int dtype, int paged, int cap,
                  int* split_len, int* nsplit, size_t* ws_bytes);
 hipError_t launch_decode(DecodeArgs a, hipStream_t stream);
+bool decode_mfma_supported(const DecodeArgs& a);
+int decode_mfma_split_len(int rows, int kv_heads, int cap);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 
 size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -28,9 +28,9 @@
 //   [min, max] summaries of segments and positions; tiles in which every pair
 //   is allowed skip the per-element mask. The exact `own` predicate is
 //   evaluated everywhere else, so any segment order or id is handled.
-// * A single-workgroup prep kernel computes the summaries, each query tile's
-//   visited key-tile range and its cost, and orders the query tiles longest
-//   first; workgroup index i * n_groups + g maps KV head g to the
+// * Two prep kernels compute the per-tile summaries (one wavefront per tile)
+//   and, in one workgroup, each query tile's visited key-tile range and cost,
+//   ordering the query tiles longest first; workgroup index i * n_groups + g maps KV head g to the
 //   round-robin XCD g % 8, keeping one head's K/V in one XCD's L2.
 #include "common.h"
 #include "internal.h"
@@ -64,37 +64,66 @@ __device__ __forceinline__ bool tiles_meet(const TileSum& q, const TileSum& k, i
   return true;
 }
 
-__device__ __forceinline__ TileSum summarize(const int32_t* pos, const int32_t* seg, int lo, int hi) {
-  TileSum s{0x7fffffff, (int)0x80000000, 0x7fffffff, (int)0x80000000};
-  for (int t = lo; t < hi; ++t) {
-    const int sg = seg[t], ps = pos[t];
-    s.seg_min = min(s.seg_min, sg);
-    s.seg_max = max(s.seg_max, sg);
-    s.pos_min = min(s.pos_min, ps);
-    s.pos_max = max(s.pos_max, ps);
-  }
-  return s;
-}
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Prep: summaries, visited ranges, longest-first order (one workgroup).
+// Prep 1: per-tile [min, max] of segments and positions. One wavefront per
+// tile: key tiles (64 tokens) first, then query tiles (tq tokens); lanes read
+// consecutive tokens and reduce with shuffles.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(PrefillArgs a, Plan pl) {
+__global__ __launch_bounds__(256) void prefill_summarize_kernel(PrefillArgs a, Plan pl) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int ti = blockIdx.x * 4 + wave;
+  if (ti >= pl.n_kt + pl.n_qt) return;
+  const bool is_k = ti < pl.n_kt;
+  const int len = is_k ? kBK : pl.tq;
+  const int lo = is_k ? ti * kBK : (ti - pl.n_kt) * pl.tq;
+  const int hi = min(a.p, lo + len);
+  int smin = 0x7fffffff, smax = (int)0x80000000, pmin = 0x7fffffff, pmax = (int)0x80000000;
+  for (int t = lo + lane; t < hi; t += 64) {
+    const int sg = a.segments[t], ps = a.positions[t];
+    smin = min(smin, sg);
+    smax = max(smax, sg);
+    pmin = min(pmin, ps);
+    pmax = max(pmax, ps);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    smin = min(smin, __shfl_xor(smin, off, 64));
+    smax = max(smax, __shfl_xor(smax, off, 64));
+    pmin = min(pmin, __shfl_xor(pmin, off, 64));
+    pmax = max(pmax, __shfl_xor(pmax, off, 64));
+  }
+  if (lane == 0) {
+    const TileSum sum{smin, smax, pmin, pmax};
+    if (is_k) pl.ksum[ti] = sum;
+    else pl.qsum[ti - pl.n_kt] = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prep 2 (one workgroup): each query tile's visited key-tile range and cost,
+// then the query tiles sorted costliest first (bitonic sort in LDS).
+// ---------------------------------------------------------------------------
+constexpr int kKsumLds = 2048;  // key-tile summaries cached in LDS
+
+__global__ __launch_bounds__(kPrepThreads) void prefill_schedule_kernel(PrefillArgs a, Plan pl) {
+  __shared__ TileSum ks[kKsumLds];
   __shared__ int cost[kSortMax];
   __shared__ int idx[kSortMax];
   const int tid = threadIdx.x;
-  for (int kt = tid; kt < pl.n_kt; kt += kPrepThreads)
-    pl.ksum[kt] = summarize(a.positions, a.segments, kt * kBK, min(a.p, (kt + 1) * kBK));
-  for (int qt = tid; qt < pl.n_qt; qt += kPrepThreads)
-    pl.qsum[qt] = summarize(a.positions, a.segments, qt * pl.tq, min(a.p, (qt + 1) * pl.tq));
+  const bool k_in_lds = pl.n_kt <= kKsumLds;
+  if (k_in_lds)
+    for (int kt = tid; kt < pl.n_kt; kt += kPrepThreads) ks[kt] = pl.ksum[kt];
   __syncthreads();
   const bool sort = pl.n_qt <= kSortMax;
   for (int qt = tid; qt < pl.n_qt; qt += kPrepThreads) {
     const TileSum q = pl.qsum[qt];
     int first = pl.n_kt, last = -1, cnt = 0;
     for (int kt = 0; kt < pl.n_kt; ++kt) {
-      if (tiles_meet(q, pl.ksum[kt], a.window)) {
+      const TileSum k = k_in_lds ? ks[kt] : pl.ksum[kt];
+      if (tiles_meet(q, k, a.window)) {
         first = min(first, kt);
         last = kt;
         ++cnt;
@@ -303,46 +332,50 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
       }
     }
     if (!full) {
+      // The literal own predicate (and the window) per element, branch-free.
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = 32 * mb + 16 * (r >> 3) + 8 * hf + (r & 7);
           const int kp = sPos[buf][j];
-          const bool ok = kt * kBK + j < P && sSeg[buf][j] == my_seg && kp <= my_pos &&
-                          (window <= 0 || (uint32_t)my_pos - (uint32_t)kp < (uint32_t)window);
-          if (!ok) s[mb][r] = kNegInf;
+          const int ksg = sSeg[buf][j];
+          const bool ok = (kt * kBK + j < P) & (ksg == my_seg) & (kp <= my_pos) &
+                          ((window <= 0) | ((uint32_t)my_pos - (uint32_t)kp < (uint32_t)window));
+          s[mb][r] = ok ? s[mb][r] : kNegInf;
         }
       }
     }
+    // Online softmax in the log2 domain. scale > 0, so the row max of the
+    // scaled scores is the scaled row max of the raw ones.
     float tmax = kNegInf;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[mb][r] *= a.scale_log2;
-        tmax = fmaxf(tmax, s[mb][r]);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * a.scale_log2;
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = fast_exp2(m_run - m_use);
     float psum = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = exp2f(s[mb][r] - m_use);
-        const float p1 = exp2f(s[mb][r + 1] - m_use);
+        const float p0 = fast_exp2(__builtin_fmaf(s[mb][r], a.scale_log2, -m_use));
+        const float p1 = fast_exp2(__builtin_fmaf(s[mb][r + 1], a.scale_log2, -m_use));
         psum += p0 + p1;
         pw[2 * mb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
       }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    // Rescale O only when some lane's running max moved.
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
+      for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
+        for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
+    }
   };
 
   // O^T += V^T P^T over the tile's 64 keys.
@@ -387,8 +420,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
   if (a.sinks != nullptr) {
     const float s2 = bf16_to_f32(static_cast<const uint16_t*>(a.sinks)[h]) * kLog2e;
     const float M = fmaxf(m_run, s2);
-    f = exp2f(m_run - M);
-    den = l_tot * f + exp2f(s2 - M);
+    f = fast_exp2(m_run - M);
+    den = l_tot * f + fast_exp2(s2 - M);
   }
   const float inv = den > 0.f ? f / den : 0.f;
   if (q_valid) {
@@ -444,8 +477,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   pl.qrange = reinterpret_cast<int2*>(ws + n_kt_b + q_b);
   pl.order = reinterpret_cast<int*>(ws + n_kt_b + q_b + r_b);
 
-  prefill_prep_kernel<<<1, kPrepThreads, 0, stream>>>(a, pl);
+  const int n_tiles = pl.n_kt + pl.n_qt;
+  prefill_summarize_kernel<<<dim3((n_tiles + 3) / 4), dim3(256), 0, stream>>>(a, pl);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  prefill_schedule_kernel<<<1, kPrepThreads, 0, stream>>>(a, pl);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.head_dim == 64) {
     if (pl.gw == 4) launch_main<64, 4>(a, pl, stream);

@@ -27,7 +27,8 @@
  *   r to page table[r, t / 64], offset t % 64.
  * - GQA: query head h reads KV head floor(h / (heads / kv_heads)).
  * - scale: 0 selects rsqrt(f32(D)) (the pages' rsqrt(cast<f32>(H / Heads)));
- *   otherwise the given value multiplies q.k.
+ *   otherwise the given value (finite, > 0) multiplies q.k; a negative or
+ *   non-finite scale is GQA_ERR_INVALID_ARG.
  * - window: 0 is no window; W > 0 keeps key position p_k for query position
  *   p_q iff 0 <= p_q - p_k < W (W keys including the query's own).
  * - sinks: NULL, or [heads] of T; exp(sinks[h]) is added to head h's softmax

@@ -72,9 +72,12 @@ def test_decode_rows_gpt2_f32():
 
 
 # --- small and edge cases -------------------------------------------------------
+# bf16 with up to 16 query heads per KV head runs on the matrix-core kernel;
+# f32 and larger groups (32 here) on the vector-ALU kernel.
 @pytest.mark.parametrize("heads,kvh,d,dtype", [(8, 8, 64, "bf16"), (32, 8, 128, "bf16"),
                                                 (64, 8, 64, "bf16"), (16, 2, 128, "f32"),
-                                                (6, 3, 64, "bf16"), (4, 4, 128, "f32")])
+                                                (6, 3, 64, "bf16"), (4, 4, 128, "f32"),
+                                                (32, 1, 64, "bf16"), (16, 1, 128, "bf16")])
 def test_decode_rows_shapes(heads, kvh, d, dtype):
     print(f"[case] decode_rows H={heads} KvH={kvh} D={d} {dtype}", flush=True)
     batch, max_seq = 7, 700
@@ -178,7 +181,7 @@ def test_decode_paged_llama8b_full():
 
 @pytest.mark.parametrize("heads,kvh,d,dtype", [(32, 8, 128, "bf16"), (8, 8, 64, "bf16"),
                                                 (64, 8, 64, "bf16"), (12, 12, 64, "f32"),
-                                                (16, 4, 128, "f32")])
+                                                (16, 4, 128, "f32"), (64, 2, 128, "bf16")])
 def test_decode_paged_shapes(heads, kvh, d, dtype):
     print(f"[case] decode_paged H={heads} KvH={kvh} D={d} {dtype}", flush=True)
     lengths = np.array([1, 2, 63, 64, 65, 128, 700, 1000, 513, 256], dtype=np.int64)

@@ -128,3 +128,20 @@ def sample_indices(n: int, k: int, gen: np.random.Generator) -> np.ndarray:
     if k >= n:
         return np.arange(n, dtype=np.int32)
     return np.sort(gen.choice(n, size=k, replace=False)).astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Device-side values for the large benchmark tensors (the 2.4 GB page pool):
+# torch's seeded generator on the device, one generator per role.
+# ---------------------------------------------------------------------------
+_ROLE_ID = {r: i for i, r in enumerate(_ROLES)}
+
+
+def device_normal(shape, seed: int, role: str, dtype, device="cuda"):
+    """Standard-normal values drawn on `device` from a generator seeded by
+    (seed, role), converted to `dtype` (round to nearest even)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 1000003 + _ROLE_ID[role])
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    return x.to(dtype)
