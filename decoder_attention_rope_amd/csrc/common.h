@@ -46,6 +46,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Interleave the low (high) 16-bit halves of two words: a's half in the low
+// 16 bits of the result, b's in the high 16 (one v_perm_b32).
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Online softmax with a lazy reference: the reference max moves only when a
+// new score exceeds it by more than 2^kLazyMaxLog2 (scores in log2 units), so
+// the running output rarely needs rescaling. Probabilities stay below
+// 2^kLazyMaxLog2, far inside the f32 and bf16 ranges, and the output and the
+// denominator share the reference, so the normalized result is unchanged.
+constexpr float kLazyMaxLog2 = 8.0f;
+
 // 2^x on the transcendental unit (v_exp_f32); the attention kernels only
 // evaluate it for x <= 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
