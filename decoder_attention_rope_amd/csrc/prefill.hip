@@ -32,6 +32,9 @@
 //   tile's visited key-tile range and cost (one wavefront per tile), then
 //   order the query tiles costliest first (a counting sort); workgroup index i * n_groups + g maps KV head g to the
 //   round-robin XCD g % 8, keeping one head's K/V in one XCD's L2.
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 #include "internal.h"
 
@@ -41,21 +44,20 @@ namespace {
 constexpr int kBK = 64;       // keys per tile
 constexpr int kPrepThreads = 1024;
 constexpr float kNegInf = -__builtin_huge_valf();
-#ifndef GQA_PREFILL_SETPRIO
-#define GQA_PREFILL_SETPRIO 0
-#endif
 
 struct TileSum {
   int seg_min, seg_max, pos_min, pos_max;
 };
 
 struct Plan {
-  TileSum* ksum;  // [n_kt]
-  TileSum* qsum;  // [n_qt]
-  int2* qrange;   // [n_qt] first / last key tile to visit
-  int* order;     // [n_qt] query tiles, costliest first
-  int* cost;      // [n_qt] key tiles each query tile visits
-  int n_kt, n_qt, tq, head_groups, gw;
+  TileSum* ksum;   // [n_kt]
+  TileSum* qsum;   // [n_qt]
+  int2* qrange;    // [n_qt] first / last key tile to visit
+  int* order;      // [n_qt] query tiles, costliest first
+  int* cost;       // [n_qt] key tiles each query tile visits
+  uint32_t* masks; // [n_qt][n_kg][4]: per group of 64 key tiles, a 64-bit
+                   // "visit" mask then a 64-bit "every pair allowed" mask
+  int n_kt, n_qt, n_kg, tq, head_groups, gw;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -76,6 +78,15 @@ __device__ __forceinline__ bool tiles_meet(const TileSum& q, const TileSum& k, i
   if (k.pos_min > q.pos_max) return false;
   if (window > 0 && (long long)q.pos_min - (long long)k.pos_max >= window) return false;
   return true;
+}
+
+// Every (query, key) pair of the two tiles is allowed: one segment on both
+// sides, every key position at or below every query position, all inside the
+// window, and key tile kt holds 64 real keys.
+__device__ __forceinline__ bool tiles_full(const TileSum& q, const TileSum& k, int kt, int p, int window) {
+  return (kt + 1) * kBK <= p && q.seg_min == q.seg_max && k.seg_min == k.seg_max &&
+         k.seg_min == q.seg_min && k.pos_max <= q.pos_min &&
+         (window <= 0 || (long long)q.pos_max - (long long)k.pos_min < window);
 }
 
 }  // namespace
@@ -117,8 +128,8 @@ __global__ __launch_bounds__(256) void prefill_summarize_kernel(PrefillArgs a, P
 }
 
 // ---------------------------------------------------------------------------
-// Prep 2: each query tile's visited key-tile range and cost, one wavefront per
-// query tile (the lanes test 64 key tiles at a time and reduce).
+// Prep 2: each query tile's visited key-tile range, cost and tile masks, one
+// wavefront per query tile (the lanes test 64 key tiles at a time).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void prefill_scan_kernel(PrefillArgs a, Plan pl) {
   const int wave = threadIdx.x >> 6;
@@ -127,11 +138,24 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(PrefillArgs a, Plan p
   if (qt >= pl.n_qt) return;
   const TileSum q = pl.qsum[qt];
   int first = pl.n_kt, last = -1, cnt = 0;
-  for (int kt = lane; kt < pl.n_kt; kt += 64) {
-    if (tiles_meet(q, pl.ksum[kt], a.window)) {
+  for (int g = 0; g < pl.n_kg; ++g) {
+    const int kt = g * 64 + lane;
+    bool meet = false, full = false;
+    if (kt < pl.n_kt) {
+      const TileSum k = pl.ksum[kt];
+      meet = tiles_meet(q, k, a.window);
+      full = meet && tiles_full(q, k, kt, a.p, a.window);
+    }
+    if (meet) {
       first = min(first, kt);
       last = max(last, kt);
       ++cnt;
+    }
+    const unsigned long long vm = __builtin_amdgcn_ballot_w64(meet);
+    const unsigned long long fm = __builtin_amdgcn_ballot_w64(full);
+    if (lane < 4) {
+      const unsigned long long w = lane < 2 ? vm : fm;
+      pl.masks[((size_t)qt * pl.n_kg + g) * 4 + lane] = (uint32_t)(w >> (32 * (lane & 1)));
     }
   }
 #pragma unroll
@@ -193,39 +217,94 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_order_kernel(Plan pl) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS layouts.
-//   K tile  [64 keys][D]: 16-byte granule g of row r stored at granule
-//           g ^ swk(r); the rows a group of lanes reads at once land in
-//           distinct bank groups.
-//   V^T tile [D][64 keys]: granule g (8 keys) of row d stored at g ^ swv(d).
+// LDS layouts (byte offsets; every access below is conflict-free in the
+// 64-bank, 4-byte-bank LDS of gfx950, where a 16-byte access is served 16
+// lanes at a time and an 8-byte access 32 lanes at a time).
+//   K tile   [64 rows][D], row stride 2 D + 16 bytes. Key r of the tile sits
+//            in row kappa(r), so lane l reads row l % 32 (+32): the 16 rows
+//            of a 16-lane group start 16 bytes apart modulo 256.
+//   V^T tile [D rows][64 keys], row stride 144 bytes: the 16 rows a 16-lane
+//            group reads start 16 bytes apart modulo 256, and the staging
+//            threads of a 32-lane group write 16 key groups of 2 dimension
+//            rows whose starts differ by 128 bytes modulo 256.
+// With padded (not XOR-swizzled) rows every read address is one per-lane
+// base plus a compile-time offset.
 // ---------------------------------------------------------------------------
+// Lanes l and l ^ 32 own the two key halves of one query column; these
+// combine their values (one cross-half lane swap, no LDS round trip).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N - 1, unrolled at
+// compile time (every index below selects registers, so none may be a
+// runtime value).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Key row feeding accumulator row m of a 32-key block: bits 2 and 3 swapped.
 __device__ __forceinline__ int kappa(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
-// K granule swizzle. D = 128 (16 granules per row): kappa of the row's low 4
-// bits, so the 16 rows that 16 consecutive lanes read for one operand hit 16
-// distinct granules (and any 8 consecutive lanes 8 distinct granules mod 8).
-// D = 64 (8 granules): the 8 rows of 8 consecutive lanes hit 8 granules.
+
 template <int D>
-__device__ __forceinline__ int swk(int row) {
-  return D == 128 ? kappa(row & 15) : ((row & 3) | ((row >> 1) & 4));
+struct Lds {
+  static constexpr int kStride = 2 * D + 16;       // K row stride (bytes)
+  static constexpr int vStride = 2 * kBK + 16;     // V^T row stride (bytes)
+  static constexpr int kBytes = kBK * kStride;     // one K tile
+  static constexpr int vBytes = D * vStride;       // one V^T tile
+  static constexpr int kOff(int buf) { return buf * kBytes; }
+  static constexpr int vOff(int buf) { return 2 * kBytes + buf * vBytes; }
+  static constexpr int posOff(int buf) { return 2 * kBytes + 2 * vBytes + buf * 2 * kBK * 4; }
+  static constexpr int segOff(int buf) { return posOff(buf) + kBK * 4; }
+  static constexpr int total = posOff(2);
+};
+
+typedef __attribute__((address_space(3))) char LdsByte;
+template <typename T>
+__device__ __forceinline__ T lds_ld(const LdsByte* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
 }
-__device__ __forceinline__ int swv(int d) { return (d + (d >> 3)) & 7; }
+template <typename T>
+__device__ __forceinline__ void lds_st(LdsByte* p, const T& v) {
+  *reinterpret_cast<__attribute__((address_space(3))) T*>(p) = v;
+}
+
+// Buffer resource over one key tile of a [P, kv_heads, D] tensor, starting at
+// head kh of the tile's first token and covering exactly its n_rows valid
+// rows: loads past them return zeros (dword 3 = raw, untyped 32-bit access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, long long elem_off,
+                                                            int n_rows, int row_bytes, int tail_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(static_cast<const char*>(base) + 2 * elem_off), (short)0,
+      (n_rows - 1) * row_bytes + tail_bytes, 0x00020000);
+}
+
 template <int D, int GW>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl) {
   constexpr int SUB = 4 / GW;   // query sub-tiles of 32 per workgroup
   constexpr int TQ = 32 * SUB;  // query tokens per workgroup
   constexpr int KS = D / 16;    // k-steps of QK^T over the head dim
   constexpr int MD = D / 32;    // 32-row blocks of O^T
-  constexpr int LPR = D / 8;    // staging threads per key row (16 B each)
+  constexpr int LPR = D / 8;    // 16-byte chunks per key row
   constexpr int RPT = D / 32;   // key rows staged per thread
-  static_assert(LPR * (kBK / RPT) == 256, "staging covers the tile");
+  constexpr int NA = kBK / RPT; // key groups of RPT rows
+  static_assert(LPR * NA == 256, "staging covers the tile");
+  using L = Lds<D>;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * kBK];
-  __shared__ __attribute__((aligned(16))) int sPos[2][kBK];
-  __shared__ __attribute__((aligned(16))) int sSeg[2][kBK];
+  __shared__ __attribute__((aligned(16))) char smem_raw[L::total];
+  LdsByte* smem = (LdsByte*)smem_raw;
 
   const int G = a.heads / a.kv_heads;
   const int n_groups = a.kv_heads * pl.head_groups;
@@ -250,12 +329,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
   const int q_ld = q_valid ? q_tok : P - 1;  // lanes past P read a real row
   const int my_pos = a.positions[q_ld];
   const int my_seg = a.segments[q_ld];
-  const int window = a.window;
+  // Positions are token positions in [0, 2^31): the difference of two fits
+  // in 32 bits, and an unsigned compare tests pos_k <= pos_q together with
+  // the window. Keys past P carry position INT_MIN, which fails it.
+  const uint32_t wlim = a.window > 0 ? (uint32_t)a.window : 0x80000000u;
 
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k);
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v);
-
   u32x4 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = load16(qg + ((long long)q_ld * a.heads + h) * D + ks * 16 + hf * 8);
@@ -277,193 +356,265 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
                        ld_const(reinterpret_cast<const int*>(pl.qrange), 2LL * qt + 1));
   rng.x = __builtin_amdgcn_readfirstlane(rng.x);
   rng.y = __builtin_amdgcn_readfirstlane(rng.y);
-  const TileSum qs = ld_const(pl.qsum, qt);
 
-  // Staging of one K/V tile: thread (c, ar) loads 16-byte chunk c of key rows
-  // ar * RPT .. ar * RPT + RPT - 1 (LPR threads cover a row, so a wavefront
-  // reads whole rows).
-  const int sc_c = tid % LPR;
-  const int sc_a = tid / LPR;
+  // Staging. K: thread (c, ar) loads 16-byte chunk c of key rows
+  // ar * RPT + i (LPR consecutive lanes cover a row). V: thread (av, cv) with
+  // the key group fastest, so the transposed LDS writes spread over the banks.
+  const int row_bytes = a.kv_heads * D * 2;
+  const int kc = tid % LPR, ka = tid / LPR;
+  const int va = tid % NA, vc = tid / NA;
+  int k_goff[RPT], v_goff[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    k_goff[i] = (ka * RPT + i) * row_bytes + kc * 16;
+    v_goff[i] = (va * RPT + i) * row_bytes + vc * 16;
+  }
+  const int k_wr = kappa(ka * RPT) * L::kStride + kc * 16;
+  const int v_wr = 8 * vc * L::vStride + va * RPT * 2;
+  const int k_rd = qn * L::kStride + hf * 16;
+  const int v_rd = qn * L::vStride + hf * 16;
   u32x4 kreg[RPT], vreg[RPT];
-  int pos_reg = 0, seg_reg = 0;
+  int pos_reg = 0, seg_reg = 0, staged_rows = 0;
 
   auto load_tile = [&](int kt) {
-    // Keys past P read row P - 1 (a real row); the mask drops them and
-    // their probability is exactly 0.
+    const int n_rows = min(kBK, P - kt * kBK);
+    const long long e0 = (long long)kt * kBK * a.kv_heads * D + (long long)kh * D;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(a.k, e0, n_rows, row_bytes, 2 * D);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(a.v, e0, n_rows, row_bytes, 2 * D);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int key = min(kt * kBK + sc_a * RPT + i, P - 1);
-      const long long off = ((long long)key * a.kv_heads + kh) * D + sc_c * 8;
-      kreg[i] = load16(kg + off);
-      vreg[i] = load16(vg + off);
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_goff[i], 0, 0);
+      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_goff[i], 0, 0);
     }
-    const int pkey = min(kt * kBK + (tid & (kBK - 1)), P - 1);
-    pos_reg = a.positions[pkey];
-    seg_reg = a.segments[pkey];
+    const __amdgpu_buffer_rsrc_t rp =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.positions + (long long)kt * kBK), (short)0, 4 * n_rows, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.segments + (long long)kt * kBK), (short)0, 4 * n_rows, 0x00020000);
+    const int lo = (tid & (kBK - 1)) * 4;
+    pos_reg = __builtin_amdgcn_raw_buffer_load_b32(rp, lo, 0, 0);
+    seg_reg = __builtin_amdgcn_raw_buffer_load_b32(rs, lo, 0, 0);
+    staged_rows = n_rows;
   };
 
-  auto store_tile = [&](int buf) {
-    uint16_t* k_s = sK[buf];
-    uint16_t* v_s = sV[buf];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int row = sc_a * RPT + i;
-      store16(k_s + row * D + ((sc_c ^ swk<D>(row)) * 8), kreg[i]);
+  // Walk the visited key tiles with the prepared masks: scalar bit scans,
+  // one scalar load per group of 64 key tiles. Phase 0 visits the tiles in
+  // which every pair is allowed, phase 1 the others (the online softmax does
+  // not depend on the order of the key tiles), so each phase runs one
+  // specialized loop body.
+  int vis_g = -1;
+  unsigned long long vis_m = 0, full_m = 0;
+  auto next_in = [&](int kt, int phase) {
+    while (kt <= rng.y) {
+      const int g = kt >> 6;
+      if (g != vis_g) {
+        const int* w = reinterpret_cast<const int*>(pl.masks) + ((long long)qt * pl.n_kg + g) * 4;
+        vis_m = (unsigned long long)(uint32_t)ld_const(w, 0) | ((unsigned long long)(uint32_t)ld_const(w, 1) << 32);
+        full_m = (unsigned long long)(uint32_t)ld_const(w, 2) | ((unsigned long long)(uint32_t)ld_const(w, 3) << 32);
+        vis_g = g;
+      }
+      const unsigned long long m = (phase == 0 ? full_m : (vis_m & ~full_m)) >> (kt & 63);
+      if (m != 0) return __builtin_amdgcn_readfirstlane(kt + (int)__builtin_ctzll(m));
+      kt = (g + 1) << 6;
     }
-    const int key0 = sc_a * RPT;
+    return rng.y + 1;
+  };
+  auto advance = [&](int kt, int& phase) {
+    int r = next_in(kt, phase);
+    if (r > rng.y && phase == 0) {
+      phase = 1;
+      r = next_in(rng.x, 1);
+    }
+    return r;
+  };
+
+  // One tile is 4 C matrix steps in four blocks (C = D / 16):
+  //   block 0  S^T for keys 0..31        (one accumulator chain)
+  //   block 1  S^T for keys 32..63       with the softmax of keys 0..31
+  //   block 2  P.V of keys 0..31         with the softmax of keys 32..63
+  //   block 3  P.V of keys 32..63        with the staging of the next tile
+  // On gfx950 a SIMD overlaps an MFMA with vector instructions of the same
+  // wavefront issued in its shadow (not with another wave's), so each step
+  // issues one MFMA followed by a slice of vector work, and a scheduling
+  // fence keeps that order. Matrix operands are read from LDS four steps
+  // ahead through a ring of registers. The O rescales of the lazy softmax
+  // (rare) sit between blocks 1 and 2 and between blocks 2 and 3.
+  constexpr int C = D / 16;
+  static_assert(KS == C && 2 * MD == C, "step counts");
+  u32x4 pw[4];
+  f32x16 s[2];
+  bf16x8 ring[4];
+  float tmax = kNegInf, m_use = 0.f, alpha = 1.f, psum = 0.f;
+
+  // Operand of matrix step st (0 <= st < 4 C) of the tile in kb / vb.
+  auto operand = [&](const LdsByte* kb, const LdsByte* vb, auto stc) {
+    constexpr int st = decltype(stc)::value;
+    if constexpr (st < 2 * C) {
+      constexpr int hb = st / C, ks = st % C;
+      return lds_ld<bf16x8>(kb + hb * 32 * L::kStride + ks * 32);
+    } else {
+      constexpr int hb = (st - 2 * C) / C, j = (st - 2 * C) % C;
+      constexpr int ks = 2 * hb + j / MD, md = j % MD;
+      return lds_ld<bf16x8>(vb + 32 * md * L::vStride + ks * 32);
+    }
+  };
+  auto mfma_step = [&](auto stc, const bf16x8& op) {
+    constexpr int st = decltype(stc)::value;
+    if constexpr (st < 2 * C) {
+      constexpr int hb = st / C, ks = st % C;
+      if constexpr (ks == 0)
+        s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, __builtin_bit_cast(bf16x8, qf[ks]), f32x16{}, 0, 0, 0);
+      else
+        s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, __builtin_bit_cast(bf16x8, qf[ks]), s[hb], 0, 0, 0);
+    } else {
+      constexpr int hb = (st - 2 * C) / C, j = (st - 2 * C) % C;
+      constexpr int ks = 2 * hb + j / MD, md = j % MD;
+      o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, __builtin_bit_cast(bf16x8, pw[ks]), o[md], 0, 0, 0);
+    }
+  };
+
+  // Slice c (0 <= c < C) of the mask and online-softmax update of one 32-key
+  // half (accumulator s[hb]): slice 0 masks and takes the row max, slice 1
+  // moves the lazy reference, slices 2 .. C - 1 turn pairs of scores into
+  // bf16 probabilities (pw[2 hb], pw[2 hb + 1], the B operands of P.V).
+  auto soft_slice = [&](const LdsByte* pb, auto hbc, auto cc, auto fullc) {
+    constexpr bool full = decltype(fullc)::value;
+    constexpr int hb = decltype(hbc)::value;
+    constexpr int c = decltype(cc)::value;
+    if constexpr (c == 0) {
+      if constexpr (!full) {
+        // The literal own predicate (and the window) per element.
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = sc_c * 8 + e;
-      const int w = e >> 1;
-      uint16_t* dst = v_s + d * kBK + ((((key0 >> 3) ^ swv(d)) << 3) | (key0 & 7));
+        for (int r = 0; r < 16; ++r) {
+          const int j = 32 * hb + 16 * (r >> 3) + 8 * hf + (r & 7);
+          const int kp = lds_ld<int>(pb + j * 4);
+          const int ksg = lds_ld<int>(pb + kBK * 4 + j * 4);
+          const bool ok = (ksg == my_seg) & ((uint32_t)my_pos - (uint32_t)kp < wlim);
+          s[hb][r] = ok ? s[hb][r] : kNegInf;
+        }
+      }
+      tmax = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[hb][r]);
+    } else if constexpr (c == 1) {
+      // Online softmax in the log2 domain. scale > 0, so the row max of the
+      // scaled scores is the scaled row max of the raw ones; m_run is the
+      // lazy reference (see kLazyMaxLog2).
+      tmax = pair_max(tmax) * a.scale_log2;
+      const float m_new = (tmax > m_run + kLazyMaxLog2) ? tmax : m_run;
+      m_use = (m_new == kNegInf) ? 0.f : m_new;
+      alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      psum = 0.f;
+    } else {
+      constexpr int q0 = 8 * (c - 2) / (C - 2), q1 = 8 * (c - 1) / (C - 2);
+      static_for<q1 - q0>([&](auto qc) {
+        constexpr int r = 2 * (q0 + decltype(qc)::value);
+        const float p0 = fast_exp2(__builtin_fmaf(s[hb][r], a.scale_log2, -m_use));
+        const float p1 = fast_exp2(__builtin_fmaf(s[hb][r + 1], a.scale_log2, -m_use));
+        psum += p0 + p1;
+        pw[2 * hb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+        // Materialize here: without the anchor the compiler sinks this work
+        // past the rescale branch, next to its use, out of the MFMA shadow.
+        asm volatile("" ::"v"(pw[2 * hb + (r >> 3)][(r & 7) >> 1]));
+      });
+      if constexpr (c == C - 1) l_run = l_run * alpha + psum;
+    }
+  };
+
+  // Rescale O only when some lane's reference moved.
+  auto rescale = [&](float f) {
+    if (__builtin_amdgcn_ballot_w64(f != 1.f) != 0) {
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[md][r] *= f;
+    }
+  };
+
+  // Slice c of staging the next tile (registers -> LDS buffer nb).
+  auto store_slice = [&](int nb, auto cc) {
+    constexpr int c = decltype(cc)::value;
+    LdsByte* kbw = smem + nb * L::kBytes;
+    LdsByte* vbw = smem + 2 * L::kBytes + nb * L::vBytes;
+    if constexpr (c == 0) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) lds_st(kbw + k_wr + i * L::kStride, kreg[i]);
+    }
+    constexpr int e0 = (c == 0 || c == C - 1) ? 0 : 8 * (c - 1) / (C - 2);
+    constexpr int e1 = (c == 0 || c == C - 1) ? 0 : 8 * c / (C - 2);
+    static_for<e1 - e0>([&](auto ec) {
+      constexpr int e = e0 + decltype(ec)::value;
+      constexpr int w = e >> 1;
+      LdsByte* dst = vbw + v_wr + e * L::vStride;
       if (RPT == 4) {
         u32x2 pk;
         pk[0] = (e & 1) ? pack_hi16(vreg[0][w], vreg[1 % RPT][w]) : pack_lo16(vreg[0][w], vreg[1 % RPT][w]);
         pk[1] = (e & 1) ? pack_hi16(vreg[2 % RPT][w], vreg[3 % RPT][w])
                         : pack_lo16(vreg[2 % RPT][w], vreg[3 % RPT][w]);
-        *reinterpret_cast<u32x2*>(dst) = pk;
+        lds_st(dst, pk);
       } else {
-        *reinterpret_cast<uint32_t*>(dst) =
-            (e & 1) ? pack_hi16(vreg[0][w], vreg[1 % RPT][w]) : pack_lo16(vreg[0][w], vreg[1 % RPT][w]);
+        lds_st(dst, (e & 1) ? pack_hi16(vreg[0][w], vreg[1 % RPT][w]) : pack_lo16(vreg[0][w], vreg[1 % RPT][w]));
       }
-    }
-    if (tid < kBK) {
-      sPos[buf][tid] = pos_reg;
-      sSeg[buf][tid] = seg_reg;
-    }
-  };
-
-  auto visit = [&](int kt) { return tiles_meet(qs, ld_const(pl.ksum, kt), window); };
-  auto next_visit = [&](int kt) {
-    while (kt <= rng.y && !visit(kt)) ++kt;
-    return __builtin_amdgcn_readfirstlane(kt);
-  };
-
-  // S^T = K Q^T over the tile's 64 keys (two independent accumulator chains,
-  // interleaved so consecutive matrix ops do not depend on each other).
-  u32x4 pw[4];
-  f32x16 s[2];
-  auto qk = [&](int buf) {
-    const uint16_t* k_s = sK[buf];
-    const int row0 = kappa(qn), row1 = kappa(qn) + 32;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
-    // Matrix bursts run at raised wave priority, so the other wavefront on
-    // the SIMD fills the gaps with its softmax instead of competing.
-    if (GQA_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(
-          k_s + row0 * D + (((2 * ks + hf) ^ swk<D>(row0)) * 8));
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(
-          k_s + row1 * D + (((2 * ks + hf) ^ swk<D>(row1)) * 8));
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, __builtin_bit_cast(bf16x8, qf[ks]), s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, __builtin_bit_cast(bf16x8, qf[ks]), s[1], 0, 0, 0);
-    }
-    if (GQA_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(0);
-  };
-
-  // Mask, online-softmax update; leaves the bf16 probabilities in pw (the B
-  // operand of the P.V product) and rescales the O accumulator.
-  auto softmax = [&](int buf, int kt) {
-    const TileSum ks_ = ld_const(pl.ksum, kt);
-    const bool full = (kt + 1) * kBK <= P && qs.seg_min == qs.seg_max &&
-                      ks_.seg_min == ks_.seg_max && ks_.seg_min == qs.seg_min &&
-                      ks_.pos_max <= qs.pos_min &&
-                      (window <= 0 || (long long)qs.pos_max - (long long)ks_.pos_min < window);
-    if (!full) {
-      // The literal own predicate (and the window) per element, branch-free.
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = 32 * mb + 16 * (r >> 3) + 8 * hf + (r & 7);
-          const int kp = sPos[buf][j];
-          const int ksg = sSeg[buf][j];
-          const bool ok = (kt * kBK + j < P) & (ksg == my_seg) & (kp <= my_pos) &
-                          ((window <= 0) | ((uint32_t)my_pos - (uint32_t)kp < (uint32_t)window));
-          s[mb][r] = ok ? s[mb][r] : kNegInf;
-        }
-      }
-    }
-    // Online softmax in the log2 domain. scale > 0, so the row max of the
-    // scaled scores is the scaled row max of the raw ones.
-    float tmax = kNegInf;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * a.scale_log2;
-    // m_run is the lazy reference (see kLazyMaxLog2).
-    const float m_new = (tmax > m_run + kLazyMaxLog2) ? tmax : m_run;
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float psum = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[mb][r], a.scale_log2, -m_use));
-        const float p1 = fast_exp2(__builtin_fmaf(s[mb][r + 1], a.scale_log2, -m_use));
-        psum += p0 + p1;
-        pw[2 * mb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // Rescale O only when some lane's reference moved.
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-#pragma unroll
-      for (int md = 0; md < MD; ++md)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
+    });
+    if (c == C - 1 && tid < kBK) {
+      // Applied here, once the loads have landed, not at issue time.
+      LdsByte* pbw = smem + L::posOff(nb);
+      lds_st(pbw + tid * 4, tid < staged_rows ? pos_reg : (int)0x80000000);
+      lds_st(pbw + kBK * 4 + tid * 4, seg_reg);
     }
   };
 
-  // O^T += V^T P^T over the tile's 64 keys (MD independent chains).
-  auto pv = [&](int buf) {
-    const uint16_t* v_s = sV[buf];
-    if (GQA_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 av[MD];
-#pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        const int d = 32 * md + qn;
-        av[md] = *reinterpret_cast<const bf16x8*>(v_s + d * kBK + (((2 * ks + hf) ^ swv(d)) * 8));
-      }
-#pragma unroll
-      for (int md = 0; md < MD; ++md)
-        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[md], __builtin_bit_cast(bf16x8, pw[ks]),
-                                                        o[md], 0, 0, 0);
-    }
-    if (GQA_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(0);
-  };
-
-  int cur = next_visit(rng.x);
+  int phase = 0;
+  int cur = advance(rng.x, phase);
+  int buf = 0;
   if (cur <= rng.y) {
     load_tile(cur);
-    store_tile(0);
+    static_for<C>([&](auto cc) { store_slice(0, cc); });
   }
   __syncthreads();
-  int buf = 0;
-  while (cur <= rng.y) {
-    const int nxt = next_visit(cur + 1);
-    qk(buf);
-    // The next tile's global loads fly during the softmax and P.V; its LDS
-    // buffer was last read before the previous barrier.
-    if (nxt <= rng.y) load_tile(nxt);
-    softmax(buf, cur);
-    pv(buf);
-    if (nxt <= rng.y) store_tile(buf ^ 1);
+
+  // One tile from LDS buffer buf (every pair allowed when FULL). The next
+  // tile's global loads fly during the whole tile; its LDS buffer (buf ^ 1)
+  // was last read before the previous barrier. When there is no next tile
+  // the staging writes stale registers into that buffer, which nothing
+  // reads again.
+  auto tile = [&](auto fullc) {
+    const LdsByte* kb = smem + buf * L::kBytes + k_rd;
+    const LdsByte* vb = smem + 2 * L::kBytes + buf * L::vBytes + v_rd;
+    const LdsByte* pb = smem + L::posOff(buf);
+    static_for<4>([&](auto stc) { ring[decltype(stc)::value] = operand(kb, vb, stc); });
+    static_for<4 * C>([&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      if constexpr (st == 2 * C || st == 3 * C) rescale(alpha);
+      mfma_step(stc, ring[st & 3]);
+      if constexpr (st + 4 < 4 * C) ring[st & 3] = operand(kb, vb, std::integral_constant<int, st + 4>{});
+      if constexpr (st >= C && st < 2 * C)
+        soft_slice(pb, std::integral_constant<int, 0>{}, std::integral_constant<int, st - C>{}, fullc);
+      if constexpr (st >= 2 * C && st < 3 * C)
+        soft_slice(pb, std::integral_constant<int, 1>{}, std::integral_constant<int, st - 2 * C>{}, fullc);
+      if constexpr (st >= 3 * C) store_slice(buf ^ 1, std::integral_constant<int, st - 3 * C>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
     __syncthreads();
     buf ^= 1;
+  };
+  while (cur <= rng.y && phase == 0) {
+    int nphase = phase;
+    const int nxt = advance(cur + 1, nphase);
+    if (nxt <= rng.y) load_tile(nxt);
+    tile(std::true_type{});
+    cur = nxt;
+    phase = nphase;
+  }
+  while (cur <= rng.y) {
+    const int nxt = next_in(cur + 1, 1);
+    if (nxt <= rng.y) load_tile(nxt);
+    tile(std::false_type{});
     cur = nxt;
   }
 
   // Normalize; the sink logit joins the denominator.
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = pair_sum(l_run);
   float f = 1.f, den = l_tot;
   if (a.sinks != nullptr) {
     const float s2 = bf16_to_f32(static_cast<const uint16_t*>(a.sinks)[h]) * kLog2e;
@@ -497,8 +648,10 @@ size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim) {
   (void)head_dim;
   const size_t n_kt = (size_t)(p + kBK - 1) / kBK;
   const size_t n_qt = (size_t)(p + 31) / 32;  // the smallest query tile
+  const size_t n_kg = (n_kt + 63) / 64;
   return align256(n_kt * sizeof(TileSum)) + align256(n_qt * sizeof(TileSum)) +
-         align256(n_qt * sizeof(int2)) + 2 * align256(n_qt * sizeof(int));
+         align256(n_qt * sizeof(int2)) + 2 * align256(n_qt * sizeof(int)) +
+         align256(n_qt * n_kg * 4 * sizeof(uint32_t));
 }
 
 template <int D, int GW>
@@ -525,6 +678,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   pl.qrange = reinterpret_cast<int2*>(ws + n_kt_b + q_b);
   pl.order = reinterpret_cast<int*>(ws + n_kt_b + q_b + r_b);
   pl.cost = reinterpret_cast<int*>(ws + n_kt_b + q_b + r_b + align256(n_qt_max * sizeof(int)));
+  pl.n_kg = (pl.n_kt + 63) / 64;
+  pl.masks = reinterpret_cast<uint32_t*>(ws + n_kt_b + q_b + r_b + 2 * align256(n_qt_max * sizeof(int)));
 
   const int n_tiles = pl.n_kt + pl.n_qt;
   prefill_summarize_kernel<<<dim3((n_tiles + 3) / 4), dim3(256), 0, stream>>>(a, pl);
