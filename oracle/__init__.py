@@ -60,6 +60,10 @@ def load(path=None):
                                     c_int, _D, _D]
     lib.orc_decode_paged.argtypes = [c_int, c_int, c_int, c_int, _D, _D, _D, c_int, c_int, _I,
                                      _I, c_int, c_dbl, c_int, _D, _D]
+    lib.orc_prefill_cached.argtypes = [c_int, c_int, c_int, c_int, _D, _I, _I, c_int, _D, _D, c_int,
+                                       c_dbl, c_int, _D, _D]
+    lib.orc_prefill_paged.argtypes = [c_int, c_int, c_int, c_int, _D, _I, _I, _D, _D, c_int, c_int,
+                                      _I, c_int, c_int, c_dbl, c_int, _D, _D]
     lib.orc_num_threads.restype = c_int
     lib.orc_mutation.restype = c_int
     _LIBS[path] = lib
@@ -211,6 +215,35 @@ class Oracle:
         self.lib.orc_decode_paged(r, h, kvh, d, _pd(q), _pd(pk), _pd(pv), num_pages, page_size,
                                   _pi(_i32(positions)), _pi(tb), tb.shape[1], scale, int(window),
                                   _pd(_f64(sinks)), _pd(out))
+        return out
+
+    def prefill_cached(self, q, rows, positions, cache_k, cache_v, scale=None, window=0,
+                       sinks=None):
+        """Chunk tokens over a contiguous cache: q [n, Heads, D]; token i reads
+        cache row rows[i] (None: row 0) at slots <= positions[i]."""
+        q, ck, cv = _f64(q), _f64(cache_k), _f64(cache_v)
+        n, h, d = q.shape
+        batch, kvh, max_seq = ck.shape[0], ck.shape[1], ck.shape[2]
+        scale = self.default_scale(d) if scale is None else float(scale)
+        out = np.zeros_like(q)
+        self.lib.orc_prefill_cached(n, h, kvh, d, _pd(q), _pi(_i32(rows)), _pi(_i32(positions)),
+                                    batch, _pd(ck), _pd(cv), max_seq, scale, int(window),
+                                    _pd(_f64(sinks)), _pd(out))
+        return out
+
+    def prefill_paged(self, q, rows, positions, pool_k, pool_v, table, scale=None, window=0,
+                      sinks=None):
+        """Chunk tokens over a paged pool: token i reads table row rows[i]
+        (None: row 0) at logical keys <= positions[i]."""
+        q, pk, pv = _f64(q), _f64(pool_k), _f64(pool_v)
+        n, h, d = q.shape
+        num_pages, kvh, page_size, _ = pk.shape
+        tb = _i32(table)
+        scale = self.default_scale(d) if scale is None else float(scale)
+        out = np.zeros_like(q)
+        self.lib.orc_prefill_paged(n, h, kvh, d, _pd(q), _pi(_i32(rows)), _pi(_i32(positions)),
+                                   _pd(pk), _pd(pv), num_pages, page_size, _pi(tb), tb.shape[0],
+                                   tb.shape[1], scale, int(window), _pd(_f64(sinks)), _pd(out))
         return out
 
 

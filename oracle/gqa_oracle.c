@@ -468,6 +468,102 @@ void orc_decode_paged(int R, int heads, int kv_heads, int D, const double* q,
   }
 }
 
+/* ------------------------------------------------------------------------ */
+/* `prefill<S>(x, pos)` with pos > 0 [L, N1] (reading; the page gives the    */
+/* signature only): the chunk's tokens were written into their cache row at */
+/* their positions (write_at, as `decode` does for one token), and each of  */
+/* them attends every slot s of that row with s <= its position (`seen`),   */
+/* then the window -- the prefix written by earlier calls included. Token i */
+/* uses cache row rows[i] (0 when rows is NULL); a row outside [0, batch)   */
+/* has no keys. q, out: [n, Heads, D]; caches [batch, KvHeads, max_seq, D]. */
+/* With one token per row this is decode_rows.                              */
+/* ------------------------------------------------------------------------ */
+void orc_prefill_cached(int n, int heads, int kv_heads, int D, const double* q,
+                        const int32_t* rows, const int32_t* positions, int batch,
+                        const double* cache_k, const double* cache_v, int max_seq,
+                        double scale, int window, const double* sinks, double* out) {
+  const long total = (long)n * heads;
+#pragma omp parallel
+  {
+    const double** kp = (const double**)malloc(sizeof(double*) * (size_t)(max_seq > 0 ? max_seq : 1));
+    const double** vp = (const double**)malloc(sizeof(double*) * (size_t)(max_seq > 0 ? max_seq : 1));
+#pragma omp for schedule(dynamic, 4)
+    for (long idx = 0; idx < total; ++idx) {
+      const int h = (int)(idx % heads);
+      const int i = (int)(idx / heads);
+      const int kh = kv_head_of(h, heads, kv_heads);
+#if ORC_MUTATE == 11
+      const int row = 0;
+#else
+      const int row = rows ? rows[i] : 0;
+#endif
+      const long pos = positions[i];
+      int nk = 0;
+      for (int s = 0; row >= 0 && row < batch && s < max_seq; ++s) {
+        if (!(s <= pos) || !in_window(pos, s, window)) continue;
+        kp[nk] = cache_k + (((size_t)row * kv_heads + kh) * max_seq + s) * D;
+        vp[nk] = cache_v + (((size_t)row * kv_heads + kh) * max_seq + s) * D;
+        ++nk;
+      }
+      attend(D, q + ((size_t)i * heads + h) * D, nk, kp, vp, scale, sinks != NULL,
+             sinks ? sinks[h] : 0.0, out + ((size_t)i * heads + h) * D);
+    }
+    free(kp);
+    free(vp);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* `prefill_paged<P, Rows, Pages>` [N1] (reading; signature only): token i   */
+/* of table row rows[i] at logical position positions[i] attends key t      */
+/* (0 <= t < pages * page_size) of that row iff t <= positions[i] and the   */
+/* window keeps it, key t living at page table[row, t / page_size], offset  */
+/* t % page_size (decode_paged's addressing; the chunk's own keys were      */
+/* written at their `slots` beforehand). Keys on page ids outside           */
+/* [0, num_pages) and rows outside [0, table_rows) contribute nothing. With */
+/* one token per row this is decode_paged.                                  */
+/* ------------------------------------------------------------------------ */
+void orc_prefill_paged(int n, int heads, int kv_heads, int D, const double* q,
+                       const int32_t* rows, const int32_t* positions, const double* pool_k,
+                       const double* pool_v, int num_pages, int page_size, const int32_t* table,
+                       int table_rows, int pages, double scale, int window, const double* sinks,
+                       double* out) {
+  const long total = (long)n * heads;
+  const long max_t = (long)pages * page_size;
+#pragma omp parallel
+  {
+    const double** kp = (const double**)malloc(sizeof(double*) * (size_t)(max_t > 0 ? max_t : 1));
+    const double** vp = (const double**)malloc(sizeof(double*) * (size_t)(max_t > 0 ? max_t : 1));
+#pragma omp for schedule(dynamic, 4)
+    for (long idx = 0; idx < total; ++idx) {
+      const int h = (int)(idx % heads);
+      const int i = (int)(idx / heads);
+      const int kh = kv_head_of(h, heads, kv_heads);
+      const int row = rows ? rows[i] : 0;
+      const long pos = positions[i];
+      int nk = 0;
+      for (long t = 0; row >= 0 && row < table_rows && t < max_t; ++t) {
+        if (!(t <= pos) || !in_window(pos, t, window)) continue;
+#if ORC_MUTATE == 12
+        long page = table[(size_t)row * pages + t / page_size];
+        long off = page_size - 1 - t % page_size;
+#else
+        long page = table[(size_t)row * pages + t / page_size];
+        long off = t % page_size;
+#endif
+        if (page < 0 || page >= num_pages) continue;
+        kp[nk] = pool_k + (((size_t)page * kv_heads + kh) * page_size + off) * D;
+        vp[nk] = pool_v + (((size_t)page * kv_heads + kh) * page_size + off) * D;
+        ++nk;
+      }
+      attend(D, q + ((size_t)i * heads + h) * D, nk, kp, vp, scale, sinks != NULL,
+             sinks ? sinks[h] : 0.0, out + ((size_t)i * heads + h) * D);
+    }
+    free(kp);
+    free(vp);
+  }
+}
+
 /* Threads OpenMP will use for the calls above. */
 int orc_num_threads(void) {
 #ifdef _OPENMP

@@ -28,6 +28,11 @@ instruct and gpt-oss-20b, blocks GroupedQueryAttention and SinkAttention):
                 with invalid ids excluded (checked with an explicit mask)
   writes        write-then-attend equals forward; out-of-range targets leave
                 the cache unchanged
+  chunk         chunked prefill over a cached prefix: q = 0 gives the mean of
+                exactly the attended slots of the right row; torch softmax
+                over an explicit mask (sink as an extra logit); a chunk into
+                empty rows equals `packed`; the paged form equals the same
+                cache stored contiguously; invalid pages and rows excluded
 """
 import numpy as np
 import torch
@@ -457,6 +462,114 @@ def pin_writes(o):
     assert np.all(out[0] == 0) and np.all(out[2] == 0), "no key -> 0"
 
 
+# ---------------------------------------------------------------------------
+# Chunked prefill over a cached prefix
+# ---------------------------------------------------------------------------
+def _chunk_keep(pos, cap, window):
+    """Slots a token at `pos` attends in a row of `cap` slots."""
+    t = np.arange(cap)
+    keep = t <= pos
+    if window > 0:
+        keep &= (pos - t >= 0) & (pos - t < window)
+    return keep
+
+
+def pin_chunk_cached(o):
+    rng = _rng(14)
+    batch, max_seq, h, kvh, d = 3, 24, 4, 2, 8
+    g = h // kvh
+    ck = rng.standard_normal((batch, kvh, max_seq, d))
+    cv = rng.standard_normal((batch, kvh, max_seq, d))
+    # chunk tokens of several rows, interleaved; a row outside the cache, a
+    # position past the cache, a negative position
+    rows = np.array([1, 0, 1, 2, 1, 0, 3, 2, -1, 0], dtype=np.int32)
+    pos = np.array([5, 0, 6, 23, 7, 1, 4, 30, 2, -1], dtype=np.int32)
+    n = rows.shape[0]
+    scale = o.default_scale(d)
+    for w, sk in ((0, None), (4, rng.standard_normal(h))):
+        # q = 0: uniform weights, the mean of the attended values (closed form)
+        out0 = o.prefill_cached(np.zeros((n, h, d)), rows, pos, ck, cv, window=w)
+        for i in range(n):
+            r = rows[i]
+            keep = _chunk_keep(pos[i], max_seq, w) if 0 <= r < batch else np.zeros(max_seq, bool)
+            for hh in range(h):
+                ref = cv[r, hh // g][keep].mean(0) if keep.any() else np.zeros(d)
+                _close(out0[i, hh], ref, 1e-13, "chunk over cache, q = 0 mean")
+        # random q: softmax over an explicit mask (torch), sink as an extra logit
+        q = rng.standard_normal((n, h, d))
+        out = o.prefill_cached(q, rows, pos, ck, cv, window=w, sinks=sk)
+        for i in range(n):
+            r = rows[i]
+            if not (0 <= r < batch) or not _chunk_keep(pos[i], max_seq, w).any():
+                assert np.all(out[i] == 0), "no key -> 0"
+                continue
+            keep = torch.from_numpy(_chunk_keep(pos[i], max_seq, w))
+            for hh in range(h):
+                logits = (torch.from_numpy(ck[r, hh // g]) @ torch.from_numpy(q[i, hh])) * scale
+                logits = logits.masked_fill(~keep, float("-inf"))
+                vals = torch.from_numpy(cv[r, hh // g])
+                if sk is not None:
+                    logits = torch.cat([logits, torch.tensor([sk[hh]], dtype=torch.float64)])
+                    vals = torch.cat([vals, torch.zeros(1, d, dtype=torch.float64)])
+                ref = (torch.softmax(logits, 0) @ vals).numpy()
+                _close(out[i, hh], ref, 1e-12, "chunk over cache vs explicit mask")
+    # a prompt written into empty rows and attended as one chunk is `packed`
+    lengths = [5, 3]
+    kk = rng.standard_normal((sum(lengths), kvh, d))
+    vv = rng.standard_normal((sum(lengths), kvh, d))
+    qq = rng.standard_normal((sum(lengths), h, d))
+    seg = np.repeat(np.arange(2, dtype=np.int32), lengths)
+    ppos = np.concatenate([np.arange(L, dtype=np.int32) for L in lengths])
+    ck2, cv2, _ = o.write_contiguous(kk, vv, ppos, np.full((2, kvh, 8, d), np.nan),
+                                     np.full((2, kvh, 8, d), np.nan), rows=seg)
+    a = o.prefill_cached(qq, seg, ppos, ck2, cv2)
+    b = o.packed(qq, kk, vv, ppos, seg)
+    _close(a, b, 1e-13, "chunk into empty rows == packed")
+
+
+def pin_chunk_paged(o):
+    rng = _rng(15)
+    rows_n, h, kvh, d, ps = 3, 4, 2, 8, 4
+    max_seq = 20
+    pages = max_seq // ps
+    ck = rng.standard_normal((rows_n, kvh, max_seq, d))
+    cv = rng.standard_normal((rows_n, kvh, max_seq, d))
+    num_pages = rows_n * pages + 2
+    table = rng.permutation(num_pages)[:rows_n * pages].reshape(rows_n, pages).astype(np.int32)
+    pk = np.full((num_pages, kvh, ps, d), np.nan)
+    pv = np.full((num_pages, kvh, ps, d), np.nan)
+    for r in range(rows_n):
+        for t in range(max_seq):
+            pk[table[r, t // ps], :, t % ps] = ck[r, :, t]
+            pv[table[r, t // ps], :, t % ps] = cv[r, :, t]
+    rows = np.array([2, 0, 2, 1, 0, 2], dtype=np.int32)
+    pos = np.array([17, 3, 18, 9, 4, 19], dtype=np.int32)
+    q = rng.standard_normal((rows.shape[0], h, d))
+    for w, sk in ((0, None), (6, rng.standard_normal(h))):
+        a = o.prefill_paged(q, rows, pos, pk, pv, table, window=w, sinks=sk)
+        b = o.prefill_cached(q, rows, pos, ck, cv, window=w, sinks=sk)
+        assert np.array_equal(a, b), "paged chunk differs from the same cache stored contiguously"
+    # invalid page ids and rows outside the table contribute nothing (q = 0)
+    t2 = table.copy()
+    t2[2, 3] = -1
+    t2[0, 0] = num_pages
+    rows2 = np.concatenate([rows, np.array([3], np.int32)])
+    pos2 = np.concatenate([pos, np.array([5], np.int32)])
+    out0 = o.prefill_paged(np.zeros((rows2.shape[0], h, d)), rows2, pos2, pk, pv, t2)
+    for i in range(rows2.shape[0]):
+        r = rows2[i]
+        if not (0 <= r < rows_n):
+            assert np.all(out0[i] == 0), "row outside the table -> 0"
+            continue
+        keep = _chunk_keep(pos2[i], max_seq, 0)
+        for pg in range(pages):
+            if not (0 <= t2[r, pg] < num_pages):
+                keep[pg * ps:(pg + 1) * ps] = False
+        for hh in range(h):
+            ref = cv[r, hh // (h // kvh)][keep].mean(0) if keep.any() else np.zeros(d)
+            _close(out0[i, hh], ref, 1e-13, "paged chunk, invalid pages excluded")
+
+
 ALL_PINS = {
     "rounding": pin_rounding,
     "inv_freq": pin_inv_freq,
@@ -473,6 +586,8 @@ ALL_PINS = {
     "decode_last_row": pin_decode_is_last_forward_row,
     "paged_contiguous": pin_paged_equals_contiguous,
     "writes": pin_writes,
+    "chunk_cached": pin_chunk_cached,
+    "chunk_paged": pin_chunk_paged,
 }
 
 
