@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "paged GQA decode KV GB/s + packed prefill TFLOP/s (% of MI355X peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
-SEED_DECODE, SEED_PREFILL = 3, 4
+SEED_DECODE, SEED_PREFILL, SEED_CHUNKED = 3, 4, 6
 
 
 def parse_args():
@@ -206,6 +206,55 @@ def main():
                  for i, n in enumerate(names)}
     step_ms = float(np.mean([ev[0].elapsed_time(ev[5]) for ev in evs]))
 
+    # ---------------- next row: chunked prefill over a paged prefix ----------------
+    # Timed on its own after the step (it is not part of the step): 16 rows of
+    # the Llama-3.1-8B paged pool, each with a prefix of U[1024, 7168] keys and
+    # a 512-token chunk whose K/V are written first.
+    wc = W.LLAMA8B_CHUNKED
+    ec = wc.extra
+    gc = W.streams(SEED_CHUNKED)
+    c_pre, c_rows, c_pos, c_table = W.chunked_layout(ec["rows"], ec["pre_lo"], ec["pre_hi"],
+                                                     ec["chunk"], ec["num_pages"], 64,
+                                                     gc["index"], ec["max_len"])
+    cn = len(c_pos)
+    c_pool_k = W.device_normal((ec["num_pages"], KVH, 64, D), SEED_CHUNKED, "pool_k", bf16)
+    c_pool_v = W.device_normal((ec["num_pages"], KVH, 64, D), SEED_CHUNKED, "pool_v", bf16)
+    c_q = W.device_normal((cn, H, D), SEED_CHUNKED, "q", bf16)
+    c_k = W.device_normal((cn, KVH, D), SEED_CHUNKED, "k", bf16)
+    c_v = W.device_normal((cn, KVH, D), SEED_CHUNKED, "v", bf16)
+    c_drows = torch.from_numpy(c_rows).to(dev)
+    c_dpos = torch.from_numpy(c_pos).to(dev)
+    c_dtab = torch.from_numpy(c_table).to(dev)
+    c_out = torch.empty((cn, H, D), dtype=bf16, device=dev)
+    cws_n = gqa.gqa_prefill_cached_workspace(cn, H, KVH, D)
+    c_ws = torch.empty(max(cws_n, 256), dtype=torch.uint8, device=dev)
+    gqa.gqa_rope_write_kv(cn, H, KVH, D, gqa.GQA_BF16, c_q, c_k, c_v, c_dpos, rope_tab, max_pos,
+                          gqa.GQA_CACHE_PAGED_TABLE, c_pool_k, c_pool_v, ec["num_pages"], 64,
+                          c_drows, None, c_dtab, c_table.shape[0], c_table.shape[1])
+
+    def chunked():
+        gqa.gqa_prefill_cached(cn, H, KVH, D, gqa.GQA_BF16, 0.0, 0, None, c_q, c_drows, c_dpos,
+                               gqa.GQA_CACHE_PAGED_TABLE, c_pool_k, c_pool_v, ec["num_pages"], 64,
+                               c_dtab, c_table.shape[0], c_table.shape[1], c_out, c_ws, cws_n)
+
+    for _ in range(args.warmup):
+        chunked()
+    c_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    for e0, e1 in c_ev:
+        e0.record(stream)
+        chunked()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    c_s = float(np.mean([e0.elapsed_time(e1) for e0, e1 in c_ev])) * 1e-3
+    c_flops = 4 * D * H * int(np.sum(c_pos.astype(np.int64) + 1))
+    c_tflops = c_flops / c_s / 1e12
+    chunk_roof = {"bound": "mfma", "achieved": c_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                  "unit": "TFLOP/s", "frac": c_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                  "algorithmic_flops": c_flops, "avg_us": c_s * 1e6,
+                  "workload": f"{ec['rows']} rows, prefixes U[{ec['pre_lo']}, {ec['pre_hi']}] "
+                              f"({int(c_pre.sum())} keys), chunk {ec['chunk']}, paged"}
+
     # ---------------- algorithmic work ----------------
     kv_bytes = int(np.sum(lengths)) * KVH * D * 2 * 2          # K + V of attended keys
     qo_bytes = 2 * rows * H * D * 2                              # q in, out
@@ -283,6 +332,7 @@ def main():
         "prefill_frac_of_mfma_peak": prefill_tflops / MFMA_BF16_PEAK_TFLOPS,
         "roofline": roof,
         "rooflines": {"decode_paged": dec_roof, "prefill_packed": pre_roof},
+        "next_rows": {"prefill_cached_paged": chunk_roof},
         "per_op_us": {k: v * 1e3 for k, v in per_op_ms.items()},
         "wall_s_timed": wall,
         "cpu_baseline": cpu,

@@ -18,6 +18,7 @@ __all__ = [
     "GQA_BF16", "GQA_F32", "GQA_CACHE_NONE", "GQA_CACHE_CONTIGUOUS", "GQA_CACHE_PAGED_TABLE",
     "GQA_CACHE_PAGED_SLOTS", "GQA_PAGE_SIZE",
     "gqa_rope_table", "gqa_rope_write_kv", "gqa_prefill_packed", "gqa_prefill_packed_workspace",
+    "gqa_prefill_cached", "gqa_prefill_cached_workspace",
     "gqa_decode_rows", "gqa_decode_rows_workspace", "gqa_decode_paged",
     "gqa_decode_paged_workspace", "gqa_status_string", "gqa_set_dry_run", "gqa_abi_version",
     "dtype_code",
@@ -54,6 +55,10 @@ _prefill_packed = _sig("gqa_prefill_packed", ctypes.c_int,
                        [_i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                         _vp, _vp, _sz, _vp])
 _prefill_ws = _sig("gqa_prefill_packed_workspace", _sz, [_i32, _i32, _i32, _i32])
+_prefill_cached = _sig("gqa_prefill_cached", ctypes.c_int,
+                       [_i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
+                        _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp])
+_prefill_cached_ws = _sig("gqa_prefill_cached_workspace", _sz, [_i32, _i32, _i32, _i32])
 _decode_rows = _sig("gqa_decode_rows", ctypes.c_int,
                     [_i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                      _vp, _sz, _vp])
@@ -145,6 +150,21 @@ def gqa_prefill_packed(p, heads, kv_heads, head_dim, dtype, scale, window, sinks
                            _ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(segments), _ptr(out),
                            _ptr(workspace), workspace_bytes, _stream(stream)),
            "gqa_prefill_packed")
+
+
+def gqa_prefill_cached_workspace(n, heads, kv_heads, head_dim):
+    return _prefill_cached_ws(n, heads, kv_heads, head_dim)
+
+
+def gqa_prefill_cached(n, heads, kv_heads, head_dim, dtype, scale, window, sinks, q, rows,
+                       positions, cache_kind, cache_k, cache_v, cache_dim0, cache_seq, table,
+                       table_rows, table_pages, out, workspace, workspace_bytes, stream=None):
+    _check(_prefill_cached(n, heads, kv_heads, head_dim, dtype, scale, window, _ptr(sinks),
+                           _ptr(q), _ptr(rows), _ptr(positions), cache_kind, _ptr(cache_k),
+                           _ptr(cache_v), cache_dim0, cache_seq, _ptr(table), table_rows,
+                           table_pages, _ptr(out), _ptr(workspace), workspace_bytes,
+                           _stream(stream)),
+           "gqa_prefill_cached")
 
 
 def gqa_decode_rows_workspace(batch, heads, kv_heads, head_dim, max_seq):

@@ -152,7 +152,7 @@ int gqa_prefill_packed(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_
   if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GQA_ERR_WORKSPACE;
   if (g_dry_run.load()) return GQA_OK;
-  gqa::PrefillArgs a;
+  gqa::PrefillArgs a{};
   a.p = p;
   a.heads = heads;
   a.kv_heads = kv_heads;
@@ -169,6 +169,74 @@ int gqa_prefill_packed(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_
   a.out = out;
   a.ws = workspace;
   a.ws_bytes = workspace_bytes;
+  a.src = gqa::kSrcPacked;
+  return hip_status(gqa::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t gqa_prefill_cached_workspace(int32_t n, int32_t heads, int32_t kv_heads,
+                                    int32_t head_dim) {
+  if (n <= 0) return 0;
+  return gqa::prefill_workspace_bytes(n, heads, kv_heads, head_dim);
+}
+
+int gqa_prefill_cached(int32_t n, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                       int32_t dtype, float scale, int32_t window, const void* sinks,
+                       const void* q, const int32_t* rows, const int32_t* positions,
+                       int32_t cache_kind, const void* cache_k, const void* cache_v,
+                       int32_t cache_dim0, int32_t cache_seq, const int32_t* table,
+                       int32_t table_rows, int32_t table_pages, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (n < 0 || window < 0) return GQA_ERR_INVALID_ARG;
+  int st = check_heads(heads, kv_heads, head_dim, dtype);
+  if (st != GQA_OK) return st;
+  if (!std::isfinite(scale) || scale < 0.0f) return GQA_ERR_INVALID_ARG;
+  if (q == nullptr || positions == nullptr || cache_k == nullptr || cache_v == nullptr ||
+      out == nullptr)
+    return GQA_ERR_INVALID_ARG;
+  if (cache_kind != GQA_CACHE_CONTIGUOUS && cache_kind != GQA_CACHE_PAGED_TABLE)
+    return GQA_ERR_INVALID_ARG;
+  if (cache_dim0 <= 0) return GQA_ERR_INVALID_ARG;
+  if (cache_kind == GQA_CACHE_CONTIGUOUS && cache_seq <= 0) return GQA_ERR_INVALID_ARG;
+  if (cache_kind == GQA_CACHE_PAGED_TABLE) {
+    if (cache_seq != GQA_PAGE_SIZE || table == nullptr || table_rows <= 0 || table_pages <= 0)
+      return GQA_ERR_INVALID_ARG;
+    if ((long long)table_pages * GQA_PAGE_SIZE > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
+  }
+  if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  if (n == 0) return GQA_OK;
+  const size_t need = gqa::prefill_workspace_bytes(n, heads, kv_heads, head_dim);
+  if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GQA_ERR_WORKSPACE;
+  if (g_dry_run.load()) return GQA_OK;
+  gqa::PrefillArgs a{};
+  a.p = n;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.head_dim = head_dim;
+  a.dtype = dtype;
+  a.scale_log2 = effective_scale_log2(scale, head_dim);
+  a.window = window;
+  a.sinks = sinks;
+  a.q = q;
+  a.k = cache_k;
+  a.v = cache_v;
+  a.positions = positions;
+  a.segments = rows;
+  a.out = out;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  if (cache_kind == GQA_CACHE_CONTIGUOUS) {
+    a.src = gqa::kSrcContiguous;
+    a.cache_rows = cache_dim0;
+    a.cap = cache_seq;
+  } else {
+    a.src = gqa::kSrcPaged;
+    a.cache_rows = table_rows;
+    a.cap = table_pages * GQA_PAGE_SIZE;
+    a.table = table;
+    a.table_pages = table_pages;
+    a.num_pages = cache_dim0;
+  }
   return hip_status(gqa::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 

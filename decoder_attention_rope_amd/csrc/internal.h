@@ -53,19 +53,29 @@ struct DecodeArgs {
   int nsplit;     // splits per row
 };
 
+// Keys of the prefill: the packed tokens themselves, or a cache the tokens
+// (and an earlier prefix) were written into.
+enum PrefillSource { kSrcPacked = 0, kSrcContiguous = 1, kSrcPaged = 2 };
+
 struct PrefillArgs {
   int p, heads, kv_heads, head_dim, dtype;
   float scale_log2;
   int window;
   const void* sinks;
   const void* q;
-  const void* k;
+  const void* k;         // packed k [p, kv_heads, D], or cache_k / pool_k
   const void* v;
   const int32_t* positions;
-  const int32_t* segments;
+  const int32_t* segments;  // packed: segment ids; cache: cache / table row (may be null = 0)
   void* out;
   void* ws;
   size_t ws_bytes;
+  int src;               // PrefillSource
+  int cache_rows;        // cache: batch (contiguous) or table rows (paged)
+  int cap;               // cache: key slots per row (max_seq, or table_pages * 64)
+  const int32_t* table;  // paged: [cache_rows, table_pages]
+  int table_pages;
+  int num_pages;
 };
 
 hipError_t launch_rope_table(int head_dim, int max_pos, float theta, int dtype, void* table,

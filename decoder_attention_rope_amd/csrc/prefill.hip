@@ -58,6 +58,7 @@ struct Plan {
   uint32_t* masks; // [n_qt][n_kg][4]: per group of 64 key tiles, a 64-bit
                    // "visit" mask then a 64-bit "every pair allowed" mask
   int n_kt, n_qt, n_kg, tq, head_groups, gw;
+  int max_cost;    // costs are clamped to [0, max_cost] for the ordering
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(256) void prefill_summarize_kernel(PrefillArgs a, P
   const int hi = min(a.p, lo + len);
   int smin = 0x7fffffff, smax = (int)0x80000000, pmin = 0x7fffffff, pmax = (int)0x80000000;
   for (int t = lo + lane; t < hi; t += 64) {
-    const int sg = a.segments[t], ps = a.positions[t];
+    const int sg = a.segments ? a.segments[t] : 0, ps = a.positions[t];
     smin = min(smin, sg);
     smax = max(smax, sg);
     pmin = min(pmin, ps);
@@ -137,6 +138,20 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(PrefillArgs a, Plan p
   const int qt = blockIdx.x * 4 + wave;
   if (qt >= pl.n_qt) return;
   const TileSum q = pl.qsum[qt];
+  if (a.src != kSrcPacked) {
+    // Cache keys: rows [seg_min, seg_max] of the cache, key tiles from the
+    // window's first slot to the last slot any query may see.
+    if (lane == 0) {
+      const int r_lo = max(q.seg_min, 0), r_hi = min(q.seg_max, a.cache_rows - 1);
+      const int last_slot = min(q.pos_max, a.cap - 1);
+      const int khi = last_slot >= 0 ? last_slot / kBK : -1;
+      const int klo = a.window > 0 ? max(0, q.pos_min - a.window + 1) / kBK : 0;
+      const long long c = (r_hi >= r_lo && khi >= klo) ? (long long)(r_hi - r_lo + 1) * (khi - klo + 1) : 0;
+      pl.qrange[qt] = make_int2(0, -1);
+      pl.cost[qt] = (int)min(c, (long long)pl.max_cost);
+    }
+    return;
+  }
   int first = pl.n_kt, last = -1, cnt = 0;
   for (int g = 0; g < pl.n_kg; ++g) {
     const int kt = g * 64 + lane;
@@ -181,16 +196,16 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_order_kernel(Plan pl) {
   __shared__ int start[kMaxCostBins + 1];
   __shared__ int part[kPrepThreads];
   const int tid = threadIdx.x;
-  const int nb = pl.n_kt + 1;  // costs 0 .. n_kt
+  const int nb = pl.max_cost + 1;  // costs 0 .. max_cost
   if (nb > kMaxCostBins) {
     for (int i = tid; i < pl.n_qt; i += kPrepThreads) pl.order[i] = i;
     return;
   }
   for (int i = tid; i < nb; i += kPrepThreads) start[i] = 0;
   __syncthreads();
-  for (int i = tid; i < pl.n_qt; i += kPrepThreads) atomicAdd(&start[pl.n_kt - pl.cost[i]], 1);
+  for (int i = tid; i < pl.n_qt; i += kPrepThreads) atomicAdd(&start[pl.max_cost - pl.cost[i]], 1);
   __syncthreads();
-  // Exclusive scan over bins (bin b = cost n_kt - b, so costly tiles first):
+  // Exclusive scan over bins (bin b = cost max_cost - b, so costly tiles first):
   // each thread sums a run of bins, a block scan of the run sums, then the
   // runs are rewritten as exclusive offsets.
   const int per = (nb + kPrepThreads - 1) / kPrepThreads;
@@ -213,7 +228,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_order_kernel(Plan pl) {
   }
   __syncthreads();
   for (int i = tid; i < pl.n_qt; i += kPrepThreads)
-    pl.order[atomicAdd(&start[pl.n_kt - pl.cost[i]], 1)] = i;
+    pl.order[atomicAdd(&start[pl.max_cost - pl.cost[i]], 1)] = i;
 }
 
 // ---------------------------------------------------------------------------
@@ -291,7 +306,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, lo
       (n_rows - 1) * row_bytes + tail_bytes, 0x00020000);
 }
 
-template <int D, int GW>
+template <int D, int GW, int SRC>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl) {
   constexpr int SUB = 4 / GW;   // query sub-tiles of 32 per workgroup
   constexpr int TQ = 32 * SUB;  // query tokens per workgroup
@@ -328,11 +343,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
   const bool q_valid = q_tok < P;
   const int q_ld = q_valid ? q_tok : P - 1;  // lanes past P read a real row
   const int my_pos = a.positions[q_ld];
-  const int my_seg = a.segments[q_ld];
-  // Positions are token positions in [0, 2^31): the difference of two fits
-  // in 32 bits, and an unsigned compare tests pos_k <= pos_q together with
-  // the window. Keys past P carry position INT_MIN, which fails it.
+  const int my_seg = SRC == kSrcPacked || a.segments ? a.segments[q_ld] : 0;
+  // Packed keys: positions are token positions in [0, 2^31), so the
+  // difference of two fits in 32 bits and an unsigned compare tests
+  // pos_k <= pos_q together with the window. Keys past P carry position
+  // INT_MIN, which fails it.
   const uint32_t wlim = a.window > 0 ? (uint32_t)a.window : 0x80000000u;
+  // Cache keys: this query sees key slots [my_lo, my_hi] of cache row my_seg
+  // (empty for a row outside the cache).
+  const int my_hi = (my_seg >= 0 && my_seg < a.cache_rows) ? min(my_pos, a.cap - 1) : -1;
+  const int my_lo = a.window > 0 ? max(my_pos - a.window + 1, 0) : 0;
 
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
   u32x4 qf[KS];
@@ -360,7 +380,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
   // Staging. K: thread (c, ar) loads 16-byte chunk c of key rows
   // ar * RPT + i (LPR consecutive lanes cover a row). V: thread (av, cv) with
   // the key group fastest, so the transposed LDS writes spread over the banks.
-  const int row_bytes = a.kv_heads * D * 2;
+  const int row_bytes = SRC == kSrcPacked ? a.kv_heads * D * 2 : D * 2;
   const int kc = tid % LPR, ka = tid / LPR;
   const int va = tid % NA, vc = tid / NA;
   int k_goff[RPT], v_goff[RPT];
@@ -376,7 +396,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
   u32x4 kreg[RPT], vreg[RPT];
   int pos_reg = 0, seg_reg = 0, staged_rows = 0;
 
-  auto load_tile = [&](int kt) {
+  // A key tile: tile index kt (64 keys) of cache row r, at pool page `page`.
+  struct TileRef {
+    int kt, r, page, rows;  // rows: cache slots of the tile anyone may see
+  };
+  auto load_tile = [&](TileRef t) {
+    const int kt = t.kt;
+    if constexpr (SRC != kSrcPacked) {
+      // 64 key slots of one cache plane (contiguous rows of D elements).
+      const int n_rows = t.rows;
+      const long long e0 = SRC == kSrcPaged
+                               ? ((long long)t.page * a.kv_heads + kh) * kBK * D
+                               : (((long long)t.r * a.kv_heads + kh) * a.cap + (long long)kt * kBK) * D;
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(a.k, e0, n_rows, row_bytes, 2 * D);
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(a.v, e0, n_rows, row_bytes, 2 * D);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_goff[i], 0, 0);
+        vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_goff[i], 0, 0);
+      }
+      return;
+    }
     const int n_rows = min(kBK, P - kt * kBK);
     const long long e0 = (long long)kt * kBK * a.kv_heads * D + (long long)kh * D;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(a.k, e0, n_rows, row_bytes, 2 * D);
@@ -425,6 +465,139 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
       r = next_in(rng.x, 1);
     }
     return r;
+  };
+
+  // Cache keys. Once per workgroup: the distinct cache rows of the query
+  // tile's tokens, each with the smallest and largest position among them
+  // (a row's token is its leader if no earlier token of the tile has the same
+  // row; leaders are flagged in a 128-bit mask, so the walk is deterministic).
+  // A row's key tiles run from the window's first slot to its largest
+  // position; loads past that position return zeros (slots nobody sees may
+  // hold anything). When the tile holds one row, the key tiles [f_lo, f_hi]
+  // are fully allowed for every query. Phase 0 walks those, phase 1 the
+  // rest; tiles on invalid pages are skipped (they hold no keys).
+  __shared__ int sTokRow[SRC == kSrcPacked ? 1 : TQ];
+  __shared__ int sTokLo[SRC == kSrcPacked ? 1 : TQ];
+  __shared__ int sTokHi[SRC == kSrcPacked ? 1 : TQ];
+  __shared__ unsigned long long sLead[2];
+  unsigned long long lead0 = 0, lead1 = 0;
+  if constexpr (SRC != kSrcPacked) {
+    const int t = qt * TQ + tid;
+    const bool tok = tid < TQ && t < P;
+    const int trow = tok ? (a.segments ? a.segments[t] : 0) : -1;
+    const int tpos = tok ? a.positions[t] : 0;
+    const bool row_ok = tok && trow >= 0 && trow < a.cache_rows;
+    if (tid < TQ) {
+      sTokRow[tid] = row_ok ? trow : -1;
+      sTokLo[tid] = tpos;
+    }
+    __syncthreads();
+    bool lead = row_ok;
+    int lo = tpos, hi = tpos;
+    if (row_ok) {
+      for (int u = 0; u < TQ; ++u) {
+        const int ru = sTokRow[u];
+        if (ru != trow) continue;
+        if (u < tid) lead = false;
+        lo = min(lo, sTokLo[u]);
+        hi = max(hi, sTokLo[u]);
+      }
+    }
+    const unsigned long long bal = __builtin_amdgcn_ballot_w64(lead);
+    __syncthreads();
+    if (tid < TQ) {
+      sTokLo[tid] = lo;
+      sTokHi[tid] = hi;
+    }
+    if (lane == 0 && wave < 2) sLead[wave] = bal;
+    __syncthreads();
+    lead0 = sLead[0];
+    lead1 = TQ > 64 ? sLead[1] : 0ull;
+  }
+  const int n_lead = __builtin_popcountll(lead0) + __builtin_popcountll(lead1);
+  const bool c_single = n_lead == 1;
+  // Walk state: current leader token u, its row, key-tile range, last slot.
+  int c_phase = 0, c_u = -1, c_row = 0, c_klo = 0, c_khi = -1, c_last = -1, c_kt = 0;
+  int c_flo = 0, c_fhi = -1;
+  auto next_row = [&]() {
+    // Next leader after c_u (bit scans over the two 64-bit halves).
+    const int from = c_u + 1;
+    int u = -1;
+    if (from < 64) {
+      const unsigned long long m = from == 0 ? lead0 : (lead0 >> from) << from;
+      if (m) u = __builtin_ctzll(m);
+    }
+    if (u < 0 && from < 128) {
+      const int f1 = max(from - 64, 0);
+      const unsigned long long m = f1 == 0 ? lead1 : (f1 >= 64 ? 0ull : (lead1 >> f1) << f1);
+      if (m) u = 64 + __builtin_ctzll(m);
+    }
+    c_u = u < 0 ? 128 : u;
+    if (u < 0) return false;
+    c_row = __builtin_amdgcn_readfirstlane(sTokRow[u]);
+    const int lo = __builtin_amdgcn_readfirstlane(sTokLo[u]);
+    const int hi = __builtin_amdgcn_readfirstlane(sTokHi[u]);
+    c_last = min(hi, a.cap - 1);
+    c_khi = c_last >= 0 ? c_last / kBK : -1;
+    c_klo = a.window > 0 ? max(0, lo - a.window + 1) / kBK : 0;
+    c_flo = max(c_klo, a.window > 0 ? (max(hi - a.window + 1, 0) + kBK - 1) / kBK : 0);
+    c_fhi = min(c_khi, c_single ? (min(lo, a.cap - 1) + 1) / kBK - 1 : -1);
+    return true;
+  };
+  // Page ids of 64 consecutive key tiles of one table row, one per lane.
+  int tab_row = -1, tab_base = 0, tab_v = -1;
+  auto page_of = [&](int r, int kt) {
+    if (r != tab_row || kt < tab_base || kt >= tab_base + 64) {
+      tab_row = r;
+      tab_base = kt & ~63;
+      const int idx = tab_base + lane;
+      tab_v = idx < a.table_pages ? a.table[(long long)r * a.table_pages + idx] : -1;
+    }
+    return __builtin_amdgcn_readlane(tab_v, kt - tab_base);
+  };
+  bool c_started = false;
+  auto cache_next = [&](int& phase) {
+    TileRef t{-1, 0, 0, 0};
+    if (!c_started) {
+      c_started = true;
+      c_phase = c_single ? 0 : 1;
+      if (next_row()) c_kt = c_phase == 0 ? c_flo : c_klo;
+    }
+    for (;;) {
+      if (c_u >= 128) break;
+      if (c_phase == 0) {
+        if (c_kt > c_fhi) {
+          // Phase 1 restarts the single row, skipping the full range.
+          c_phase = 1;
+          c_kt = c_klo;
+          continue;
+        }
+      } else {
+        if (c_kt > c_khi) {
+          if (!next_row()) break;
+          c_kt = c_klo;
+          continue;
+        }
+        if (c_single && c_kt >= c_flo && c_kt <= c_fhi) {
+          c_kt = c_fhi + 1;
+          continue;
+        }
+      }
+      const int kt = c_kt++;
+      int page = 0;
+      if constexpr (SRC == kSrcPaged) {
+        page = page_of(c_row, kt);
+        if (page < 0 || page >= a.num_pages) continue;
+      }
+      t = TileRef{kt, c_row, page, min(kBK, c_last - kt * kBK + 1)};
+      break;
+    }
+    phase = c_phase;
+    t.kt = __builtin_amdgcn_readfirstlane(t.kt);
+    t.r = __builtin_amdgcn_readfirstlane(t.r);
+    t.page = __builtin_amdgcn_readfirstlane(t.page);
+    t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+    return t;
   };
 
   // One tile is 4 C matrix steps in four blocks (C = D / 16):
@@ -476,7 +649,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
   // half (accumulator s[hb]): slice 0 masks and takes the row max, slice 1
   // moves the lazy reference, slices 2 .. C - 1 turn pairs of scores into
   // bf16 probabilities (pw[2 hb], pw[2 hb + 1], the B operands of P.V).
-  auto soft_slice = [&](const LdsByte* pb, auto hbc, auto cc, auto fullc) {
+  auto soft_slice = [&](const LdsByte* pb, int lo_j, int hi_j, auto hbc, auto cc, auto fullc) {
     constexpr bool full = decltype(fullc)::value;
     constexpr int hb = decltype(hbc)::value;
     constexpr int c = decltype(cc)::value;
@@ -486,9 +659,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = 32 * hb + 16 * (r >> 3) + 8 * hf + (r & 7);
-          const int kp = lds_ld<int>(pb + j * 4);
-          const int ksg = lds_ld<int>(pb + kBK * 4 + j * 4);
-          const bool ok = (ksg == my_seg) & ((uint32_t)my_pos - (uint32_t)kp < wlim);
+          bool ok;
+          if constexpr (SRC == kSrcPacked) {
+            const int kp = lds_ld<int>(pb + j * 4);
+            const int ksg = lds_ld<int>(pb + kBK * 4 + j * 4);
+            ok = (ksg == my_seg) & ((uint32_t)my_pos - (uint32_t)kp < wlim);
+          } else {
+            // Key slot kt * 64 + j of the tile's row.
+            ok = (j >= lo_j) & (j <= hi_j);
+          }
           s[hb][r] = ok ? s[hb][r] : kNegInf;
         }
       }
@@ -556,7 +735,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
         lds_st(dst, (e & 1) ? pack_hi16(vreg[0][w], vreg[1 % RPT][w]) : pack_lo16(vreg[0][w], vreg[1 % RPT][w]));
       }
     });
-    if (c == C - 1 && tid < kBK) {
+    if (SRC == kSrcPacked && c == C - 1 && tid < kBK) {
       // Applied here, once the loads have landed, not at issue time.
       LdsByte* pbw = smem + L::posOff(nb);
       lds_st(pbw + tid * 4, tid < staged_rows ? pos_reg : (int)0x80000000);
@@ -564,10 +743,29 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
     }
   };
 
+  // The first tile, then the iteration: phase 0 (every pair allowed) and
+  // phase 1 (masked) tiles in turn.
+  auto first_tile = [&](int& phase) {
+    if constexpr (SRC == kSrcPacked) {
+      phase = 0;
+      return TileRef{advance(rng.x, phase), 0, 0, 0};
+    } else {
+      return cache_next(phase);
+    }
+  };
+  auto next_tile = [&](TileRef cur, int& phase) {
+    if constexpr (SRC == kSrcPacked) {
+      return TileRef{advance(cur.kt + 1, phase), 0, 0, 0};
+    } else {
+      return cache_next(phase);
+    }
+  };
+  auto valid = [&](TileRef t) { return SRC == kSrcPacked ? t.kt <= rng.y : t.kt >= 0; };
+
   int phase = 0;
-  int cur = advance(rng.x, phase);
+  TileRef cur = first_tile(phase);
   int buf = 0;
-  if (cur <= rng.y) {
+  if (valid(cur)) {
     load_tile(cur);
     static_for<C>([&](auto cc) { store_slice(0, cc); });
   }
@@ -578,10 +776,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
   // was last read before the previous barrier. When there is no next tile
   // the staging writes stale registers into that buffer, which nothing
   // reads again.
-  auto tile = [&](auto fullc) {
+  auto tile = [&](auto fullc, TileRef t) {
     const LdsByte* kb = smem + buf * L::kBytes + k_rd;
     const LdsByte* vb = smem + 2 * L::kBytes + buf * L::vBytes + v_rd;
     const LdsByte* pb = smem + L::posOff(buf);
+    // Cache keys: this lane's visible slots relative to the tile.
+    const int lo_j = my_lo - t.kt * kBK;
+    const int hi_j = (t.r == my_seg ? my_hi : -1) - t.kt * kBK;
     static_for<4>([&](auto stc) { ring[decltype(stc)::value] = operand(kb, vb, stc); });
     static_for<4 * C>([&](auto stc) {
       constexpr int st = decltype(stc)::value;
@@ -589,27 +790,29 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
       mfma_step(stc, ring[st & 3]);
       if constexpr (st + 4 < 4 * C) ring[st & 3] = operand(kb, vb, std::integral_constant<int, st + 4>{});
       if constexpr (st >= C && st < 2 * C)
-        soft_slice(pb, std::integral_constant<int, 0>{}, std::integral_constant<int, st - C>{}, fullc);
+        soft_slice(pb, lo_j, hi_j, std::integral_constant<int, 0>{}, std::integral_constant<int, st - C>{}, fullc);
       if constexpr (st >= 2 * C && st < 3 * C)
-        soft_slice(pb, std::integral_constant<int, 1>{}, std::integral_constant<int, st - 2 * C>{}, fullc);
+        soft_slice(pb, lo_j, hi_j, std::integral_constant<int, 1>{}, std::integral_constant<int, st - 2 * C>{},
+                   fullc);
       if constexpr (st >= 3 * C) store_slice(buf ^ 1, std::integral_constant<int, st - 3 * C>{});
       __builtin_amdgcn_sched_barrier(0);
     });
     __syncthreads();
     buf ^= 1;
   };
-  while (cur <= rng.y && phase == 0) {
+  while (valid(cur) && phase == 0) {
     int nphase = phase;
-    const int nxt = advance(cur + 1, nphase);
-    if (nxt <= rng.y) load_tile(nxt);
-    tile(std::true_type{});
+    const TileRef nxt = next_tile(cur, nphase);
+    if (valid(nxt)) load_tile(nxt);
+    tile(std::true_type{}, cur);
     cur = nxt;
     phase = nphase;
   }
-  while (cur <= rng.y) {
-    const int nxt = next_in(cur + 1, 1);
-    if (nxt <= rng.y) load_tile(nxt);
-    tile(std::false_type{});
+  while (valid(cur)) {
+    int nphase = 1;
+    const TileRef nxt = next_tile(cur, nphase);
+    if (valid(nxt)) load_tile(nxt);
+    tile(std::false_type{}, cur);
     cur = nxt;
   }
 
@@ -657,7 +860,10 @@ size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim) {
 template <int D, int GW>
 static void launch_main(const PrefillArgs& a, const Plan& pl, hipStream_t stream) {
   const int n_groups = a.kv_heads * pl.head_groups;
-  prefill_kernel<D, GW><<<dim3(pl.n_qt * n_groups), dim3(256), 0, stream>>>(a, pl);
+  const dim3 grid(pl.n_qt * n_groups), block(256);
+  if (a.src == kSrcContiguous) prefill_kernel<D, GW, kSrcContiguous><<<grid, block, 0, stream>>>(a, pl);
+  else if (a.src == kSrcPaged) prefill_kernel<D, GW, kSrcPaged><<<grid, block, 0, stream>>>(a, pl);
+  else prefill_kernel<D, GW, kSrcPacked><<<grid, block, 0, stream>>>(a, pl);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
@@ -666,8 +872,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   pl.gw = group_width(G);
   pl.head_groups = G / pl.gw;
   pl.tq = 32 * (4 / pl.gw);
-  pl.n_kt = (a.p + kBK - 1) / kBK;
+  // Cache keys need no key-tile summaries or masks.
+  pl.n_kt = a.src == kSrcPacked ? (a.p + kBK - 1) / kBK : 0;
   pl.n_qt = (a.p + pl.tq - 1) / pl.tq;
+  pl.max_cost = a.src == kSrcPacked ? pl.n_kt : min(kMaxCostBins - 1, a.cap / kBK + 1);
   const size_t n_kt_b = align256((size_t)pl.n_kt * sizeof(TileSum));
   const size_t n_qt_max = (size_t)(a.p + 31) / 32;
   const size_t q_b = align256(n_qt_max * sizeof(TileSum));

@@ -150,6 +150,40 @@ size_t gqa_prefill_packed_workspace(int32_t p, int32_t heads, int32_t kv_heads,
                                     int32_t head_dim);
 
 /*
+ * gqa_prefill_cached -- chunked prefill over a cached prefix: the attention
+ * of `prefill<S>(x, pos)` with pos > 0 (contiguous cache) and of
+ * `prefill_paged` (paged pool) of the GroupedQueryAttention block, llama-
+ * 3.1-8b-instruct card, serving signatures. Those pages give signatures
+ * only; the reading taken: token i, whose k and v were already written into
+ * its cache row by gqa_rope_write_kv (call it first, on the same stream),
+ * attends key slot s of cache row rows[i] iff s <= positions[i] and the
+ * window keeps it -- the prefix written by earlier calls included.
+ *   cache_kind GQA_CACHE_CONTIGUOUS: cache_k, cache_v [cache_dim0 = batch,
+ *     kv_heads, cache_seq = max_seq, D]; rows[i] is the batch row.
+ *   cache_kind GQA_CACHE_PAGED_TABLE: pool_k, pool_v [cache_dim0 =
+ *     num_pages, kv_heads, cache_seq = 64, D]; logical slot s of table row
+ *     r is page table[r, s / 64], offset s % 64 (table [table_rows,
+ *     table_pages]); rows[i] is the table row.
+ *   q, out [n, heads, D] of T (q already rotated); rows, positions [n]
+ *   (rows NULL: every token reads row 0). A row outside the cache / table
+ *   gives no keys (output 0); keys on page ids outside [0, num_pages)
+ *   contribute nothing. Built for T = bf16, D in {64, 128}. Tokens of one
+ *   row kept contiguous in n order make the query tiles single-row (fast).
+ *   workspace: at least gqa_prefill_cached_workspace(n, ...) bytes,
+ *   256-byte aligned. Errors as gqa_prefill_packed.
+ */
+int gqa_prefill_cached(int32_t n, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                       int32_t dtype, float scale, int32_t window, const void* sinks,
+                       const void* q, const int32_t* rows, const int32_t* positions,
+                       int32_t cache_kind, const void* cache_k, const void* cache_v,
+                       int32_t cache_dim0, int32_t cache_seq, const int32_t* table,
+                       int32_t table_rows, int32_t table_pages, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+size_t gqa_prefill_cached_workspace(int32_t n, int32_t heads, int32_t kv_heads,
+                                    int32_t head_dim);
+
+/*
  * gqa_decode_rows -- `decode` / decode_rows: row b's query attends every slot
  * s of its cache row with s <= positions[b] (seen = iota(MaxSeq) <= pos) and
  * inside the window; slots past positions[b] are never read. A position at or

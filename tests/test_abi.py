@@ -166,6 +166,34 @@ def test_entry_point_argument_checks(g):
             8, 8, 256, 10 ** 12)
 
 
+def test_prefill_cached_argument_checks(g):
+    bad_arg, unsup, ws_err = _codes(g)
+    cont, paged = g.GQA_CACHE_CONTIGUOUS, g.GQA_CACHE_PAGED_TABLE
+    nb = g.gqa_prefill_cached_workspace(10, 8, 8, 64)
+    assert nb > 0 and g.gqa_prefill_cached_workspace(0, 8, 8, 64) == 0
+
+    def call(status, n=10, dtype=0, q=8, pos=8, kind=cont, dim0=4, seq=32, table=None, trows=0,
+             tpages=0, ws=256, wsb=None, window=0):
+        _expect(g, status, g.gqa_prefill_cached, n, 8, 8, 64, dtype, 0.0, window, None, q, 8, pos,
+                kind, 8, 8, dim0, seq, table, trows, tpages, 8, ws, nb if wsb is None else wsb)
+
+    call(g.GQA_OK)                                           # contiguous
+    call(g.GQA_OK, kind=paged, seq=64, table=8, trows=2, tpages=3)
+    call(g.GQA_OK, n=0, ws=None, wsb=0)                      # empty is fine
+    call(bad_arg, q=None)
+    call(bad_arg, pos=None)
+    call(bad_arg, window=-1)
+    call(bad_arg, kind=g.GQA_CACHE_PAGED_SLOTS)             # slots address writes only
+    call(bad_arg, seq=0)
+    call(bad_arg, dim0=0)
+    call(bad_arg, kind=paged, seq=32, table=8, trows=2, tpages=3)   # pages hold 64 slots
+    call(bad_arg, kind=paged, seq=64, table=None, trows=2, tpages=3)
+    call(bad_arg, kind=paged, seq=64, table=8, trows=2, tpages=2 ** 26)
+    call(unsup, dtype=1)                                     # bf16 only
+    call(ws_err, wsb=16)
+    call(ws_err, ws=257)
+
+
 def test_workspace_sizes(g):
     assert g.gqa_decode_rows_workspace(0, 8, 8, 64, 10) == 0
     a = g.gqa_decode_paged_workspace(64, 128, 32, 8, 128)

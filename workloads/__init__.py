@@ -71,6 +71,12 @@ GPT_OSS_SINK = Workload("gpt-oss-20b SinkAttention bf16, prefill 4096 + 256 deco
                         64, 8, 64, "bf16", 500000.0,
                         dict(prefill=4096, decode_steps=256, windows=(128, 0), max_seq=4352))
 
+LLAMA8B_CHUNKED = Workload("llama-3.1-8b chunked prefill over a paged prefix bf16, Rows 16, "
+                           "prefix U[1024,7168], chunk 512",
+                           32, 8, 128, "bf16", 500000.0,
+                           dict(rows=16, pre_lo=1024, pre_hi=7168, chunk=512, num_pages=2200,
+                                max_len=8192))
+
 ALL = (TINY_LLAMA, GPT2_DECODE_ROWS, LLAMA8B_PAGED, LLAMA8B_PACKED, GPT_OSS_SINK)
 
 
@@ -116,6 +122,30 @@ def paged_layout(rows: int, len_lo: int, len_hi: int, num_pages: int, page_size:
         cursor += int(need[r])
     positions = (lengths - 1).astype(np.int32)
     return lengths, positions, table
+
+
+def chunked_layout(rows: int, pre_lo: int, pre_hi: int, chunk: int, num_pages: int,
+                   page_size: int, gen: np.random.Generator, max_len: int):
+    """Chunked prefill over a paged prefix: row r holds a prefix of
+    U[pre_lo, pre_hi] tokens and receives `chunk` new tokens at positions
+    prefix_r .. prefix_r + chunk - 1; pages as in paged_layout for the total
+    length. Returns (prefixes, token_rows[n], token_positions[n], table),
+    tokens of one row contiguous."""
+    prefixes = gen.integers(pre_lo, pre_hi + 1, size=rows).astype(np.int64)
+    lengths = prefixes + chunk
+    pages = -(-max_len // page_size)
+    need = -(-lengths // page_size)
+    if int(need.sum()) > num_pages or int(lengths.max()) > max_len:
+        raise ValueError("page pool or table too small for the drawn lengths")
+    perm = gen.permutation(num_pages).astype(np.int32)
+    table = np.full((rows, pages), -1, dtype=np.int32)
+    cursor = 0
+    for r in range(rows):
+        table[r, :need[r]] = perm[cursor:cursor + need[r]]
+        cursor += int(need[r])
+    tok_rows = np.repeat(np.arange(rows, dtype=np.int32), chunk)
+    tok_pos = np.concatenate([np.arange(p, p + chunk) for p in prefixes]).astype(np.int32)
+    return prefixes, tok_rows, tok_pos, table
 
 
 def uniform_positions(n: int, lo: int, hi: int, gen: np.random.Generator) -> np.ndarray:
