@@ -255,6 +255,39 @@ def main():
                   "workload": f"{ec['rows']} rows, prefixes U[{ec['pre_lo']}, {ec['pre_hi']}] "
                               f"({int(c_pre.sum())} keys), chunk {ec['chunk']}, paged"}
 
+    # ---------------- next row: step_paged on the same pool ----------------
+    # The 16 chunks plus one decode token per row (at the chunk's last
+    # position, attending the whole row) in one call.
+    s_rows = ec["rows"]
+    s_pos = (c_pre + ec["chunk"] - 1).astype(np.int32)
+    s_q = W.device_normal((cn + s_rows, H, D), SEED_CHUNKED, "extra", bf16)
+    s_out = torch.empty((cn + s_rows, H, D), dtype=bf16, device=dev)
+    s_dpos = torch.from_numpy(s_pos).to(dev)
+    sws_n = gqa.gqa_step_paged_workspace(cn, s_rows, c_table.shape[1], H, KVH, D)
+    s_ws = torch.empty(max(sws_n, 256), dtype=torch.uint8, device=dev)
+
+    def stepped():
+        gqa.gqa_step_paged(cn, s_rows, c_table.shape[1], H, KVH, D, gqa.GQA_BF16, 0.0, 0, None, s_q,
+                           c_drows, c_dpos, c_pool_k, c_pool_v, ec["num_pages"], c_dtab, s_dpos,
+                           s_out, s_ws, sws_n)
+
+    for _ in range(args.warmup):
+        stepped()
+    s_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    for e0, e1 in s_ev:
+        e0.record(stream)
+        stepped()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    s_s = float(np.mean([e0.elapsed_time(e1) for e0, e1 in s_ev])) * 1e-3
+    s_flops = c_flops + 4 * D * H * int(np.sum(s_pos.astype(np.int64) + 1))
+    s_tflops = s_flops / s_s / 1e12
+    step_roof = {"bound": "mfma", "achieved": s_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": s_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                 "algorithmic_flops": s_flops, "avg_us": s_s * 1e6,
+                 "workload": f"step_paged: the {cn} chunk tokens above + {s_rows} decode tokens"}
+
     # ---------------- algorithmic work ----------------
     kv_bytes = int(np.sum(lengths)) * KVH * D * 2 * 2          # K + V of attended keys
     qo_bytes = 2 * rows * H * D * 2                              # q in, out
@@ -332,7 +365,7 @@ def main():
         "prefill_frac_of_mfma_peak": prefill_tflops / MFMA_BF16_PEAK_TFLOPS,
         "roofline": roof,
         "rooflines": {"decode_paged": dec_roof, "prefill_packed": pre_roof},
-        "next_rows": {"prefill_cached_paged": chunk_roof},
+        "next_rows": {"prefill_cached_paged": chunk_roof, "step_paged": step_roof},
         "per_op_us": {k: v * 1e3 for k, v in per_op_ms.items()},
         "wall_s_timed": wall,
         "cpu_baseline": cpu,

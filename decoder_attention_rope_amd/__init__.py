@@ -18,7 +18,8 @@ __all__ = [
     "GQA_BF16", "GQA_F32", "GQA_CACHE_NONE", "GQA_CACHE_CONTIGUOUS", "GQA_CACHE_PAGED_TABLE",
     "GQA_CACHE_PAGED_SLOTS", "GQA_PAGE_SIZE",
     "gqa_rope_table", "gqa_rope_write_kv", "gqa_prefill_packed", "gqa_prefill_packed_workspace",
-    "gqa_prefill_cached", "gqa_prefill_cached_workspace",
+    "gqa_prefill_cached", "gqa_prefill_cached_workspace", "gqa_step_packed",
+    "gqa_step_packed_workspace", "gqa_step_paged", "gqa_step_paged_workspace",
     "gqa_decode_rows", "gqa_decode_rows_workspace", "gqa_decode_paged",
     "gqa_decode_paged_workspace", "gqa_status_string", "gqa_set_dry_run", "gqa_abi_version",
     "dtype_code",
@@ -59,6 +60,14 @@ _prefill_cached = _sig("gqa_prefill_cached", ctypes.c_int,
                        [_i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
                         _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp])
 _prefill_cached_ws = _sig("gqa_prefill_cached_workspace", _sz, [_i32, _i32, _i32, _i32])
+_step_packed = _sig("gqa_step_packed", ctypes.c_int,
+                    [_i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                     _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp])
+_step_packed_ws = _sig("gqa_step_packed_workspace", _sz, [_i32, _i32, _i32, _i32, _i32, _i32])
+_step_paged = _sig("gqa_step_paged", ctypes.c_int,
+                   [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp,
+                    _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp])
+_step_paged_ws = _sig("gqa_step_paged_workspace", _sz, [_i32, _i32, _i32, _i32, _i32, _i32])
 _decode_rows = _sig("gqa_decode_rows", ctypes.c_int,
                     [_i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                      _vp, _sz, _vp])
@@ -165,6 +174,34 @@ def gqa_prefill_cached(n, heads, kv_heads, head_dim, dtype, scale, window, sinks
                            table_pages, _ptr(out), _ptr(workspace), workspace_bytes,
                            _stream(stream)),
            "gqa_prefill_cached")
+
+
+def gqa_step_packed_workspace(batch, p, heads, kv_heads, head_dim, max_seq):
+    return _step_packed_ws(batch, p, heads, kv_heads, head_dim, max_seq)
+
+
+def gqa_step_packed(batch, p, heads, kv_heads, head_dim, dtype, scale, window, sinks, q, k, v,
+                    positions, segments, cache_k, cache_v, max_seq, step_positions, out, workspace,
+                    workspace_bytes, stream=None):
+    _check(_step_packed(batch, p, heads, kv_heads, head_dim, dtype, scale, window, _ptr(sinks),
+                        _ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(segments), _ptr(cache_k),
+                        _ptr(cache_v), max_seq, _ptr(step_positions), _ptr(out), _ptr(workspace),
+                        workspace_bytes, _stream(stream)),
+           "gqa_step_packed")
+
+
+def gqa_step_paged_workspace(p, rows, pages, heads, kv_heads, head_dim):
+    return _step_paged_ws(p, rows, pages, heads, kv_heads, head_dim)
+
+
+def gqa_step_paged(p, rows, pages, heads, kv_heads, head_dim, dtype, scale, window, sinks, q,
+                   token_rows, positions, pool_k, pool_v, num_pages, table, step_positions, out,
+                   workspace, workspace_bytes, stream=None):
+    _check(_step_paged(p, rows, pages, heads, kv_heads, head_dim, dtype, scale, window,
+                       _ptr(sinks), _ptr(q), _ptr(token_rows), _ptr(positions), _ptr(pool_k),
+                       _ptr(pool_v), num_pages, _ptr(table), _ptr(step_positions), _ptr(out),
+                       _ptr(workspace), workspace_bytes, _stream(stream)),
+           "gqa_step_paged")
 
 
 def gqa_decode_rows_workspace(batch, heads, kv_heads, head_dim, max_seq):

@@ -134,11 +134,11 @@ size_t gqa_prefill_packed_workspace(int32_t p, int32_t heads, int32_t kv_heads,
   return gqa::prefill_workspace_bytes(p, heads, kv_heads, head_dim);
 }
 
-int gqa_prefill_packed(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
-                       int32_t dtype, float scale, int32_t window, const void* sinks,
-                       const void* q, const void* k, const void* v,
-                       const int32_t* positions, const int32_t* segments, void* out,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+static int prefill_packed_impl(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                               int32_t dtype, float scale, int32_t window, const void* sinks,
+                               const void* q, const void* k, const void* v,
+                               const int32_t* positions, const int32_t* segments, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream, bool launch) {
   if (p < 0 || window < 0) return GQA_ERR_INVALID_ARG;
   int st = check_heads(heads, kv_heads, head_dim, dtype);
   if (st != GQA_OK) return st;
@@ -151,7 +151,7 @@ int gqa_prefill_packed(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_
   const size_t need = gqa::prefill_workspace_bytes(p, heads, kv_heads, head_dim);
   if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GQA_ERR_WORKSPACE;
-  if (g_dry_run.load()) return GQA_OK;
+  if (!launch) return GQA_OK;
   gqa::PrefillArgs a{};
   a.p = p;
   a.heads = heads;
@@ -173,19 +173,30 @@ int gqa_prefill_packed(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_
   return hip_status(gqa::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
+int gqa_prefill_packed(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                       int32_t dtype, float scale, int32_t window, const void* sinks,
+                       const void* q, const void* k, const void* v,
+                       const int32_t* positions, const int32_t* segments, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_packed_impl(p, heads, kv_heads, head_dim, dtype, scale, window, sinks, q, k, v,
+                             positions, segments, out, workspace, workspace_bytes, stream,
+                             !g_dry_run.load());
+}
+
 size_t gqa_prefill_cached_workspace(int32_t n, int32_t heads, int32_t kv_heads,
                                     int32_t head_dim) {
   if (n <= 0) return 0;
   return gqa::prefill_workspace_bytes(n, heads, kv_heads, head_dim);
 }
 
-int gqa_prefill_cached(int32_t n, int32_t heads, int32_t kv_heads, int32_t head_dim,
-                       int32_t dtype, float scale, int32_t window, const void* sinks,
-                       const void* q, const int32_t* rows, const int32_t* positions,
-                       int32_t cache_kind, const void* cache_k, const void* cache_v,
-                       int32_t cache_dim0, int32_t cache_seq, const int32_t* table,
-                       int32_t table_rows, int32_t table_pages, void* out, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+static int prefill_cached_impl(int32_t n, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                               int32_t dtype, float scale, int32_t window, const void* sinks,
+                               const void* q, const int32_t* rows, const int32_t* positions,
+                               int32_t cache_kind, const void* cache_k, const void* cache_v,
+                               int32_t cache_dim0, int32_t cache_seq, const int32_t* table,
+                               int32_t table_rows, int32_t table_pages, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               bool launch) {
   if (n < 0 || window < 0) return GQA_ERR_INVALID_ARG;
   int st = check_heads(heads, kv_heads, head_dim, dtype);
   if (st != GQA_OK) return st;
@@ -207,7 +218,7 @@ int gqa_prefill_cached(int32_t n, int32_t heads, int32_t kv_heads, int32_t head_
   const size_t need = gqa::prefill_workspace_bytes(n, heads, kv_heads, head_dim);
   if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GQA_ERR_WORKSPACE;
-  if (g_dry_run.load()) return GQA_OK;
+  if (!launch) return GQA_OK;
   gqa::PrefillArgs a{};
   a.p = n;
   a.heads = heads;
@@ -240,6 +251,19 @@ int gqa_prefill_cached(int32_t n, int32_t heads, int32_t kv_heads, int32_t head_
   return hip_status(gqa::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
+int gqa_prefill_cached(int32_t n, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                       int32_t dtype, float scale, int32_t window, const void* sinks,
+                       const void* q, const int32_t* rows, const int32_t* positions,
+                       int32_t cache_kind, const void* cache_k, const void* cache_v,
+                       int32_t cache_dim0, int32_t cache_seq, const int32_t* table,
+                       int32_t table_rows, int32_t table_pages, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return prefill_cached_impl(n, heads, kv_heads, head_dim, dtype, scale, window, sinks, q, rows,
+                             positions, cache_kind, cache_k, cache_v, cache_dim0, cache_seq, table,
+                             table_rows, table_pages, out, workspace, workspace_bytes, stream,
+                             !g_dry_run.load());
+}
+
 static size_t decode_ws(int rows, int heads, int kv_heads, int head_dim, int dtype, int paged,
                         int cap) {
   size_t ws = 0;
@@ -264,21 +288,21 @@ size_t gqa_decode_paged_workspace(int32_t rows, int32_t pages, int32_t heads, in
 }
 
 static int decode_common(gqa::DecodeArgs& a, size_t workspace_bytes, void* workspace,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool launch) {
   const size_t need =
       decode_ws(a.rows, a.heads, a.kv_heads, a.head_dim, a.dtype, a.paged, a.cap);
   if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GQA_ERR_WORKSPACE;
-  if (g_dry_run.load()) return GQA_OK;
+  if (!launch) return GQA_OK;
   a.ws = static_cast<float*>(workspace);
   return hip_status(gqa::launch_decode(a, stream));
 }
 
-int gqa_decode_rows(int32_t batch, int32_t heads, int32_t kv_heads, int32_t head_dim,
+static int decode_rows_impl(int32_t batch, int32_t heads, int32_t kv_heads, int32_t head_dim,
                     int32_t dtype, float scale, int32_t window, const void* sinks,
                     const void* q, const void* cache_k, const void* cache_v, int32_t max_seq,
                     const int32_t* positions, void* out, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    size_t workspace_bytes, void* stream, bool launch) {
   if (batch < 0 || window < 0 || max_seq <= 0) return GQA_ERR_INVALID_ARG;
   int st = check_heads(heads, kv_heads, head_dim, dtype);
   if (st != GQA_OK) return st;
@@ -306,14 +330,24 @@ int gqa_decode_rows(int32_t batch, int32_t heads, int32_t kv_heads, int32_t head
   a.pages = 0;
   a.num_pages = 0;
   a.out = out;
-  return decode_common(a, workspace_bytes, workspace, static_cast<hipStream_t>(stream));
+  return decode_common(a, workspace_bytes, workspace, static_cast<hipStream_t>(stream), launch);
 }
 
-int gqa_decode_paged(int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
+int gqa_decode_rows(int32_t batch, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                    int32_t dtype, float scale, int32_t window, const void* sinks,
+                    const void* q, const void* cache_k, const void* cache_v, int32_t max_seq,
+                    const int32_t* positions, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return decode_rows_impl(batch, heads, kv_heads, head_dim, dtype, scale, window, sinks, q, cache_k,
+                          cache_v, max_seq, positions, out, workspace, workspace_bytes, stream,
+                          !g_dry_run.load());
+}
+
+static int decode_paged_impl(int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
                      int32_t head_dim, int32_t dtype, float scale, int32_t window,
                      const void* sinks, const void* q, const void* pool_k, const void* pool_v,
                      int32_t num_pages, const int32_t* positions, const int32_t* table,
-                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                     void* out, void* workspace, size_t workspace_bytes, void* stream, bool launch) {
   if (rows < 0 || pages <= 0 || num_pages <= 0 || window < 0) return GQA_ERR_INVALID_ARG;
   if ((long long)pages * GQA_PAGE_SIZE > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
   int st = check_heads(heads, kv_heads, head_dim, dtype);
@@ -342,7 +376,135 @@ int gqa_decode_paged(int32_t rows, int32_t pages, int32_t heads, int32_t kv_head
   a.pages = pages;
   a.num_pages = num_pages;
   a.out = out;
-  return decode_common(a, workspace_bytes, workspace, static_cast<hipStream_t>(stream));
+  return decode_common(a, workspace_bytes, workspace, static_cast<hipStream_t>(stream), launch);
 }
 
+int gqa_decode_paged(int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
+                     int32_t head_dim, int32_t dtype, float scale, int32_t window,
+                     const void* sinks, const void* q, const void* pool_k, const void* pool_v,
+                     int32_t num_pages, const int32_t* positions, const int32_t* table,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_paged_impl(rows, pages, heads, kv_heads, head_dim, dtype, scale, window, sinks, q,
+                           pool_k, pool_v, num_pages, positions, table, out, workspace,
+                           workspace_bytes, stream, !g_dry_run.load());
+}
+
+
+// ---------------------------------------------------------------------------
+// step_packed / step_paged (llama-3.1-8b-instruct and gpt-oss-20b cards,
+// serving signatures): one call over prefill tokens and one decode token per
+// row, in the token order of the pages' types. Both parts write their k/v
+// first (gqa_rope_write_kv); here each part runs its attention kernels on the
+// same stream, out of one caller workspace (the prefill part's bytes, then the
+// decode part's, each 256-byte aligned).
+// ---------------------------------------------------------------------------
+static size_t align_up_256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t gqa_step_packed_workspace(int32_t batch, int32_t p, int32_t heads, int32_t kv_heads,
+                                 int32_t head_dim, int32_t max_seq) {
+  if (batch < 0 || p < 0) return 0;
+  const size_t a = p > 0 ? align_up_256(gqa_prefill_packed_workspace(p, heads, kv_heads, head_dim)) : 0;
+  const size_t b = batch > 0 ? gqa_decode_rows_workspace(batch, heads, kv_heads, head_dim, max_seq) : 0;
+  return a + b;
+}
+
+int gqa_step_packed(int32_t batch, int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                    int32_t dtype, float scale, int32_t window, const void* sinks, const void* q,
+                    const void* k, const void* v, const int32_t* positions,
+                    const int32_t* segments, const void* cache_k, const void* cache_v,
+                    int32_t max_seq, const int32_t* step_positions, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (batch < 0 || p < 0) return GQA_ERR_INVALID_ARG;
+  int st = check_heads(heads, kv_heads, head_dim, dtype);
+  if (st != GQA_OK) return st;
+  if (q == nullptr || out == nullptr) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  const size_t need = gqa_step_packed_workspace(batch, p, heads, kv_heads, head_dim, max_seq);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GQA_ERR_WORKSPACE;
+  const size_t row = (size_t)heads * head_dim * 2;  // bytes of one token's q / out (bf16)
+  const size_t pre_ws = p > 0 ? align_up_256(gqa_prefill_packed_workspace(p, heads, kv_heads, head_dim)) : 0;
+  char* ws = static_cast<char*>(workspace);
+  // Validate both parts before enqueuing either (dry-run validation first).
+  const bool launch = !g_dry_run.load();
+  int s1 = p > 0 ? prefill_packed_impl(p, heads, kv_heads, head_dim, dtype, scale, window, sinks,
+                                      static_cast<const char*>(q) + batch * row, k, v, positions,
+                                      segments, static_cast<char*>(out) + batch * row, ws,
+                                      pre_ws, stream, false)
+                 : GQA_OK;
+  int s2 = batch > 0 ? decode_rows_impl(batch, heads, kv_heads, head_dim, dtype, scale, window,
+                                        sinks, q, cache_k, cache_v, max_seq, step_positions, out,
+                                        ws == nullptr ? nullptr : ws + pre_ws,
+                                        workspace_bytes - pre_ws, stream, false)
+                     : GQA_OK;
+  if (s1 != GQA_OK) return s1;
+  if (s2 != GQA_OK) return s2;
+  if (!launch) return GQA_OK;
+  if (batch > 0) {
+    s2 = decode_rows_impl(batch, heads, kv_heads, head_dim, dtype, scale, window, sinks, q, cache_k,
+                          cache_v, max_seq, step_positions, out, ws + pre_ws,
+                          workspace_bytes - pre_ws, stream, true);
+    if (s2 != GQA_OK) return s2;
+  }
+  if (p > 0)
+    return prefill_packed_impl(p, heads, kv_heads, head_dim, dtype, scale, window, sinks,
+                               static_cast<const char*>(q) + batch * row, k, v, positions, segments,
+                               static_cast<char*>(out) + batch * row, ws, pre_ws, stream, true);
+  return GQA_OK;
+}
+
+size_t gqa_step_paged_workspace(int32_t p, int32_t rows, int32_t pages, int32_t heads,
+                                int32_t kv_heads, int32_t head_dim) {
+  if (p < 0 || rows < 0) return 0;
+  const size_t a = p > 0 ? align_up_256(gqa_prefill_cached_workspace(p, heads, kv_heads, head_dim)) : 0;
+  const size_t b = rows > 0 ? gqa_decode_paged_workspace(rows, pages, heads, kv_heads, head_dim) : 0;
+  return a + b;
+}
+
+int gqa_step_paged(int32_t p, int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
+                   int32_t head_dim, int32_t dtype, float scale, int32_t window, const void* sinks,
+                   const void* q, const int32_t* token_rows, const int32_t* positions,
+                   const void* pool_k, const void* pool_v, int32_t num_pages,
+                   const int32_t* table, const int32_t* step_positions, void* out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (p < 0 || rows < 0) return GQA_ERR_INVALID_ARG;
+  int st = check_heads(heads, kv_heads, head_dim, dtype);
+  if (st != GQA_OK) return st;
+  if (q == nullptr || out == nullptr) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  if (rows <= 0 && p > 0) return GQA_ERR_INVALID_ARG;  // the table has `rows` rows
+  const size_t need = gqa_step_paged_workspace(p, rows, pages, heads, kv_heads, head_dim);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GQA_ERR_WORKSPACE;
+  const size_t row = (size_t)heads * head_dim * 2;
+  const size_t pre_ws = p > 0 ? align_up_256(gqa_prefill_cached_workspace(p, heads, kv_heads, head_dim)) : 0;
+  char* ws = static_cast<char*>(workspace);
+  const bool launch = !g_dry_run.load();
+  int s1 = p > 0 ? prefill_cached_impl(p, heads, kv_heads, head_dim, dtype, scale, window, sinks, q,
+                                       token_rows, positions, GQA_CACHE_PAGED_TABLE, pool_k, pool_v,
+                                       num_pages, GQA_PAGE_SIZE, table, rows, pages, out, ws,
+                                       pre_ws, stream, false)
+                 : GQA_OK;
+  int s2 = rows > 0 ? decode_paged_impl(rows, pages, heads, kv_heads, head_dim, dtype, scale, window,
+                                        sinks, static_cast<const char*>(q) + p * row, pool_k,
+                                        pool_v, num_pages, step_positions, table,
+                                        static_cast<char*>(out) + p * row,
+                                        ws == nullptr ? nullptr : ws + pre_ws,
+                                        workspace_bytes - pre_ws, stream, false)
+                    : GQA_OK;
+  if (s1 != GQA_OK) return s1;
+  if (s2 != GQA_OK) return s2;
+  if (!launch) return GQA_OK;
+  if (rows > 0) {
+    s2 = decode_paged_impl(rows, pages, heads, kv_heads, head_dim, dtype, scale, window, sinks,
+                           static_cast<const char*>(q) + p * row, pool_k, pool_v, num_pages,
+                           step_positions, table, static_cast<char*>(out) + p * row, ws + pre_ws,
+                           workspace_bytes - pre_ws, stream, true);
+    if (s2 != GQA_OK) return s2;
+  }
+  if (p > 0)
+    return prefill_cached_impl(p, heads, kv_heads, head_dim, dtype, scale, window, sinks, q,
+                               token_rows, positions, GQA_CACHE_PAGED_TABLE, pool_k, pool_v,
+                               num_pages, GQA_PAGE_SIZE, table, rows, pages, out, ws, pre_ws,
+                               stream, true);
+  return GQA_OK;
+}
 }  // extern "C"

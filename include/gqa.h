@@ -222,6 +222,57 @@ int gqa_decode_paged(int32_t rows, int32_t pages, int32_t heads, int32_t kv_head
 size_t gqa_decode_paged_workspace(int32_t rows, int32_t pages, int32_t heads,
                                   int32_t kv_heads, int32_t head_dim);
 
+/*
+ * gqa_step_packed -- `step_packed<P>` of GroupedQueryAttention (llama-
+ * 3.1-8b-instruct card) and SinkAttention (gpt-oss-20b card, with the
+ * window): one call over `batch` decode tokens and `p` packed prefill
+ * tokens, in the order of the pages' x: [1, Batch + P, H] -- the decode
+ * tokens first. Signature only on the pages; the reading taken: decode token
+ * b attends slots <= step_positions[b] of contiguous cache row b (as
+ * gqa_decode_rows), the packed tokens attend each other under `own` (as
+ * gqa_prefill_packed). Every token's k/v are written first by
+ * gqa_rope_write_kv.
+ *   q, out [batch + p, heads, D] of T; k, v [p, kv_heads, D] (the packed
+ *   tokens, rotated); positions, segments [p]; cache_k, cache_v [batch,
+ *   kv_heads, max_seq, D]; step_positions [batch]. bf16 only.
+ *   workspace: gqa_step_packed_workspace(...) bytes, 256-byte aligned.
+ * Both parts are validated before either is enqueued; statuses as the two
+ * entries above.
+ */
+int gqa_step_packed(int32_t batch, int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                    int32_t dtype, float scale, int32_t window, const void* sinks, const void* q,
+                    const void* k, const void* v, const int32_t* positions,
+                    const int32_t* segments, const void* cache_k, const void* cache_v,
+                    int32_t max_seq, const int32_t* step_positions, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+size_t gqa_step_packed_workspace(int32_t batch, int32_t p, int32_t heads, int32_t kv_heads,
+                                 int32_t head_dim, int32_t max_seq);
+
+/*
+ * gqa_step_paged -- `step_paged<P, Rows, Pages>` (llama-3.1-8b-instruct
+ * card): `p` chunk tokens then one decode token for each of `rows` table
+ * rows, in the order of the pages' x: [1, P + Rows, H]. Signature only; the
+ * reading taken: chunk token i attends the paged row token_rows[i] at slots
+ * <= positions[i], prefix included (as gqa_prefill_cached, PAGED_TABLE);
+ * decode token r attends table row r at slots <= step_positions[r] (as
+ * gqa_decode_paged). Every token's k/v are written first (gqa_rope_write_kv
+ * with PAGED_SLOTS or PAGED_TABLE).
+ *   q, out [p + rows, heads, D] of T; token_rows, positions [p]; pools
+ *   [num_pages, kv_heads, 64, D]; table [rows, pages]; step_positions
+ *   [rows]. bf16 only. workspace: gqa_step_paged_workspace(...) bytes,
+ *   256-byte aligned.
+ */
+int gqa_step_paged(int32_t p, int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
+                   int32_t head_dim, int32_t dtype, float scale, int32_t window, const void* sinks,
+                   const void* q, const int32_t* token_rows, const int32_t* positions,
+                   const void* pool_k, const void* pool_v, int32_t num_pages,
+                   const int32_t* table, const int32_t* step_positions, void* out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+size_t gqa_step_paged_workspace(int32_t p, int32_t rows, int32_t pages, int32_t heads,
+                                int32_t kv_heads, int32_t head_dim);
+
 /* Human-readable name of a status code (static storage). */
 const char* gqa_status_string(int32_t status);
 

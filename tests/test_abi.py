@@ -194,6 +194,34 @@ def test_prefill_cached_argument_checks(g):
     call(ws_err, ws=257)
 
 
+def test_step_entries_argument_checks(g):
+    bad_arg, unsup, ws_err = _codes(g)
+    nb = g.gqa_step_packed_workspace(4, 100, 8, 8, 64, 512)
+    assert nb >= g.gqa_prefill_packed_workspace(100, 8, 8, 64) + \
+        g.gqa_decode_rows_workspace(4, 8, 8, 64, 512)
+    sp = lambda st, batch=4, p=100, dtype=0, q=8, seg=8, cache=8, wsb=nb: _expect(  # noqa: E731
+        g, st, g.gqa_step_packed, batch, p, 8, 8, 64, dtype, 0.0, 0, None, q, 8, 8, 8, seg, cache,
+        cache, 512, 8, 8, 256, wsb)
+    sp(g.GQA_OK)
+    sp(g.GQA_OK, batch=0)
+    sp(g.GQA_OK, p=0)
+    sp(bad_arg, q=None)
+    sp(bad_arg, seg=None)          # the packed part needs segments
+    sp(bad_arg, cache=None)        # the decode part needs the cache
+    sp(unsup, dtype=1)
+    sp(ws_err, wsb=nb - 1)
+    nbp = g.gqa_step_paged_workspace(300, 16, 128, 32, 8, 128)
+    assert nbp >= g.gqa_prefill_cached_workspace(300, 32, 8, 128)
+    spg = lambda st, p=300, rows=16, pages=128, table=8, wsb=nbp: _expect(  # noqa: E731
+        g, st, g.gqa_step_paged, p, rows, pages, 32, 8, 128, 0, 0.0, 0, None, 8, 8, 8, 8, 8, 2000,
+        table, 8, 8, 256, wsb)
+    spg(g.GQA_OK)
+    spg(g.GQA_OK, p=0)
+    spg(bad_arg, table=None)
+    spg(bad_arg, pages=0)
+    spg(ws_err, wsb=16)
+
+
 def test_workspace_sizes(g):
     assert g.gqa_decode_rows_workspace(0, 8, 8, 64, 10) == 0
     a = g.gqa_decode_paged_workspace(64, 128, 32, 8, 128)
