@@ -64,6 +64,7 @@ def load(path=None):
                                        c_dbl, c_int, _D, _D]
     lib.orc_prefill_paged.argtypes = [c_int, c_int, c_int, c_int, _D, _I, _I, _D, _D, c_int, c_int,
                                       _I, c_int, c_int, c_dbl, c_int, _D, _D]
+    lib.orc_linear.argtypes = [c_int, c_int, c_int, _D, _D, _D, c_int, _D]
     lib.orc_num_threads.restype = c_int
     lib.orc_mutation.restype = c_int
     _LIBS[path] = lib
@@ -245,6 +246,15 @@ class Oracle:
                                    _pd(pk), _pd(pv), num_pages, page_size, _pi(tb), tb.shape[0],
                                    tb.shape[1], scale, int(window), _pd(_f64(sinks)), _pd(out))
         return out
+
+    def linear(self, x, weight, bias=None, dtype="bf16"):
+        """Linear forward: x [n, in], weight [out, in], bias [out] -> [n, out] of T."""
+        x, w = _f64(x), _f64(weight)
+        n, fin = x.shape
+        fout = w.shape[0]
+        y = np.zeros((n, fout), dtype=np.float64)
+        self.lib.orc_linear(n, fin, fout, _pd(x), _pd(w), _pd(_f64(bias)), _dt(dtype), _pd(y))
+        return y
 
 
 _DEFAULT = None

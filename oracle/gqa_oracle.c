@@ -564,6 +564,33 @@ void orc_prefill_paged(int n, int heads, int kv_heads, int D, const double* q,
   }
 }
 
+/* ------------------------------------------------------------------------ */
+/* std.nn.linear::Linear<In, Out, T> `forward` [L, N1]: param weight         */
+/* [Out, In], optional param bias [Out]; y[t, o] = sum_i x[t, i] * w[o, i]  */
+/* (+ b[o]) for every leading index t, a Tensor of T. Reading: the sum is   */
+/* exact (fp64 here), the bias added, and the result rounded once to T.     */
+/* q_proj / k_proj / v_proj of GroupedQueryAttention are three such          */
+/* modules applied to the same x. x [n, in]; w [out, in]; b [out] or NULL.  */
+/* ------------------------------------------------------------------------ */
+void orc_linear(int n, int in, int out_f, const double* x, const double* w, const double* b,
+                int dtype, double* y) {
+#pragma omp parallel for schedule(static)
+  for (long idx = 0; idx < (long)n * out_f; ++idx) {
+    const long t = idx / out_f;
+    const int o = (int)(idx % out_f);
+    double acc = 0.0;
+    for (int i = 0; i < in; ++i) {
+#if ORC_MUTATE == 13
+      acc += x[t * in + i] * w[(size_t)i * out_f + o % in];
+#else
+      acc += x[t * in + i] * w[(size_t)o * in + i];
+#endif
+    }
+    if (b) acc += b[o];
+    y[idx] = dtype == ORC_DT_NONE ? acc : orc_round(acc, dtype);
+  }
+}
+
 /* Threads OpenMP will use for the calls above. */
 int orc_num_threads(void) {
 #ifdef _OPENMP

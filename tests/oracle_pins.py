@@ -28,6 +28,8 @@ instruct and gpt-oss-20b, blocks GroupedQueryAttention and SinkAttention):
                 with invalid ids excluded (checked with an explicit mask)
   writes        write-then-attend equals forward; out-of-range targets leave
                 the cache unchanged
+  linear        torch float64 F.linear rounded once to bf16; identity and
+                one-hot weights select the inputs
   chunk         chunked prefill over a cached prefix: q = 0 gives the mean of
                 exactly the attended slots of the right row; torch softmax
                 over an explicit mask (sink as an extra logit); a chunk into
@@ -570,6 +572,32 @@ def pin_chunk_paged(o):
             _close(out0[i, hh], ref, 1e-13, "paged chunk, invalid pages excluded")
 
 
+# ---------------------------------------------------------------------------
+# Linear (the q / k / v projections)
+# ---------------------------------------------------------------------------
+def pin_linear(o):
+    rng = _rng(16)
+    n, fin, fout = 7, 24, 10
+    x = _bf16_vals(rng.standard_normal((n, fin)))
+    w = _bf16_vals(rng.standard_normal((fout, fin)))
+    b = _bf16_vals(rng.standard_normal(fout))
+    # against torch's float64 F.linear, then one rounding to bf16 (torch's)
+    for bias in (None, b):
+        ref = F.linear(torch.from_numpy(x), torch.from_numpy(w),
+                       None if bias is None else torch.from_numpy(bias))
+        ref_t = ref.to(torch.bfloat16).to(torch.float64).numpy()
+        got = o.linear(x, w, bias, "bf16")
+        assert np.array_equal(got, ref_t), "linear differs from F.linear rounded to bf16"
+        raw = o.linear(x, w, bias, "none")
+        _close(raw, ref.numpy(), 1e-12, "linear before rounding")
+    # identity weights return x; a one-hot row selects one input feature
+    eye = np.eye(fin)
+    assert np.array_equal(o.linear(x, eye, None, "bf16"), x)
+    sel = np.zeros((3, fin))
+    sel[0, 5] = sel[1, 0] = sel[2, fin - 1] = 1.0
+    assert np.array_equal(o.linear(x, sel, None, "bf16"), x[:, [5, 0, fin - 1]])
+
+
 ALL_PINS = {
     "rounding": pin_rounding,
     "inv_freq": pin_inv_freq,
@@ -588,6 +616,7 @@ ALL_PINS = {
     "writes": pin_writes,
     "chunk_cached": pin_chunk_cached,
     "chunk_paged": pin_chunk_paged,
+    "linear": pin_linear,
 }
 
 

@@ -4,7 +4,7 @@ Each ORC_MUTATE value in oracle/gqa_oracle.c plants one plausible mistake
 (a wrong KV-head index, a dropped scale, a flipped RoPE sign, a strict `own`
 comparison, an off-by-one window, a scaled sink, a strict `seen`, a swapped
 page index, a wrong inv_freq denominator, truncating rounding, an ignored
-cache row, reversed in-page offsets). The oracle is
+cache row, reversed in-page offsets, a transposed Linear weight). The oracle is
 rebuilt with each one into a temporary directory; the pins must reject it.
 """
 import os
@@ -28,6 +28,7 @@ MUTATIONS = {
     10: "rounding truncates",
     11: "chunked prefill ignores the token's cache row",
     12: "paged chunk reverses offsets inside a page",
+    13: "linear reads the weight transposed",
 }
 
 
