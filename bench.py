@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "paged GQA decode KV GB/s + packed prefill TFLOP/s (% of MI355X peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
-SEED_DECODE, SEED_PREFILL, SEED_CHUNKED = 3, 4, 6
+SEED_DECODE, SEED_PREFILL, SEED_CHUNKED, SEED_QKV = 3, 4, 6, 7
 
 
 def parse_args():
@@ -288,6 +288,48 @@ def main():
                  "algorithmic_flops": s_flops, "avg_us": s_s * 1e6,
                  "workload": f"step_paged: the {cn} chunk tokens above + {s_rows} decode tokens"}
 
+    # ---------------- next row: fused q / k / v projections + rope + KV write ----------------
+    # Llama-3.1-8B projections of the 16,384 prefill tokens (hidden 4096 ->
+    # 32 + 8 + 8 heads of 128), rotated and written into the contiguous cache,
+    # timed beside the step; a plain bf16 GEMM of the same shape through
+    # torch.matmul (hipBLASLt) is timed as a yardstick.
+    hid = 4096
+    gx = W.device_normal((P, hid), SEED_QKV, "q", bf16)
+    gwq = W.device_normal((H * D, hid), SEED_QKV, "k", bf16) * (hid ** -0.5)
+    gwk = W.device_normal((KVH * D, hid), SEED_QKV, "v", bf16) * (hid ** -0.5)
+    gwv = W.device_normal((KVH * D, hid), SEED_QKV, "extra", bf16) * (hid ** -0.5)
+    g_q = torch.empty((P, H, D), dtype=bf16, device=dev)
+
+    def fused_qkv():
+        gqa.gqa_qkv_rope_write(P, hid, H, KVH, D, gqa.GQA_BF16, gx, gwq, gwk, gwv, None, None, None,
+                               p_pos, rope_tab, max_pos, g_q, None, None,
+                               gqa.GQA_CACHE_CONTIGUOUS, p_cache_k, p_cache_v, nseg, cache_len,
+                               p_seg, None, None, 0, 0)
+
+    gwcat = torch.cat([gwq, gwk, gwv], 0).contiguous()
+
+    def timed(fn):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        for e0, e1 in pairs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in pairs])) * 1e-3
+
+    q_s = timed(fused_qkv)
+    mm_s = timed(lambda: gx @ gwcat.t())
+    q_flops = 2 * P * hid * (H + 2 * KVH) * D
+    qkv_roof = {"bound": "mfma", "achieved": q_flops / q_s / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": q_flops / q_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                "traffic": None, "algorithmic_flops": q_flops, "avg_us": q_s * 1e6,
+                "hipblaslt_gemm_only_us": mm_s * 1e6,
+                "workload": f"{P} tokens x hidden {hid} -> (32 + 8 + 8) x 128, rope, contiguous cache"}
+    del gx, gwq, gwk, gwv, gwcat, g_q
+
     # ---------------- algorithmic work ----------------
     kv_bytes = int(np.sum(lengths)) * KVH * D * 2 * 2          # K + V of attended keys
     qo_bytes = 2 * rows * H * D * 2                              # q in, out
@@ -365,7 +407,8 @@ def main():
         "prefill_frac_of_mfma_peak": prefill_tflops / MFMA_BF16_PEAK_TFLOPS,
         "roofline": roof,
         "rooflines": {"decode_paged": dec_roof, "prefill_packed": pre_roof},
-        "next_rows": {"prefill_cached_paged": chunk_roof, "step_paged": step_roof},
+        "next_rows": {"prefill_cached_paged": chunk_roof, "step_paged": step_roof,
+                      "qkv_rope_write": qkv_roof},
         "per_op_us": {k: v * 1e3 for k, v in per_op_ms.items()},
         "wall_s_timed": wall,
         "cpu_baseline": cpu,

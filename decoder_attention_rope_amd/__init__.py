@@ -20,6 +20,7 @@ __all__ = [
     "gqa_rope_table", "gqa_rope_write_kv", "gqa_prefill_packed", "gqa_prefill_packed_workspace",
     "gqa_prefill_cached", "gqa_prefill_cached_workspace", "gqa_step_packed",
     "gqa_step_packed_workspace", "gqa_step_paged", "gqa_step_paged_workspace",
+    "gqa_qkv_rope_write",
     "gqa_decode_rows", "gqa_decode_rows_workspace", "gqa_decode_paged",
     "gqa_decode_paged_workspace", "gqa_status_string", "gqa_set_dry_run", "gqa_abi_version",
     "dtype_code",
@@ -68,6 +69,9 @@ _step_paged = _sig("gqa_step_paged", ctypes.c_int,
                    [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp,
                     _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp])
 _step_paged_ws = _sig("gqa_step_paged_workspace", _sz, [_i32, _i32, _i32, _i32, _i32, _i32])
+_qkv = _sig("gqa_qkv_rope_write", ctypes.c_int,
+            [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+             _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _vp])
 _decode_rows = _sig("gqa_decode_rows", ctypes.c_int,
                     [_i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                      _vp, _sz, _vp])
@@ -202,6 +206,18 @@ def gqa_step_paged(p, rows, pages, heads, kv_heads, head_dim, dtype, scale, wind
                        _ptr(pool_v), num_pages, _ptr(table), _ptr(step_positions), _ptr(out),
                        _ptr(workspace), workspace_bytes, _stream(stream)),
            "gqa_step_paged")
+
+
+def gqa_qkv_rope_write(n, hidden, heads, kv_heads, head_dim, dtype, x, w_q, w_k, w_v, b_q, b_k,
+                       b_v, positions, rope_table, rope_max_pos, q_out, k_out, v_out, cache_kind,
+                       cache_k, cache_v, cache_dim0, cache_seq, rows, slots, table, table_rows,
+                       table_pages, stream=None):
+    _check(_qkv(n, hidden, heads, kv_heads, head_dim, dtype, _ptr(x), _ptr(w_q), _ptr(w_k),
+                _ptr(w_v), _ptr(b_q), _ptr(b_k), _ptr(b_v), _ptr(positions), _ptr(rope_table),
+                rope_max_pos, _ptr(q_out), _ptr(k_out), _ptr(v_out), cache_kind, _ptr(cache_k),
+                _ptr(cache_v), cache_dim0, cache_seq, _ptr(rows), _ptr(slots), _ptr(table),
+                table_rows, table_pages, _stream(stream)),
+           "gqa_qkv_rope_write")
 
 
 def gqa_decode_rows_workspace(batch, heads, kv_heads, head_dim, max_seq):

@@ -507,4 +507,73 @@ int gqa_step_paged(int32_t p, int32_t rows, int32_t pages, int32_t heads, int32_
                                stream, true);
   return GQA_OK;
 }
+
+int gqa_qkv_rope_write(int32_t n, int32_t hidden, int32_t heads, int32_t kv_heads,
+                       int32_t head_dim, int32_t dtype, const void* x, const void* w_q,
+                       const void* w_k, const void* w_v, const void* b_q, const void* b_k,
+                       const void* b_v, const int32_t* positions, const void* rope_table,
+                       int32_t rope_max_pos, void* q_out, void* k_out, void* v_out,
+                       int32_t cache_kind, void* cache_k, void* cache_v, int32_t cache_dim0,
+                       int32_t cache_seq, const int32_t* rows, const int32_t* slots,
+                       const int32_t* table, int32_t table_rows, int32_t table_pages,
+                       void* stream) {
+  if (n < 0 || hidden <= 0) return GQA_ERR_INVALID_ARG;
+  int st = check_heads(heads, kv_heads, head_dim, dtype);
+  if (st != GQA_OK) return st;
+  if (x == nullptr || w_q == nullptr || w_k == nullptr || w_v == nullptr || q_out == nullptr)
+    return GQA_ERR_INVALID_ARG;
+  if (cache_kind < GQA_CACHE_NONE || cache_kind > GQA_CACHE_PAGED_SLOTS) return GQA_ERR_INVALID_ARG;
+  if (rope_table != nullptr && (rope_max_pos <= 0 || positions == nullptr)) return GQA_ERR_INVALID_ARG;
+  if (cache_kind != GQA_CACHE_NONE) {
+    if (cache_k == nullptr || cache_dim0 <= 0) return GQA_ERR_INVALID_ARG;
+    if (cache_kind == GQA_CACHE_CONTIGUOUS && (cache_seq <= 0 || positions == nullptr))
+      return GQA_ERR_INVALID_ARG;
+    if (cache_kind != GQA_CACHE_CONTIGUOUS && cache_seq != GQA_PAGE_SIZE) return GQA_ERR_INVALID_ARG;
+    if (cache_kind == GQA_CACHE_PAGED_TABLE &&
+        (table == nullptr || table_rows <= 0 || table_pages <= 0 || positions == nullptr))
+      return GQA_ERR_INVALID_ARG;
+    if (cache_kind == GQA_CACHE_PAGED_SLOTS && slots == nullptr) return GQA_ERR_INVALID_ARG;
+  }
+  if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  // Tiles: K slabs of 64 hidden features, 128 output features per tile.
+  if (hidden % 64 != 0 || ((long long)(heads + 2 * kv_heads) * head_dim) % 128 != 0)
+    return GQA_ERR_UNSUPPORTED;
+  if (((long long)n + 128) * hidden * 2 > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
+  if (n == 0 || g_dry_run.load()) return GQA_OK;
+  gqa::QkvArgs a{};
+  a.n = n;
+  a.hidden = hidden;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.head_dim = head_dim;
+  a.x = x;
+  a.wq = w_q;
+  a.wk = w_k;
+  a.wv = w_v;
+  a.bq = b_q;
+  a.bk = b_k;
+  a.bv = b_v;
+  a.q_out = q_out;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.wr.n = n;
+  a.wr.heads = heads;
+  a.wr.kv_heads = kv_heads;
+  a.wr.head_dim = head_dim;
+  a.wr.dtype = dtype;
+  a.wr.positions = positions;
+  a.wr.rope_table = rope_table;
+  a.wr.rope_max_pos = rope_max_pos;
+  a.wr.cache_kind = cache_kind;
+  a.wr.cache_k = cache_k;
+  a.wr.cache_v = cache_v;
+  a.wr.cache_dim0 = cache_dim0;
+  a.wr.cache_seq = cache_seq;
+  a.wr.rows = rows;
+  a.wr.slots = slots;
+  a.wr.table = table;
+  a.wr.table_rows = table_rows;
+  a.wr.table_pages = table_pages;
+  return hip_status(gqa::launch_qkv(a, static_cast<hipStream_t>(stream)));
+}
 }  // extern "C"

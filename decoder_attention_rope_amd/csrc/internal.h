@@ -78,6 +78,26 @@ struct PrefillArgs {
   int num_pages;
 };
 
+// Fused projections: x [n, hidden] times the q / k / v weights ([features,
+// hidden] each), + optional biases, rounded to bf16, rotated and written
+// (q to q_out, k / v to k_out / v_out and the cache described by wr, whose
+// q / k / v fields are unused).
+struct QkvArgs {
+  int n, hidden, heads, kv_heads, head_dim;
+  const void* x;
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  const void* bq;
+  const void* bk;
+  const void* bv;
+  void* q_out;
+  void* k_out;
+  void* v_out;
+  RopeWriteArgs wr;
+};
+hipError_t launch_qkv(const QkvArgs& a, hipStream_t stream);
+
 hipError_t launch_rope_table(int head_dim, int max_pos, float theta, int dtype, void* table,
                              hipStream_t stream);
 hipError_t launch_rope_write(const RopeWriteArgs& a, hipStream_t stream);

@@ -15,6 +15,7 @@
 // exact there) and rounded once to T.
 #include "common.h"
 #include "internal.h"
+#include "rope_common.h"
 
 namespace gqa {
 
@@ -47,78 +48,6 @@ __global__ void rope_table_kernel(int head_dim, int max_pos, float theta, T* tab
 // ---------------------------------------------------------------------------
 // Fused rotate + write.
 // ---------------------------------------------------------------------------
-template <typename T>
-__device__ __forceinline__ void rotate_chunk(u32x4& lo, u32x4& hi, const u32x4& cw,
-                                             const u32x4& sw);
-
-// bf16: 8 elements per 16-byte chunk.
-template <>
-__device__ __forceinline__ void rotate_chunk<uint16_t>(u32x4& lo, u32x4& hi, const u32x4& cw,
-                                                       const u32x4& sw) {
-  float xl[8], xh[8], c[8], s[8];
-  Elem<uint16_t>::to_f32(lo, xl);
-  Elem<uint16_t>::to_f32(hi, xh);
-  Elem<uint16_t>::to_f32(cw, c);
-  Elem<uint16_t>::to_f32(sw, s);
-  uint16_t yl[8], yh[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const double ylo = (double)xl[e] * (double)c[e] - (double)xh[e] * (double)s[e];
-    const double yhi = (double)xh[e] * (double)c[e] + (double)xl[e] * (double)s[e];
-    yl[e] = f64_to_bf16(ylo);
-    yh[e] = f64_to_bf16(yhi);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo[i] = (uint32_t)yl[2 * i] | ((uint32_t)yl[2 * i + 1] << 16);
-    hi[i] = (uint32_t)yh[2 * i] | ((uint32_t)yh[2 * i + 1] << 16);
-  }
-}
-
-// f32: 4 elements per chunk.
-template <>
-__device__ __forceinline__ void rotate_chunk<float>(u32x4& lo, u32x4& hi, const u32x4& cw,
-                                                    const u32x4& sw) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const double xl = (double)__uint_as_float(lo[e]);
-    const double xh = (double)__uint_as_float(hi[e]);
-    const double c = (double)__uint_as_float(cw[e]);
-    const double s = (double)__uint_as_float(sw[e]);
-    lo[e] = __float_as_uint((float)(xl * c - xh * s));
-    hi[e] = __float_as_uint((float)(xh * c + xl * s));
-  }
-}
-
-// Element offset of token t / kv head kh in the cache, or -1 when write_at
-// masks the write out.
-__device__ __forceinline__ long long cache_offset(const RopeWriteArgs& a, int t, int kh) {
-  const int D = a.head_dim;
-  switch (a.cache_kind) {
-    case 1: {  // contiguous [batch, kv_heads, max_seq, D]
-      const int row = a.rows ? a.rows[t] : 0;
-      const int pos = a.positions[t];
-      if (row < 0 || row >= a.cache_dim0 || pos < 0 || pos >= a.cache_seq) return -1;
-      return (((long long)row * a.kv_heads + kh) * a.cache_seq + pos) * D;
-    }
-    case 2: {  // paged, logical position through the table
-      const int row = a.rows ? a.rows[t] : 0;
-      const long long pos = a.positions[t];
-      if (row < 0 || row >= a.table_rows) return -1;
-      if (pos < 0 || pos >= (long long)a.table_pages * kPageSize) return -1;
-      const int page = a.table[(long long)row * a.table_pages + pos / kPageSize];
-      if (page < 0 || page >= a.cache_dim0) return -1;
-      return (((long long)page * a.kv_heads + kh) * kPageSize + pos % kPageSize) * D;
-    }
-    case 3: {  // paged, physical slot
-      const long long slot = a.slots[t];
-      if (slot < 0 || slot >= (long long)a.cache_dim0 * kPageSize) return -1;
-      return (((slot / kPageSize) * a.kv_heads + kh) * kPageSize + slot % kPageSize) * D;
-    }
-    default:
-      return -1;
-  }
-}
 
 template <typename T>
 __global__ __launch_bounds__(256) void rope_write_kernel(RopeWriteArgs a) {

@@ -130,6 +130,36 @@ int gqa_rope_write_kv(int32_t n, int32_t heads, int32_t kv_heads, int32_t head_d
                       void* stream);
 
 /*
+ * gqa_qkv_rope_write -- the q / k / v projections of GroupedQueryAttention
+ * (Linnet "examples/01-llama" page, src/attention.linnet `forward` /
+ * `decode`: q_proj, k_proj, v_proj are std.nn.linear::Linear, y = x W^T + b
+ * as a Tensor of T) fused with the rotation and the cache write of
+ * gqa_rope_write_kv: q = rope(q_proj(x)), k = rope(k_proj(x)), v = v_proj(x),
+ * each projection rounded to T before the rotation, the rotation exact and
+ * rounded once to T.
+ *   x [n, hidden]; w_q [heads*D, hidden], w_k and w_v [kv_heads*D, hidden]
+ *   (the modules' `weight` layout [Out, In]); b_q [heads*D], b_k, b_v
+ *   [kv_heads*D] or NULL (no bias). q_out [n, heads, D] (required); k_out,
+ *   v_out [n, kv_heads, D] or NULL. positions [n], rope_table / rope_max_pos
+ *   and the cache arguments as gqa_rope_write_kv (rope_table NULL: no
+ *   rotation; cache_kind NONE: no cache write).
+ *   Built for T = bf16, D in {64, 128}, hidden % 64 == 0 and
+ *   (heads + 2 kv_heads) * D % 128 == 0 (else GQA_ERR_UNSUPPORTED). The
+ *   projection sums run in f32 on the matrix cores, so a result that lies
+ *   within an f32 rounding of a bf16 rounding boundary may round the other way
+ *   than the exact sum would.
+ */
+int gqa_qkv_rope_write(int32_t n, int32_t hidden, int32_t heads, int32_t kv_heads,
+                       int32_t head_dim, int32_t dtype, const void* x, const void* w_q,
+                       const void* w_k, const void* w_v, const void* b_q, const void* b_k,
+                       const void* b_v, const int32_t* positions, const void* rope_table,
+                       int32_t rope_max_pos, void* q_out, void* k_out, void* v_out,
+                       int32_t cache_kind, void* cache_k, void* cache_v, int32_t cache_dim0,
+                       int32_t cache_seq, const int32_t* rows, const int32_t* slots,
+                       const int32_t* table, int32_t table_rows, int32_t table_pages,
+                       void* stream);
+
+/*
  * gqa_prefill_packed -- attention of `packed<P>` / prefill_packed: token i
  * attends key j iff segments[i] == segments[j] && positions[j] <=
  * positions[i] (the `own` mask, literal: any segment ids, any order) and the
