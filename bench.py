@@ -250,7 +250,8 @@ def main():
     c_flops = 4 * D * H * int(np.sum(c_pos.astype(np.int64) + 1))
     c_tflops = c_flops / c_s / 1e12
     chunk_roof = {"bound": "mfma", "achieved": c_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-                  "unit": "TFLOP/s", "frac": c_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                  "unit": "TFLOP/s", "frac": c_tflops / MFMA_BF16_PEAK_TFLOPS,
+                  "traffic": traffic_for("prefill_cached_paged", ["prefill.hip", "common.h"]),
                   "algorithmic_flops": c_flops, "avg_us": c_s * 1e6,
                   "workload": f"{ec['rows']} rows, prefixes U[{ec['pre_lo']}, {ec['pre_hi']}] "
                               f"({int(c_pre.sum())} keys), chunk {ec['chunk']}, paged"}
@@ -325,7 +326,8 @@ def main():
     q_flops = 2 * P * hid * (H + 2 * KVH) * D
     qkv_roof = {"bound": "mfma", "achieved": q_flops / q_s / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": q_flops / q_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                "traffic": None, "algorithmic_flops": q_flops, "avg_us": q_s * 1e6,
+                "traffic": traffic_for("qkv_rope_write", ["qkv.hip", "rope_common.h", "common.h"]),
+                "algorithmic_flops": q_flops, "avg_us": q_s * 1e6,
                 "hipblaslt_gemm_only_us": mm_s * 1e6,
                 "workload": f"{P} tokens x hidden {hid} -> (32 + 8 + 8) x 128, rope, contiguous cache"}
     del gx, gwq, gwk, gwv, gwcat, g_q
