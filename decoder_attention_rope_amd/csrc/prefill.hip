@@ -19,11 +19,12 @@
 // * The key order inside a 32-key block is permuted (bits 2 and 3 of the row
 //   index swapped) so that the probabilities a lane holds after the softmax
 //   are exactly the B operand of the P.V product O^T = V^T P^T; no data moves
-//   between lanes. V is written to LDS transposed (dimension-major, XOR
-//   swizzled) while it is staged, so the A operand V^T is one 16-byte LDS
-//   read per lane.
-// * K/V tiles of 64 keys are double-buffered in LDS: the global loads of the
-//   next tile are in flight while the current tile is on the matrix cores.
+//   between lanes. V stays key-major in LDS (16-byte chunks XOR-swizzled) and
+//   the A operand V^T is read with transposing 8-byte LDS reads.
+// * K/V tiles of 64 keys go from memory straight into LDS (buffer loads with
+//   an LDS destination, no registers), issued one tile ahead and spread over
+//   the matrix steps; V is loaded one tile behind K, because a slot runs the
+//   S^T of one tile next to the P.V of the previous one.
 // * Tiles that cannot hold an allowed key are skipped using per-tile
 //   [min, max] summaries of segments and positions; tiles in which every pair
 //   is allowed skip the per-element mask. The exact `own` predicate is
@@ -234,16 +235,21 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_order_kernel(Plan pl) {
 // ---------------------------------------------------------------------------
 // LDS layouts (byte offsets; every access below is conflict-free in the
 // 64-bank, 4-byte-bank LDS of gfx950, where a 16-byte access is served 16
-// lanes at a time and an 8-byte access 32 lanes at a time).
-//   K tile   [64 rows][D], row stride 2 D + 16 bytes. Key r of the tile sits
-//            in row kappa(r), so lane l reads row l % 32 (+32): the 16 rows
-//            of a 16-lane group start 16 bytes apart modulo 256.
-//   V^T tile [D rows][64 keys], row stride 144 bytes: the 16 rows a 16-lane
-//            group reads start 16 bytes apart modulo 256, and the staging
-//            threads of a 32-lane group write 16 key groups of 2 dimension
-//            rows whose starts differ by 128 bytes modulo 256.
-// With padded (not XOR-swizzled) rows every read address is one per-lane
-// base plus a compile-time offset.
+// lanes at a time and an 8-byte access 32 lanes at a time). Tiles are filled
+// by direct buffer-to-LDS loads, which place lane l's 16 bytes at
+// base + 16 l, so a layout is chosen through the global address each lane
+// fetches.
+//   K tile [64 rows][D], row stride 2 D + 16 bytes (D / 8 + 1 chunks of 16
+//          bytes; lanes that land on a row's pad chunk fetch out of range and
+//          write zeros). Row r holds key kappa(r) of the tile, so lane l
+//          reads row l % 32 (+32): the 16 rows of a 16-lane group start 16
+//          bytes apart modulo 256.
+//   V tile [64 rows][D], row stride 2 D, 16-byte chunk c of row r stored at
+//          chunk c ^ vswz(r). The P.V operand is read with transposing
+//          8-byte reads: a 16-lane group covers 4 keys x 16 dimensions, and
+//          with the swizzle the 4 rows x 4 chunks a 32-lane half reads fall
+//          on distinct banks.
+//   positions, segments: 64 x 4 bytes each per tile (packed keys).
 // ---------------------------------------------------------------------------
 // Lanes l and l ^ 32 own the two key halves of one query column; these
 // combine their values (one cross-half lane swap, no LDS round trip).
@@ -273,20 +279,26 @@ __device__ __forceinline__ int kappa(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-template <int D>
+template <int D, int NKB, int NPB>
 struct Lds {
-  static constexpr int kStride = 2 * D + 16;       // K row stride (bytes)
-  static constexpr int vStride = 2 * kBK + 16;     // V^T row stride (bytes)
-  static constexpr int kBytes = kBK * kStride;     // one K tile
-  static constexpr int vBytes = D * vStride;       // one V^T tile
+  static constexpr int kStride = 2 * D + 16;     // K row stride (bytes)
+  static constexpr int kChunks = D / 8 + 1;      // 16-byte chunks per K row
+  static constexpr int vStride = 2 * D;          // V row stride (bytes)
+  static constexpr int kBytes = kBK * kStride;   // one K tile = kChunks KiB
+  static constexpr int vBytes = kBK * vStride;   // one V tile = D / 8 KiB
   static constexpr int kOff(int buf) { return buf * kBytes; }
-  static constexpr int vOff(int buf) { return 2 * kBytes + buf * vBytes; }
-  static constexpr int posOff(int buf) { return 2 * kBytes + 2 * vBytes + buf * 2 * kBK * 4; }
-  static constexpr int segOff(int buf) { return posOff(buf) + kBK * 4; }
-  static constexpr int total = posOff(2);
+  static constexpr int vOff(int buf) { return NKB * kBytes + buf * vBytes; }
+  static constexpr int posOff(int buf) { return NKB * (kBytes + vBytes) + buf * 2 * kBK * 4; }
+  static constexpr int total = posOff(NPB);
 };
+// Chunk swizzle of V row r (see above).
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
 
 typedef __attribute__((address_space(3))) char LdsByte;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 template <typename T>
 __device__ __forceinline__ T lds_ld(const LdsByte* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
@@ -296,27 +308,54 @@ __device__ __forceinline__ void lds_st(LdsByte* p, const T& v) {
   *reinterpret_cast<__attribute__((address_space(3))) T*>(p) = v;
 }
 
-// Buffer resource over one key tile of a [P, kv_heads, D] tensor, starting at
-// head kh of the tile's first token and covering exactly its n_rows valid
-// rows: loads past them return zeros (dword 3 = raw, untyped 32-bit access).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, long long elem_off,
-                                                            int n_rows, int row_bytes, int tail_bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(static_cast<const char*>(base) + 2 * elem_off), (short)0,
-      (n_rows - 1) * row_bytes + tail_bytes, 0x00020000);
+// Raw buffer descriptor (base, num_records bytes, untyped 32-bit access) as
+// four scalar registers, for the asm loads below.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, int num_records) {
+  const unsigned long long p = reinterpret_cast<unsigned long long>(base);
+  i32x4 r;
+  r[0] = (int)(uint32_t)p;
+  r[1] = (int)((p >> 32) & 0xffff);
+  r[2] = num_records;
+  r[3] = 0x00020000;
+  return r;
+}
+// Direct buffer-to-LDS load: BYTES (4 or 16) per lane from base + voffset,
+// written at LDS byte address lds + BYTES * lane (zeros for lanes out of
+// range). Issued as asm so that the compiler's wait-counter bookkeeping
+// leaves these loads alone: the kernel waits for them explicitly, a tile or
+// two after issue, and an automatic wait before each LDS read would drain
+// them at once.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(i32x4 rsrc, uint32_t lds, int voffset) {
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voffset), "s"(rsrc) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voffset), "s"(rsrc) : "memory", "m0");
 }
 
+// Wavefronts per workgroup, and how many key tiles ahead of the matrix work
+// the tile loads run. Two 4-wave workgroups share a CU, so the two
+// wavefronts of a SIMD belong to different workgroups and never wait on each
+// other's barriers; with loads one tile ahead a workgroup's LDS (two K, two
+// V and three position buffers) lets two fit.
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillAhead = 1;
+
 template <int D, int GW, int SRC>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl) {
-  constexpr int SUB = 4 / GW;   // query sub-tiles of 32 per workgroup
+__global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill_kernel(PrefillArgs a, Plan pl) {
+  constexpr int NW = kPrefillWaves;
+  constexpr int AHEAD = kPrefillAhead;
+  constexpr int NKB = AHEAD + 1;  // K (and V) buffers
+  constexpr int NPB = AHEAD + 2;  // position buffers
+  constexpr int SUB = NW / GW;  // query sub-tiles of 32 per workgroup
   constexpr int TQ = 32 * SUB;  // query tokens per workgroup
   constexpr int KS = D / 16;    // k-steps of QK^T over the head dim
   constexpr int MD = D / 32;    // 32-row blocks of O^T
-  constexpr int LPR = D / 8;    // 16-byte chunks per key row
-  constexpr int RPT = D / 32;   // key rows staged per thread
-  constexpr int NA = kBK / RPT; // key groups of RPT rows
-  static_assert(LPR * NA == 256, "staging covers the tile");
-  using L = Lds<D>;
+  static_assert(TQ <= 128, "cache-row leaders fit a 128-bit mask");
+  using L = Lds<D, NKB, NPB>;
 
   __shared__ __attribute__((aligned(16))) char smem_raw[L::total];
   LdsByte* smem = (LdsByte*)smem_raw;
@@ -332,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
   const int qt = __builtin_amdgcn_readfirstlane(ld_const(pl.order, wi));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = wave % GW;
   const int st = wave / GW;
   const int h = kh * G + hg * GW + hl;
@@ -346,8 +385,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
   const int my_seg = SRC == kSrcPacked || a.segments ? a.segments[q_ld] : 0;
   // Packed keys: positions are token positions in [0, 2^31), so the
   // difference of two fits in 32 bits and an unsigned compare tests
-  // pos_k <= pos_q together with the window. Keys past P carry position
-  // INT_MIN, which fails it.
+  // pos_k <= pos_q together with the window.
   const uint32_t wlim = a.window > 0 ? (uint32_t)a.window : 0x80000000u;
   // Cache keys: this query sees key slots [my_lo, my_hi] of cache row my_seg
   // (empty for a row outside the cache).
@@ -377,64 +415,121 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
   rng.x = __builtin_amdgcn_readfirstlane(rng.x);
   rng.y = __builtin_amdgcn_readfirstlane(rng.y);
 
-  // Staging. K: thread (c, ar) loads 16-byte chunk c of key rows
-  // ar * RPT + i (LPR consecutive lanes cover a row). V: thread (av, cv) with
-  // the key group fastest, so the transposed LDS writes spread over the banks.
+  // Tile loads go straight from memory into LDS, AHEAD key tiles ahead of
+  // the matrix work, spread over the workgroup's wavefronts: a K tile is
+  // L::kChunks 1-KiB loads (the last one by wave 0), a V tile D / 8, and for
+  // packed keys the positions (wave 1) and segments (wave 2) one 256-byte
+  // load each. Lane offsets (bytes from the tile's first row) are fixed per
+  // wavefront; padding lanes fetch out of range and write zeros.
   const int row_bytes = SRC == kSrcPacked ? a.kv_heads * D * 2 : D * 2;
-  const int kc = tid % LPR, ka = tid / LPR;
-  const int va = tid % NA, vc = tid / NA;
-  int k_goff[RPT], v_goff[RPT];
+  constexpr int KU = (L::kChunks - 1) / NW;  // K loads per wavefront, all waves
+  constexpr int VU = (D / 8) / NW;           // V loads per wavefront
+  static_assert(KU * NW == L::kChunks - 1 && VU * NW == D / 8, "loads cover the tiles");
+  constexpr int kOob = 0x40000000;           // past every tile's range
+  int k_voff[KU + 1], v_voff[VU];
+  auto k_lane_off = [&](int i) {
+    const int p = 64 * i + lane;  // 16-byte chunk of the padded tile
+    const int row = p / L::kChunks, ch = p - row * L::kChunks;
+    return ch == D / 8 ? kOob : kappa(row) * row_bytes + ch * 16;
+  };
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    k_goff[i] = (ka * RPT + i) * row_bytes + kc * 16;
-    v_goff[i] = (va * RPT + i) * row_bytes + vc * 16;
+  for (int u = 0; u < KU; ++u) k_voff[u] = k_lane_off(wave + NW * u);
+  k_voff[KU] = k_lane_off(L::kChunks - 1);
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int p = 64 * (wave + NW * u) + lane;
+    const int row = p / (D / 8), ch = p % (D / 8);
+    v_voff[u] = row * row_bytes + ((ch ^ vswz<D>(row)) << 4);
   }
-  const int k_wr = kappa(ka * RPT) * L::kStride + kc * 16;
-  const int v_wr = 8 * vc * L::vStride + va * RPT * 2;
+  // Loads per wavefront per tile set, and the waits: a slot issues one K set
+  // and one V set, and before its closing barrier waits for the sets the
+  // previous slot issued.
+  const bool extra_load = wave == 0 || (SRC == kSrcPacked && (wave == 1 || wave == 2));
   const int k_rd = qn * L::kStride + hf * 16;
-  const int v_rd = qn * L::vStride + hf * 16;
-  u32x4 kreg[RPT], vreg[RPT];
-  int pos_reg = 0, seg_reg = 0, staged_rows = 0;
+  // P.V operand reads (transposing, 4 keys x 16 dimensions per 16-lane
+  // group): lane l of group g = l / 16 supplies the address of key
+  // 8 (g / 2) + (l % 16) / 4 (+4 for the second read), dimensions
+  // 32 md + 16 (g % 2) + 4 (l % 4) .. +3; it receives 4 keys of dimension
+  // 32 md + l % 32.
+  int v_rd[MD];
+  {
+    const int vg = lane >> 4, vs = lane & 15;
+    const int row = 8 * (vg >> 1) + (vs >> 2);
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const int ch = 4 * md + 2 * (vg & 1) + ((vs >> 1) & 1);
+      v_rd[md] = row * L::vStride + ((ch ^ vswz<D>(row)) << 4) + ((vs & 1) << 3);
+    }
+  }
 
-  // A key tile: tile index kt (64 keys) of cache row r, at pool page `page`.
+  // A key tile: tile index kt (64 keys) of cache row r, at pool page `page`;
+  // full: every pair with the query tile is allowed.
   struct TileRef {
-    int kt, r, page, rows;  // rows: cache slots of the tile anyone may see
+    int kt, r, page, rows, full;  // rows: cache slots of the tile anyone may see
   };
-  auto load_tile = [&](TileRef t) {
-    const int kt = t.kt;
+  // Buffer resource over one operand (K or V) of a key tile: 64 key slots of
+  // one cache plane, or 64 packed tokens at KV head kh.
+  auto tile_src = [&](TileRef t, const void* base) {
+    long long e0;
+    int n_rows;
     if constexpr (SRC != kSrcPacked) {
-      // 64 key slots of one cache plane (contiguous rows of D elements).
-      const int n_rows = t.rows;
-      const long long e0 = SRC == kSrcPaged
-                               ? ((long long)t.page * a.kv_heads + kh) * kBK * D
-                               : (((long long)t.r * a.kv_heads + kh) * a.cap + (long long)kt * kBK) * D;
-      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(a.k, e0, n_rows, row_bytes, 2 * D);
-      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(a.v, e0, n_rows, row_bytes, 2 * D);
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_goff[i], 0, 0);
-        vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_goff[i], 0, 0);
-      }
-      return;
+      e0 = SRC == kSrcPaged ? ((long long)t.page * a.kv_heads + kh) * kBK * D
+                            : (((long long)t.r * a.kv_heads + kh) * a.cap + (long long)t.kt * kBK) * D;
+      n_rows = t.rows;
+    } else {
+      e0 = (long long)t.kt * kBK * a.kv_heads * D + (long long)kh * D;
+      n_rows = min(kBK, P - t.kt * kBK);
     }
-    const int n_rows = min(kBK, P - kt * kBK);
-    const long long e0 = (long long)kt * kBK * a.kv_heads * D + (long long)kh * D;
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(a.k, e0, n_rows, row_bytes, 2 * D);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(a.v, e0, n_rows, row_bytes, 2 * D);
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_goff[i], 0, 0);
-      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_goff[i], 0, 0);
-    }
-    const __amdgpu_buffer_rsrc_t rp =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(a.positions + (long long)kt * kBK), (short)0, 4 * n_rows, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(a.segments + (long long)kt * kBK), (short)0, 4 * n_rows, 0x00020000);
-    const int lo = (tid & (kBK - 1)) * 4;
-    pos_reg = __builtin_amdgcn_raw_buffer_load_b32(rp, lo, 0, 0);
-    seg_reg = __builtin_amdgcn_raw_buffer_load_b32(rs, lo, 0, 0);
-    staged_rows = n_rows;
+    return raw_rsrc(static_cast<const char*>(base) + 2 * e0, (n_rows - 1) * row_bytes + 2 * D);
   };
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  // Load u of a K set (tile t into K buffer kb and position buffer pb).
+  struct KSet {
+    i32x4 rk, rp, rs;
+  };
+  auto k_set = [&](TileRef t) {
+    KSet s;
+    s.rk = tile_src(t, a.k);
+    if constexpr (SRC == kSrcPacked) {
+      const int n_rows = min(kBK, P - t.kt * kBK);
+      s.rp = raw_rsrc(a.positions + (long long)t.kt * kBK, 4 * n_rows);
+      s.rs = raw_rsrc(a.segments + (long long)t.kt * kBK, 4 * n_rows);
+    } else {
+      s.rp = s.rk;
+      s.rs = s.rk;
+    }
+    return s;
+  };
+  auto k_load = [&](const KSet& s, int kb, int pb, auto uc) {
+    constexpr int u = decltype(uc)::value;
+    if constexpr (u < KU) {
+      lds_dma<16>(s.rk, lds0 + L::kOff(kb) + 1024 * (wave + NW * u), k_voff[u]);
+    } else {
+      if (wave == 0) {
+        lds_dma<16>(s.rk, lds0 + L::kOff(kb) + 1024 * (L::kChunks - 1), k_voff[KU]);
+      } else if (SRC == kSrcPacked && wave == 1) {
+        lds_dma<4>(s.rp, lds0 + L::posOff(pb), lane * 4);
+      } else if (SRC == kSrcPacked && wave == 2) {
+        lds_dma<4>(s.rs, lds0 + L::posOff(pb) + kBK * 4, lane * 4);
+      }
+    }
+  };
+  auto v_load = [&](i32x4 rv, int vb, auto uc) {
+    constexpr int u = decltype(uc)::value;
+    lds_dma<16>(rv, lds0 + L::vOff(vb) + 1024 * (wave + NW * u), v_voff[u]);
+  };
+  // Wait until the tile loads of all but the last AHEAD - 1 slots have
+  // landed (a slot issues KU + VU loads, one more on the waves with an extra
+  // load).
+  auto wait_loads = [&](bool extra) {
+    constexpr int n0 = (AHEAD - 1) * (KU + VU), n1 = (AHEAD - 1) * (KU + VU + 1);
+    static_assert(n1 < 16, "vmcnt field");
+    if (extra) __builtin_amdgcn_s_waitcnt(0xF70 | n1);
+    else __builtin_amdgcn_s_waitcnt(0xF70 | n0);
+  };
+  // Workgroup barrier that neither waits for the loads in flight nor lets
+  // the compiler move memory accesses across it.
+  auto barrier = [&]() { asm volatile("s_barrier" ::: "memory"); };
 
   // Walk the visited key tiles with the prepared masks: scalar bit scans,
   // one scalar load per group of 64 key tiles. Phase 0 visits the tiles in
@@ -544,16 +639,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
     c_fhi = min(c_khi, c_single ? (min(lo, a.cap - 1) + 1) / kBK - 1 : -1);
     return true;
   };
-  // Page ids of 64 consecutive key tiles of one table row, one per lane.
-  int tab_row = -1, tab_base = 0, tab_v = -1;
+  // Page id of key tile kt of table row r (a scalar load: the walk runs
+  // while tile loads are in flight, and a vector load would wait for them).
   auto page_of = [&](int r, int kt) {
-    if (r != tab_row || kt < tab_base || kt >= tab_base + 64) {
-      tab_row = r;
-      tab_base = kt & ~63;
-      const int idx = tab_base + lane;
-      tab_v = idx < a.table_pages ? a.table[(long long)r * a.table_pages + idx] : -1;
-    }
-    return __builtin_amdgcn_readlane(tab_v, kt - tab_base);
+    return kt < a.table_pages ? ld_const(a.table, (long long)r * a.table_pages + kt) : -1;
   };
   bool c_started = false;
   auto cache_next = [&](int& phase) {
@@ -600,109 +689,157 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
     return t;
   };
 
-  // One tile is 4 C matrix steps in four blocks (C = D / 16):
-  //   block 0  S^T for keys 0..31        (one accumulator chain)
-  //   block 1  S^T for keys 32..63       with the softmax of keys 0..31
-  //   block 2  P.V of keys 0..31         with the softmax of keys 32..63
-  //   block 3  P.V of keys 32..63        with the staging of the next tile
-  // On gfx950 a SIMD overlaps an MFMA with vector instructions of the same
-  // wavefront issued in its shadow (not with another wave's), so each step
-  // issues one MFMA followed by a slice of vector work, and a scheduling
-  // fence keeps that order. Matrix operands are read from LDS four steps
-  // ahead through a ring of registers. The O rescales of the lazy softmax
-  // (rare) sit between blocks 1 and 2 and between blocks 2 and 3.
-  constexpr int C = D / 16;
+  // Software pipeline over 32-key halves of the key tiles. Half-slot j
+  // issues the S^T MFMAs of half j, the P.V MFMAs of half j - 2 (alternating,
+  // so the S^T accumulator chain never waits on itself) and, in the shadow of
+  // those MFMAs, the softmax of half j - 1. A slot is the two half-slots of
+  // key tile T: it reads K of tile T and V of tile T - 1 and issues the loads
+  // of K (and positions) of tile T + AHEAD and V of tile T + AHEAD - 1, so
+  // AHEAD + 1 K and V buffers and AHEAD + 2 position buffers rotate. On gfx950 a SIMD overlaps an MFMA
+  // with vector instructions issued in its shadow, so each step issues one
+  // MFMA followed by a slice of vector work, and a scheduling fence keeps
+  // that order; every slice's inputs were produced a step or more earlier.
+  // Matrix operands are read from LDS four steps ahead through a ring of
+  // registers. The O rescales of the lazy softmax (rare) close a half-slot
+  // whose softmax moved the reference.
+  constexpr int C = D / 16;        // S^T MFMAs (and P.V MFMAs) per half
   static_assert(KS == C && 2 * MD == C, "step counts");
-  u32x4 pw[4];
-  f32x16 s[2];
+  constexpr int HS = 2 * C;        // matrix steps per half-slot
+  constexpr int NSOFT = 14;        // softmax slices per half
+  constexpr int NLOAD = KU + 1 + VU;  // load steps at the start of a slot
+  static_assert(NLOAD <= HS, "loads fit the first half-slot");
+  u32x4 pw[4];                     // P of the halves of parity 0 and 1 (bf16)
+  f32x16 s[2];                     // S^T of the halves of parity 0 and 1
   bf16x8 ring[4];
-  float tmax = kNegInf, m_use = 0.f, alpha = 1.f, psum = 0.f;
+  float tmax = kNegInf, m_use = 0.f, alpha = 1.f;
+  float xa0 = 0.f, xa1 = 0.f, ea0 = 0.f, ea1 = 0.f, psa = 0.f, psb = 0.f;
 
-  // Operand of matrix step st (0 <= st < 4 C) of the tile in kb / vb.
-  auto operand = [&](const LdsByte* kb, const LdsByte* vb, auto stc) {
-    constexpr int st = decltype(stc)::value;
-    if constexpr (st < 2 * C) {
-      constexpr int hb = st / C, ks = st % C;
-      return lds_ld<bf16x8>(kb + hb * 32 * L::kStride + ks * 32);
+  // Operand of slot step g: half-slot h = g / HS, step i = g % HS; even
+  // steps are S^T MFMAs (K rows of half h of tile T), odd ones P.V MFMAs
+  // (V^T of keys of half h of tile T - 1, two transposing reads).
+  auto operand = [&](const LdsByte* kb, const LdsByte* vb, auto gc) {
+    constexpr int g = decltype(gc)::value;
+    constexpr int h = g / HS, i = g % HS;
+    if constexpr (i % 2 == 0) {
+      return lds_ld<bf16x8>(kb + h * 32 * L::kStride + (i / 2) * 32);
     } else {
-      constexpr int hb = (st - 2 * C) / C, j = (st - 2 * C) % C;
-      constexpr int ks = 2 * hb + j / MD, md = j % MD;
-      return lds_ld<bf16x8>(vb + 32 * md * L::vStride + ks * 32);
+      constexpr int j = i / 2, kk = j / MD, md = j % MD;
+      typedef __attribute__((address_space(3))) bf16x4 LdsV4;
+      const LdsByte* p = vb + v_rd[md] + 16 * (2 * h + kk) * L::vStride;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsV4*)p);
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsV4*)(p + 4 * L::vStride));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
-  auto mfma_step = [&](auto stc, const bf16x8& op) {
-    constexpr int st = decltype(stc)::value;
-    if constexpr (st < 2 * C) {
-      constexpr int hb = st / C, ks = st % C;
+  auto mfma_at = [&](auto gc, const bf16x8& op) {
+    constexpr int g = decltype(gc)::value;
+    constexpr int h = g / HS, i = g % HS;
+    if constexpr (i % 2 == 0) {
+      constexpr int ks = i / 2;
       if constexpr (ks == 0)
-        s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, __builtin_bit_cast(bf16x8, qf[ks]), f32x16{}, 0, 0, 0);
+        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, __builtin_bit_cast(bf16x8, qf[ks]), f32x16{}, 0, 0, 0);
       else
-        s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, __builtin_bit_cast(bf16x8, qf[ks]), s[hb], 0, 0, 0);
+        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, __builtin_bit_cast(bf16x8, qf[ks]), s[h], 0, 0, 0);
     } else {
-      constexpr int hb = (st - 2 * C) / C, j = (st - 2 * C) % C;
-      constexpr int ks = 2 * hb + j / MD, md = j % MD;
-      o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, __builtin_bit_cast(bf16x8, pw[ks]), o[md], 0, 0, 0);
+      constexpr int j = i / 2, kk = j / MD, md = j % MD;
+      o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, __builtin_bit_cast(bf16x8, pw[2 * h + kk]), o[md], 0, 0, 0);
     }
   };
 
-  // Slice c (0 <= c < C) of the mask and online-softmax update of one 32-key
-  // half (accumulator s[hb]): slice 0 masks and takes the row max, slice 1
-  // moves the lazy reference, slices 2 .. C - 1 turn pairs of scores into
-  // bf16 probabilities (pw[2 hb], pw[2 hb + 1], the B operands of P.V).
-  auto soft_slice = [&](const LdsByte* pb, int lo_j, int hi_j, auto hbc, auto cc, auto fullc) {
-    constexpr bool full = decltype(fullc)::value;
+  // Slice c (0 <= c < NSOFT) of the mask and online-softmax update of the
+  // 32-key half hb of a tile (accumulator s[hb]):
+  //   0, 1   mask (when masked) rows 8c .. 8c + 7 and fold them into the max
+  //   2      combine the two lane halves' maxima
+  //   3      move the lazy reference
+  //   4 .. 13  probabilities as a three-stage pipeline over the 8 row pairs
+  //          (slice 4 + k: pack pair k - 2 to bf16 and add it to the sums,
+  //          exponentiate pair k - 1, scale pair k), so no instruction waits
+  //          on one issued in the same slice.
+  auto soft_slice = [&](const LdsByte* pb, int lo_j, int hi_j, int n_j, auto hbc, auto cc, bool masked) {
     constexpr int hb = decltype(hbc)::value;
     constexpr int c = decltype(cc)::value;
-    if constexpr (c == 0) {
-      if constexpr (!full) {
-        // The literal own predicate (and the window) per element.
+    if constexpr (c < 2) {
+      if (__builtin_expect(masked, 0)) {
+        // The literal own predicate (and the window) per element; rows
+        // 8c .. 8c + 7 are the 8 consecutive keys jb + 8 hf + e.
+        constexpr int jb = 32 * hb + 16 * c;
+        if constexpr (SRC == kSrcPacked) {
+          const LdsByte* pp = pb + (jb + 8 * hf) * 4;
+          // Keys past P (zeros in LDS) are excluded by index: e < e_end.
+          const int e_end = n_j - jb - 8 * hf;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = 32 * hb + 16 * (r >> 3) + 8 * hf + (r & 7);
-          bool ok;
-          if constexpr (SRC == kSrcPacked) {
-            const int kp = lds_ld<int>(pb + j * 4);
-            const int ksg = lds_ld<int>(pb + kBK * 4 + j * 4);
-            ok = (ksg == my_seg) & ((uint32_t)my_pos - (uint32_t)kp < wlim);
-          } else {
-            // Key slot kt * 64 + j of the tile's row.
-            ok = (j >= lo_j) & (j <= hi_j);
+          for (int q4 = 0; q4 < 2; ++q4) {
+            const u32x4 kp = lds_ld<u32x4>(pp + 16 * q4), ksg = lds_ld<u32x4>(pp + kBK * 4 + 16 * q4);
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const int e = 4 * q4 + e4;
+              const bool ok = ((int)ksg[e4] == my_seg) & ((uint32_t)my_pos - kp[e4] < wlim) & (e < e_end);
+              s[hb][8 * c + e] = ok ? s[hb][8 * c + e] : kNegInf;
+            }
           }
-          s[hb][r] = ok ? s[hb][r] : kNegInf;
+        } else {
+          // Key slot kt * 64 + jb + 8 hf + e of the tile's row is visible
+          // for e in [e_lo, e_hi].
+          const int e_lo = lo_j - jb - 8 * hf, e_hi = hi_j - jb - 8 * hf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[hb][8 * c + e] = ((e >= e_lo) & (e <= e_hi)) ? s[hb][8 * c + e] : kNegInf;
         }
       }
-      tmax = kNegInf;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[hb][r]);
-    } else if constexpr (c == 1) {
+      const float m0 = fmaxf(fmaxf(s[hb][8 * c], s[hb][8 * c + 1]), s[hb][8 * c + 2]);
+      const float m1 = fmaxf(fmaxf(s[hb][8 * c + 3], s[hb][8 * c + 4]), s[hb][8 * c + 5]);
+      const float m2 = fmaxf(s[hb][8 * c + 6], s[hb][8 * c + 7]);
+      const float mc = fmaxf(fmaxf(m0, m1), m2);
+      tmax = c == 0 ? mc : fmaxf(tmax, mc);
+      // Keep this slice's work in its step (the compiler would merge it
+      // into the next slice, past the mask branch).
+      asm volatile("" : "+v"(tmax));
+    } else if constexpr (c == 2) {
       // Online softmax in the log2 domain. scale > 0, so the row max of the
-      // scaled scores is the scaled row max of the raw ones; m_run is the
-      // lazy reference (see kLazyMaxLog2).
+      // scaled scores is the scaled row max of the raw ones.
       tmax = pair_max(tmax) * a.scale_log2;
+      asm volatile("" : "+v"(tmax));
+    } else if constexpr (c == 3) {
+      // m_run is the lazy reference (see kLazyMaxLog2).
       const float m_new = (tmax > m_run + kLazyMaxLog2) ? tmax : m_run;
       m_use = (m_new == kNegInf) ? 0.f : m_new;
       alpha = fast_exp2(m_run - m_use);
       m_run = m_new;
-      psum = 0.f;
+      psa = 0.f;
+      psb = 0.f;
+      asm volatile("" : "+v"(m_use), "+v"(alpha), "+v"(m_run));
     } else {
-      constexpr int q0 = 8 * (c - 2) / (C - 2), q1 = 8 * (c - 1) / (C - 2);
-      static_for<q1 - q0>([&](auto qc) {
-        constexpr int r = 2 * (q0 + decltype(qc)::value);
-        const float p0 = fast_exp2(__builtin_fmaf(s[hb][r], a.scale_log2, -m_use));
-        const float p1 = fast_exp2(__builtin_fmaf(s[hb][r + 1], a.scale_log2, -m_use));
-        psum += p0 + p1;
-        pw[2 * hb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
-        // Materialize here: without the anchor the compiler sinks this work
+      constexpr int k = c - 4;
+      if constexpr (k >= 2) {
+        constexpr int r = 2 * (k - 2);
+        pw[2 * hb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(ea0, ea1);
+        psa += ea0;
+        psb += ea1;
+        // Materialize here: without the anchors the compiler sinks this work
         // past the rescale branch, next to its use, out of the MFMA shadow.
         asm volatile("" ::"v"(pw[2 * hb + (r >> 3)][(r & 7) >> 1]));
-      });
-      if constexpr (c == C - 1) l_run = l_run * alpha + psum;
+        asm volatile("" : "+v"(psa), "+v"(psb));
+      }
+      if constexpr (k >= 1 && k <= 8) {
+        ea0 = fast_exp2(xa0);
+        ea1 = fast_exp2(xa1);
+        asm volatile("" : "+v"(ea0), "+v"(ea1));
+      }
+      if constexpr (k <= 7) {
+        constexpr int r = 2 * k;
+        xa0 = __builtin_fmaf(s[hb][r], a.scale_log2, -m_use);
+        xa1 = __builtin_fmaf(s[hb][r + 1], a.scale_log2, -m_use);
+        asm volatile("" : "+v"(xa0), "+v"(xa1));
+      }
+      if constexpr (k == 9) {
+        l_run = l_run * alpha + (psa + psb);
+        asm volatile("" : "+v"(l_run));
+      }
     }
   };
 
   // Rescale O only when some lane's reference moved.
   auto rescale = [&](float f) {
-    if (__builtin_amdgcn_ballot_w64(f != 1.f) != 0) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(f != 1.f) != 0, 0)) {
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -710,111 +847,141 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
     }
   };
 
-  // Slice c of staging the next tile (registers -> LDS buffer nb).
-  auto store_slice = [&](int nb, auto cc) {
-    constexpr int c = decltype(cc)::value;
-    LdsByte* kbw = smem + nb * L::kBytes;
-    LdsByte* vbw = smem + 2 * L::kBytes + nb * L::vBytes;
-    if constexpr (c == 0) {
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) lds_st(kbw + k_wr + i * L::kStride, kreg[i]);
-    }
-    constexpr int e0 = (c == 0 || c == C - 1) ? 0 : 8 * (c - 1) / (C - 2);
-    constexpr int e1 = (c == 0 || c == C - 1) ? 0 : 8 * c / (C - 2);
-    static_for<e1 - e0>([&](auto ec) {
-      constexpr int e = e0 + decltype(ec)::value;
-      constexpr int w = e >> 1;
-      LdsByte* dst = vbw + v_wr + e * L::vStride;
-      if (RPT == 4) {
-        u32x2 pk;
-        pk[0] = (e & 1) ? pack_hi16(vreg[0][w], vreg[1 % RPT][w]) : pack_lo16(vreg[0][w], vreg[1 % RPT][w]);
-        pk[1] = (e & 1) ? pack_hi16(vreg[2 % RPT][w], vreg[3 % RPT][w])
-                        : pack_lo16(vreg[2 % RPT][w], vreg[3 % RPT][w]);
-        lds_st(dst, pk);
-      } else {
-        lds_st(dst, (e & 1) ? pack_hi16(vreg[0][w], vreg[1 % RPT][w]) : pack_lo16(vreg[0][w], vreg[1 % RPT][w]));
-      }
-    });
-    if (SRC == kSrcPacked && c == C - 1 && tid < kBK) {
-      // Applied here, once the loads have landed, not at issue time.
-      LdsByte* pbw = smem + L::posOff(nb);
-      lds_st(pbw + tid * 4, tid < staged_rows ? pos_reg : (int)0x80000000);
-      lds_st(pbw + kBK * 4 + tid * 4, seg_reg);
-    }
-  };
-
-  // The first tile, then the iteration: phase 0 (every pair allowed) and
-  // phase 1 (masked) tiles in turn.
-  auto first_tile = [&](int& phase) {
-    if constexpr (SRC == kSrcPacked) {
-      phase = 0;
-      return TileRef{advance(rng.x, phase), 0, 0, 0};
-    } else {
-      return cache_next(phase);
-    }
-  };
-  auto next_tile = [&](TileRef cur, int& phase) {
-    if constexpr (SRC == kSrcPacked) {
-      return TileRef{advance(cur.kt + 1, phase), 0, 0, 0};
-    } else {
-      return cache_next(phase);
-    }
-  };
+  // The key tiles in visiting order: phase 0 (every pair allowed) first,
+  // then phase 1 (masked); the online softmax does not depend on the order.
   auto valid = [&](TileRef t) { return SRC == kSrcPacked ? t.kt <= rng.y : t.kt >= 0; };
+  int wphase = 0;
+  int last_kt = -1;
+  auto gen = [&]() {
+    TileRef t;
+    if constexpr (SRC == kSrcPacked) {
+      const int kt = advance(last_kt < 0 ? rng.x : last_kt + 1, wphase);
+      t = TileRef{kt, 0, 0, 0, 0};
+      if (kt <= rng.y) last_kt = kt;
+    } else {
+      t = cache_next(wphase);
+    }
+    t.full = wphase == 0;
+    return t;
+  };
 
-  int phase = 0;
-  TileRef cur = first_tile(phase);
-  int buf = 0;
-  if (valid(cur)) {
-    load_tile(cur);
-    static_for<C>([&](auto cc) { store_slice(0, cc); });
-  }
-  __syncthreads();
-
-  // One tile from LDS buffer buf (every pair allowed when FULL). The next
-  // tile's global loads fly during the whole tile; its LDS buffer (buf ^ 1)
-  // was last read before the previous barrier. When there is no next tile
-  // the staging writes stale registers into that buffer, which nothing
-  // reads again.
-  auto tile = [&](auto fullc, TileRef t) {
-    const LdsByte* kb = smem + buf * L::kBytes + k_rd;
-    const LdsByte* vb = smem + 2 * L::kBytes + buf * L::vBytes + v_rd;
-    const LdsByte* pb = smem + L::posOff(buf);
-    // Cache keys: this lane's visible slots relative to the tile.
-    const int lo_j = my_lo - t.kt * kBK;
-    const int hi_j = (t.r == my_seg ? my_hi : -1) - t.kt * kBK;
-    static_for<4>([&](auto stc) { ring[decltype(stc)::value] = operand(kb, vb, stc); });
-    static_for<4 * C>([&](auto stc) {
-      constexpr int st = decltype(stc)::value;
-      if constexpr (st == 2 * C || st == 3 * C) rescale(alpha);
-      mfma_step(stc, ring[st & 3]);
-      if constexpr (st + 4 < 4 * C) ring[st & 3] = operand(kb, vb, std::integral_constant<int, st + 4>{});
-      if constexpr (st >= C && st < 2 * C)
-        soft_slice(pb, lo_j, hi_j, std::integral_constant<int, 0>{}, std::integral_constant<int, st - C>{}, fullc);
-      if constexpr (st >= 2 * C && st < 3 * C)
-        soft_slice(pb, lo_j, hi_j, std::integral_constant<int, 1>{}, std::integral_constant<int, st - 2 * C>{},
-                   fullc);
-      if constexpr (st >= 3 * C) store_slice(buf ^ 1, std::integral_constant<int, st - 3 * C>{});
+  // One slot (T = its index). DO_S: key tile t exists (its S^T and the
+  // softmax of its first half run, the loads of tiles kn (K) and vn (V) are
+  // issued, and the walk finds the tile after kn, t_gen); DO_PREV: tile tp
+  // (the previous one) exists (the softmax of its second half and its P.V
+  // run). Unless `masked`, every pair of both tiles is allowed (a uniform
+  // branch: one loop body serves both kinds of slot).
+  TileRef t_gen{-1, 0, 0, 0, 0};
+  auto slot = [&](bool masked, auto dosc, auto doprevc, TileRef t, TileRef tp, TileRef kn, TileRef vn, int T) {
+    constexpr bool DO_S = decltype(dosc)::value;
+    constexpr bool DO_PREV = decltype(doprevc)::value;
+    const LdsByte* kb = smem + L::kOff(T % NKB) + k_rd;
+    const LdsByte* vb = smem + L::vOff((T + NKB - 1) % NKB);
+    const LdsByte* pb_t = smem + L::posOff(T % NPB);
+    const LdsByte* pb_p = smem + L::posOff((T + NPB - 1) % NPB);
+    // Cache keys: this lane's visible slots relative to each tile; packed
+    // keys: the real keys of each tile.
+    const int lo_t = my_lo - t.kt * kBK;
+    const int hi_t = (t.r == my_seg ? my_hi : -1) - t.kt * kBK;
+    const int lo_p = my_lo - tp.kt * kBK;
+    const int hi_p = (tp.r == my_seg ? my_hi : -1) - tp.kt * kBK;
+    const int n_t = P - t.kt * kBK, n_p = P - tp.kt * kBK;
+    const KSet ks = k_set(kn);
+    const i32x4 rv = tile_src(vn, a.v);
+    auto has_mfma = [](auto gc) {
+      constexpr int i = decltype(gc)::value % HS;
+      return std::integral_constant<bool, (i % 2 == 0) ? DO_S : DO_PREV>{};
+    };
+    static_for<4>([&](auto gc) {
+      if constexpr (decltype(has_mfma(gc))::value) ring[decltype(gc)::value] = operand(kb, vb, gc);
+    });
+    static_for<2 * HS>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      constexpr int h = g / HS, i = g % HS;
+      if constexpr (decltype(has_mfma(gc))::value) mfma_at(gc, ring[g & 3]);
+      if constexpr (g + 4 < 2 * HS) {
+        using gn = std::integral_constant<int, g + 4>;
+        if constexpr (decltype(has_mfma(gn{}))::value) ring[(g + 4) & 3] = operand(kb, vb, gn{});
+      }
+      if constexpr (DO_S && h == 0 && i < NLOAD) {
+        if constexpr (i <= KU) k_load(ks, (T + AHEAD) % NKB, (T + AHEAD) % NPB, std::integral_constant<int, i>{});
+        else v_load(rv, (T + AHEAD - 1) % NKB, std::integral_constant<int, i - KU - 1>{});
+      }
+      if constexpr (DO_S && h == 1 && i == 0) t_gen = gen();
+      // Half-slot 0 runs the softmax of tile tp's second half, half-slot 1
+      // that of tile t's first half; slice c sits at step 2 + c (HS - 2) / NSOFT,
+      // clear of the latency of the S^T MFMAs it reads.
+      constexpr bool soft = h == 0 ? DO_PREV : DO_S;
+      if constexpr (soft) {
+        static_for<NSOFT>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          if constexpr (2 + c * (HS - 2) / NSOFT == i)
+            soft_slice(h == 0 ? pb_p : pb_t, h == 0 ? lo_p : lo_t, h == 0 ? hi_p : hi_t, h == 0 ? n_p : n_t,
+                       std::integral_constant<int, 1 - h>{}, cc, masked);
+        });
+      }
+      if constexpr (soft && i == HS - 1) rescale(alpha);
       __builtin_amdgcn_sched_barrier(0);
     });
-    __syncthreads();
-    buf ^= 1;
+    if constexpr (DO_S) {
+      // The loads of the previous slot have landed (this slot's may fly on).
+      wait_loads(extra_load);
+      barrier();
+    }
   };
-  while (valid(cur) && phase == 0) {
-    int nphase = phase;
-    const TileRef nxt = next_tile(cur, nphase);
-    if (valid(nxt)) load_tile(nxt);
-    tile(std::true_type{}, cur);
-    cur = nxt;
-    phase = nphase;
+
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  static_assert(AHEAD == 1 || AHEAD == 2, "tile look-ahead");
+  TileRef cur = gen();
+  if (valid(cur)) {
+    // The tiles after cur: n1, and n2 when the loads run two tiles ahead.
+    TileRef n1 = gen();
+    TileRef n2 = AHEAD >= 2 ? gen() : cur;
+    auto or_cur = [&](TileRef x, TileRef c) { return valid(x) ? x : c; };
+    // Tiles whose K and V a slot loads (a tile past the end loads cur again,
+    // into a buffer nobody reads, which keeps the wait counts exact).
+    auto kn_of = [&]() { return AHEAD >= 2 ? or_cur(n2, cur) : or_cur(n1, cur); };
+    auto vn_of = [&]() { return AHEAD >= 2 ? or_cur(n1, cur) : cur; };
+    auto shift = [&](TileRef& prev) {
+      prev = cur;
+      cur = n1;
+      if constexpr (AHEAD >= 2) {
+        n1 = n2;
+        n2 = t_gen;
+      } else {
+        n1 = t_gen;
+      }
+    };
+    // Prologue: K of the first AHEAD tiles and V of the first AHEAD - 1.
+    {
+      const KSet k0 = k_set(cur);
+      static_for<KU + 1>([&](auto uc) { k_load(k0, 0, 0, uc); });
+      if constexpr (AHEAD >= 2) {
+        const KSet k1 = k_set(or_cur(n1, cur));
+        static_for<KU + 1>([&](auto uc) { k_load(k1, 1, 1, uc); });
+        const i32x4 r0 = tile_src(cur, a.v);
+        static_for<VU>([&](auto uc) { v_load(r0, 0, uc); });
+      }
+      wait_loads(extra_load);
+      barrier();
+    }
+    slot(true, T_{}, F_{}, cur, cur, kn_of(), vn_of(), 0);
+    TileRef prev;
+    shift(prev);
+    int T = 1;
+    // Full tiles come first, so a slot whose tile is full has a full
+    // previous tile too.
+    while (valid(cur)) {
+      slot(!cur.full, T_{}, T_{}, cur, prev, kn_of(), vn_of(), T);
+      shift(prev);
+      ++T;
+    }
+    // Drain: the last tile's second half and its P.V.
+    slot(true, F_{}, T_{}, prev, prev, prev, prev, T);
   }
-  while (valid(cur)) {
-    int nphase = 1;
-    const TileRef nxt = next_tile(cur, nphase);
-    if (valid(nxt)) load_tile(nxt);
-    tile(std::false_type{}, cur);
-    cur = nxt;
-  }
+  // No tile load may still be writing this workgroup's LDS when it exits.
+  __builtin_amdgcn_s_waitcnt(0xF70);
 
   // Normalize; the sink logit joins the denominator.
   const float l_tot = pair_sum(l_run);
@@ -840,6 +1007,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, Plan pl)
   }
 }
 
+
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
@@ -860,7 +1028,7 @@ size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim) {
 template <int D, int GW>
 static void launch_main(const PrefillArgs& a, const Plan& pl, hipStream_t stream) {
   const int n_groups = a.kv_heads * pl.head_groups;
-  const dim3 grid(pl.n_qt * n_groups), block(256);
+  const dim3 grid(pl.n_qt * n_groups), block(64 * kPrefillWaves);
   if (a.src == kSrcContiguous) prefill_kernel<D, GW, kSrcContiguous><<<grid, block, 0, stream>>>(a, pl);
   else if (a.src == kSrcPaged) prefill_kernel<D, GW, kSrcPaged><<<grid, block, 0, stream>>>(a, pl);
   else prefill_kernel<D, GW, kSrcPacked><<<grid, block, 0, stream>>>(a, pl);
@@ -871,7 +1039,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   Plan pl;
   pl.gw = group_width(G);
   pl.head_groups = G / pl.gw;
-  pl.tq = 32 * (4 / pl.gw);
+  pl.tq = 32 * (kPrefillWaves / pl.gw);
   // Cache keys need no key-tile summaries or masks.
   pl.n_kt = a.src == kSrcPacked ? (a.p + kBK - 1) / kBK : 0;
   pl.n_qt = (a.p + pl.tq - 1) / pl.tq;
