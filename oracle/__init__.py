@@ -65,6 +65,9 @@ def load(path=None):
     lib.orc_prefill_paged.argtypes = [c_int, c_int, c_int, c_int, _D, _I, _I, _D, _D, c_int, c_int,
                                       _I, c_int, c_int, c_dbl, c_int, _D, _D]
     lib.orc_linear.argtypes = [c_int, c_int, c_int, _D, _D, _D, c_int, _D]
+    lib.orc_packed_lse.argtypes = [c_int, c_int, c_int, c_int, _D, _D, _I, _I, c_dbl, c_int, _D]
+    lib.orc_packed_backward.argtypes = [c_int, c_int, c_int, c_int, _D, _D, _D, _D, _I, _I, c_dbl,
+                                        c_int, _D, _D, _D]
     lib.orc_num_threads.restype = c_int
     lib.orc_mutation.restype = c_int
     _LIBS[path] = lib
@@ -191,6 +194,31 @@ class Oracle:
                             _pi(_i32(segments)), scale, int(window), _pd(_f64(sinks)),
                             int(nq), _pi(sel), _pd(out))
         return out
+
+    def packed_lse(self, q, k, positions, segments, scale=None, window=0):
+        """Natural-log softmax denominators of packed(): [P, Heads] (-inf: no key)."""
+        q, k = _f64(q), _f64(k)
+        p, h, d = q.shape
+        kvh = k.shape[1]
+        scale = self.default_scale(d) if scale is None else float(scale)
+        lse = np.zeros((p, h), dtype=np.float64)
+        self.lib.orc_packed_lse(p, h, kvh, d, _pd(q), _pd(k), _pi(_i32(positions)),
+                                _pi(_i32(segments)), scale, int(window), _pd(lse))
+        return lse
+
+    def packed_backward(self, q, k, v, dout, positions, segments, scale=None, window=0):
+        """Gradients of sum(dout * packed(q, k, v)) -> (dq, dk, dv), shapes of q, k, v."""
+        q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+        p, h, d = q.shape
+        kvh = k.shape[1]
+        scale = self.default_scale(d) if scale is None else float(scale)
+        dq = np.zeros_like(q)
+        dk = np.zeros_like(k)
+        dv = np.zeros_like(v)
+        self.lib.orc_packed_backward(p, h, kvh, d, _pd(q), _pd(k), _pd(v), _pd(g),
+                                     _pi(_i32(positions)), _pi(_i32(segments)), scale,
+                                     int(window), _pd(dq), _pd(dk), _pd(dv))
+        return dq, dk, dv
 
     def decode_rows(self, q, cache_k, cache_v, positions, scale=None, window=0, sinks=None):
         """q [B, Heads, D], caches [B, KvHeads, MaxSeq, D] -> [B, Heads, D]."""

@@ -591,6 +591,127 @@ void orc_linear(int n, int in, int out_f, const double* x, const double* w, cons
   }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Log-sum-exp of `packed<P>` [L, N1]: per query token i and head h, the     */
+/* natural log of sum_j exp(scale * <q_i, k_j>) over the keys own[i, j]      */
+/* keeps (the softmax denominator at reference 0); -inf for an empty set.    */
+/* A training step's backward pass reads it instead of recomputing it.      */
+/* lse: [P, Heads].                                                          */
+/* ------------------------------------------------------------------------ */
+void orc_packed_lse(int P, int heads, int kv_heads, int D, const double* q, const double* k,
+                    const int32_t* positions, const int32_t* segments, double scale, int window,
+                    double* lse) {
+#pragma omp parallel for schedule(dynamic, 4)
+  for (long idx = 0; idx < (long)P * heads; ++idx) {
+    const int h = (int)(idx % heads);
+    const int i = (int)(idx / heads);
+    const int kh = kv_head_of(h, heads, kv_heads);
+    double m = -INFINITY;
+    for (int pass = 0; pass < 2; ++pass) {
+      double z = 0.0;
+      for (int j = 0; j < P; ++j) {
+        if (!(segments[i] == segments[j] && positions[j] <= positions[i]) ||
+            !in_window(positions[i], positions[j], window))
+          continue;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += q[((size_t)i * heads + h) * D + d] * k[((size_t)j * kv_heads + kh) * D + d];
+        const double sj = scale * dot;
+        if (pass == 0) {
+          if (sj > m) m = sj;
+        } else {
+          z += exp(sj - m);
+        }
+      }
+      if (pass == 1) lse[idx] = m == -INFINITY ? -INFINITY : m + log(z);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward of `packed<P>` (no sinks): the gradients of                     */
+/* L = sum_{i,h,d} dout[i,h,d] * out[i,h,d] with respect to q, k and v,     */
+/* where out[i,h] = sum_j p_ij v_j, p_ij = exp(s_ij - lse_ih),              */
+/* s_ij = scale <q_ih, k_j> over the keys own[i, j] keeps. The chain rule    */
+/* through the softmax gives, with dp_ij = <dout_ih, v_j> and               */
+/* delta_ih = sum_j p_ij dp_ij:                                             */
+/*   dv_j += p_ij dout_ih,  ds_ij = p_ij (dp_ij - delta_ih),                */
+/*   dq_ih += scale sum_j ds_ij k_j,  dk_j += scale ds_ij q_ih;              */
+/* a KV head's dk, dv sum over the query heads that read it (the repeat of  */
+/* grouped-query attention). One thread per KV head, so the sums never race. */
+/* q, dout, dq: [P, Heads, D]; k, v, dk, dv: [P, KvHeads, D].               */
+/* ------------------------------------------------------------------------ */
+void orc_packed_backward(int P, int heads, int kv_heads, int D, const double* q, const double* k,
+                         const double* v, const double* dout, const int32_t* positions,
+                         const int32_t* segments, double scale, int window, double* dq,
+                         double* dk, double* dv) {
+  for (long x = 0; x < (long)P * heads * D; ++x) dq[x] = 0.0;
+  for (long x = 0; x < (long)P * kv_heads * D; ++x) {
+    dk[x] = 0.0;
+    dv[x] = 0.0;
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int kh = 0; kh < kv_heads; ++kh) {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(P > 0 ? P : 1));
+    double* dp = (double*)malloc(sizeof(double) * (size_t)(P > 0 ? P : 1));
+    int* js = (int*)malloc(sizeof(int) * (size_t)(P > 0 ? P : 1));
+    for (int h = 0; h < heads; ++h) {
+      if (kv_head_of(h, heads, kv_heads) != kh) continue;
+      for (int i = 0; i < P; ++i) {
+        const double* qi = q + ((size_t)i * heads + h) * D;
+        const double* gi = dout + ((size_t)i * heads + h) * D;
+        int nk = 0;
+        double m = -INFINITY;
+        for (int j = 0; j < P; ++j) {
+          if (!(segments[i] == segments[j] && positions[j] <= positions[i]) ||
+              !in_window(positions[i], positions[j], window))
+            continue;
+          double dot = 0.0;
+          for (int d = 0; d < D; ++d) dot += qi[d] * k[((size_t)j * kv_heads + kh) * D + d];
+          js[nk] = j;
+          s[nk] = scale * dot;
+          if (s[nk] > m) m = s[nk];
+          ++nk;
+        }
+        if (nk == 0) continue;
+        double z = 0.0;
+        for (int t = 0; t < nk; ++t) {
+          s[t] = exp(s[t] - m);
+          z += s[t];
+        }
+        double delta = 0.0;
+        for (int t = 0; t < nk; ++t) {
+          s[t] /= z; /* p_ij */
+          const double* vj = v + ((size_t)js[t] * kv_heads + kh) * D;
+          double g = 0.0;
+          for (int d = 0; d < D; ++d) g += gi[d] * vj[d];
+          dp[t] = g;
+          delta += s[t] * g;
+        }
+        for (int t = 0; t < nk; ++t) {
+          const int j = js[t];
+#if ORC_MUTATE == 14
+          const double ds = s[t] * dp[t];
+#else
+          const double ds = s[t] * (dp[t] - delta);
+#endif
+          double* dkj = dk + ((size_t)j * kv_heads + kh) * D;
+          double* dvj = dv + ((size_t)j * kv_heads + kh) * D;
+          const double* kj = k + ((size_t)j * kv_heads + kh) * D;
+          double* dqi = dq + ((size_t)i * heads + h) * D;
+          for (int d = 0; d < D; ++d) {
+            dvj[d] += s[t] * gi[d];
+            dkj[d] += scale * ds * qi[d];
+            dqi[d] += scale * ds * kj[d];
+          }
+        }
+      }
+    }
+    free(s);
+    free(dp);
+    free(js);
+  }
+}
+
 /* Threads OpenMP will use for the calls above. */
 int orc_num_threads(void) {
 #ifdef _OPENMP

@@ -598,6 +598,89 @@ def pin_linear(o):
     assert np.array_equal(o.linear(x, sel, None, "bf16"), x[:, [5, 0, fin - 1]])
 
 
+def _torch_packed(q, k, v, positions, segments, scale, window):
+    """The packed attention through torch (float64): a key mask built from
+    own[i, j] and the window, F.scaled_dot_product_attention per head."""
+    qt, kt, vt = (torch.from_numpy(x) for x in (q, k, v))
+    pos = torch.from_numpy(positions.astype(np.int64))
+    seg = torch.from_numpy(segments.astype(np.int64))
+    keep = (seg[:, None] == seg[None, :]) & (pos[None, :] <= pos[:, None])
+    if window > 0:
+        keep &= (pos[:, None] - pos[None, :]) < window
+    g = q.shape[1] // k.shape[1]
+    kx = kt.repeat_interleave(g, dim=1).permute(1, 0, 2)
+    vx = vt.repeat_interleave(g, dim=1).permute(1, 0, 2)
+    return qt, kt, vt, keep, kx, vx
+
+
+def pin_packed_lse(o):
+    rng = _rng(17)
+    lengths = [5, 1, 9, 6]
+    h, kvh, d = 4, 2, 8
+    p = sum(lengths)
+    positions = np.concatenate([np.arange(n) for n in lengths]).astype(np.int32)
+    segments = np.concatenate([np.full(n, i) for i, n in enumerate(lengths)]).astype(np.int32)
+    q = _bf16_vals(rng.standard_normal((p, h, d)))
+    k = _bf16_vals(rng.standard_normal((p, kvh, d)))
+    scale = d ** -0.5
+    for window in (0, 3):
+        lse = o.packed_lse(q, k, positions, segments, scale, window)
+        qt, kt, _, keep, kx, _ = _torch_packed(q, k, k, positions, segments, scale, window)
+        scores = scale * torch.matmul(qt.permute(1, 0, 2), kx.transpose(1, 2))
+        scores = scores.masked_fill(~keep, float("-inf"))
+        ref = torch.logsumexp(scores, dim=-1).permute(1, 0).numpy()
+        _close(lse, ref, 1e-12, f"packed lse (window {window})")
+    # a segment's first token sees only itself: lse = scale * <q, k>
+    first = 5
+    for hh in range(h):
+        kk = hh // (h // kvh)
+        assert abs(lse[first, hh] - scale * float(q[first, hh] @ k[first, kk])) < 1e-12
+
+
+def pin_packed_backward(o):
+    rng = _rng(18)
+    lengths = [6, 1, 11, 4]
+    h, kvh, d = 4, 2, 8
+    p = sum(lengths)
+    positions = np.concatenate([np.arange(n) for n in lengths]).astype(np.int32)
+    segments = np.concatenate([np.full(n, i) for i, n in enumerate(lengths)]).astype(np.int32)
+    q = rng.standard_normal((p, h, d))
+    k = rng.standard_normal((p, kvh, d))
+    v = rng.standard_normal((p, kvh, d))
+    g = rng.standard_normal((p, h, d))
+    scale = d ** -0.5
+    for window in (0, 4):
+        dq, dk, dv = o.packed_backward(q, k, v, g, positions, segments, scale, window)
+        # torch autograd through scaled_dot_product_attention (float64)
+        qt, kt, vt, keep, _, _ = _torch_packed(q, k, v, positions, segments, scale, window)
+        qt.requires_grad_(True)
+        kt.requires_grad_(True)
+        vt.requires_grad_(True)
+        grp = h // kvh
+        kx = kt.repeat_interleave(grp, dim=1).permute(1, 0, 2)
+        vx = vt.repeat_interleave(grp, dim=1).permute(1, 0, 2)
+        out = F.scaled_dot_product_attention(qt.permute(1, 0, 2), kx, vx, attn_mask=keep, scale=scale)
+        out.permute(1, 0, 2).backward(torch.from_numpy(g))
+        _close(dq, qt.grad.numpy(), 1e-11, f"dq (window {window})")
+        _close(dk, kt.grad.numpy(), 1e-11, f"dk (window {window})")
+        _close(dv, vt.grad.numpy(), 1e-11, f"dv (window {window})")
+    # central differences of the oracle's own forward at a few entries
+    dq, dk, dv = o.packed_backward(q, k, v, g, positions, segments, scale, 0)
+    loss = lambda qq, kk, vv: float(np.sum(g * o.packed(qq, kk, vv, positions, segments, scale)))
+    eps = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(4):
+            idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = {"q": (q, k, v), "k": (q, k, v), "v": (q, k, v)}[name]
+            fp = loss(*(xp if a is x else a for a in args))
+            fm = loss(*(xm if a is x else a for a in args))
+            fd = (fp - fm) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-6 * (1 + abs(fd)), f"d{name}{idx}: {grad[idx]} vs {fd}"
+
+
 ALL_PINS = {
     "rounding": pin_rounding,
     "inv_freq": pin_inv_freq,
@@ -617,6 +700,8 @@ ALL_PINS = {
     "chunk_cached": pin_chunk_cached,
     "chunk_paged": pin_chunk_paged,
     "linear": pin_linear,
+    "packed_lse": pin_packed_lse,
+    "packed_backward": pin_packed_backward,
 }
 
 

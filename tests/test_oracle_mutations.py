@@ -29,6 +29,7 @@ MUTATIONS = {
     11: "chunked prefill ignores the token's cache row",
     12: "paged chunk reverses offsets inside a page",
     13: "linear reads the weight transposed",
+    14: "attention backward drops the softmax row term delta",
 }
 
 
