@@ -20,7 +20,8 @@ __all__ = [
     "gqa_rope_table", "gqa_rope_write_kv", "gqa_prefill_packed", "gqa_prefill_packed_workspace",
     "gqa_prefill_cached", "gqa_prefill_cached_workspace", "gqa_step_packed",
     "gqa_step_packed_workspace", "gqa_step_paged", "gqa_step_paged_workspace",
-    "gqa_qkv_rope_write",
+    "gqa_qkv_rope_write", "gqa_prefill_packed_lse", "gqa_prefill_packed_backward",
+    "gqa_prefill_packed_backward_workspace",
     "gqa_decode_rows", "gqa_decode_rows_workspace", "gqa_decode_paged",
     "gqa_decode_paged_workspace", "gqa_status_string", "gqa_set_dry_run", "gqa_abi_version",
     "dtype_code",
@@ -57,6 +58,13 @@ _prefill_packed = _sig("gqa_prefill_packed", ctypes.c_int,
                        [_i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                         _vp, _vp, _sz, _vp])
 _prefill_ws = _sig("gqa_prefill_packed_workspace", _sz, [_i32, _i32, _i32, _i32])
+_prefill_lse = _sig("gqa_prefill_packed_lse", ctypes.c_int,
+                    [_i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32] + [_vp] * 7 +
+                    [_vp, _sz, _vp])
+_prefill_bwd = _sig("gqa_prefill_packed_backward", ctypes.c_int,
+                    [_i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32] + [_vp] * 11 +
+                    [_vp, _sz, _vp])
+_prefill_bwd_ws = _sig("gqa_prefill_packed_backward_workspace", _sz, [_i32, _i32, _i32, _i32])
 _prefill_cached = _sig("gqa_prefill_cached", ctypes.c_int,
                        [_i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
                         _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp])
@@ -163,6 +171,28 @@ def gqa_prefill_packed(p, heads, kv_heads, head_dim, dtype, scale, window, sinks
                            _ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(segments), _ptr(out),
                            _ptr(workspace), workspace_bytes, _stream(stream)),
            "gqa_prefill_packed")
+
+
+def gqa_prefill_packed_lse(p, heads, kv_heads, head_dim, dtype, scale, window, q, k, v,
+                           positions, segments, out, lse, workspace, workspace_bytes, stream=None):
+    _check(_prefill_lse(p, heads, kv_heads, head_dim, dtype, scale, window, _ptr(q), _ptr(k),
+                        _ptr(v), _ptr(positions), _ptr(segments), _ptr(out), _ptr(lse),
+                        _ptr(workspace), workspace_bytes, _stream(stream)),
+           "gqa_prefill_packed_lse")
+
+
+def gqa_prefill_packed_backward_workspace(p, heads, kv_heads, head_dim):
+    return _prefill_bwd_ws(p, heads, kv_heads, head_dim)
+
+
+def gqa_prefill_packed_backward(p, heads, kv_heads, head_dim, dtype, scale, window, q, k, v, out,
+                                dout, lse, positions, segments, dq, dk, dv, workspace,
+                                workspace_bytes, stream=None):
+    _check(_prefill_bwd(p, heads, kv_heads, head_dim, dtype, scale, window, _ptr(q), _ptr(k),
+                        _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(positions),
+                        _ptr(segments), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                        workspace_bytes, _stream(stream)),
+           "gqa_prefill_packed_backward")
 
 
 def gqa_prefill_cached_workspace(n, heads, kv_heads, head_dim):

@@ -183,6 +183,88 @@ int gqa_prefill_packed(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_
                              !g_dry_run.load());
 }
 
+int gqa_prefill_packed_lse(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                           int32_t dtype, float scale, int32_t window, const void* q, const void* k,
+                           const void* v, const int32_t* positions, const int32_t* segments,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (lse == nullptr) return GQA_ERR_INVALID_ARG;
+  const int st = prefill_packed_impl(p, heads, kv_heads, head_dim, dtype, scale, window, nullptr, q, k,
+                                     v, positions, segments, out, workspace, workspace_bytes, stream,
+                                     false);
+  if (st != GQA_OK || p == 0 || g_dry_run.load()) return st;
+  gqa::PrefillArgs a{};
+  a.p = p;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.head_dim = head_dim;
+  a.dtype = dtype;
+  a.scale_log2 = effective_scale_log2(scale, head_dim);
+  a.window = window;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.positions = positions;
+  a.segments = segments;
+  a.out = out;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  a.src = gqa::kSrcPacked;
+  a.lse = lse;
+  return hip_status(gqa::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t gqa_prefill_packed_backward_workspace(int32_t p, int32_t heads, int32_t kv_heads,
+                                             int32_t head_dim) {
+  (void)kv_heads;
+  (void)head_dim;
+  if (p <= 0 || heads <= 0) return 0;
+  return gqa::prefill_bwd_workspace_bytes(p, heads);
+}
+
+int gqa_prefill_packed_backward(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                int32_t dtype, float scale, int32_t window, const void* q,
+                                const void* k, const void* v, const void* out, const void* dout,
+                                const float* lse, const int32_t* positions,
+                                const int32_t* segments, void* dq, void* dk, void* dv,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (p < 0 || window < 0) return GQA_ERR_INVALID_ARG;
+  const int st = check_heads(heads, kv_heads, head_dim, dtype);
+  if (st != GQA_OK) return st;
+  if (!std::isfinite(scale) || scale < 0.0f) return GQA_ERR_INVALID_ARG;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr ||
+      lse == nullptr || positions == nullptr || segments == nullptr || dq == nullptr ||
+      dk == nullptr || dv == nullptr)
+    return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  if (p == 0) return GQA_OK;
+  const size_t need = gqa::prefill_bwd_workspace_bytes(p, heads);
+  if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GQA_ERR_WORKSPACE;
+  if (g_dry_run.load()) return GQA_OK;
+  gqa::BwdArgs a{};
+  a.p = p;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.head_dim = head_dim;
+  a.scale = scale != 0.0f ? scale : (float)(1.0 / std::sqrt((double)head_dim));
+  a.window = window;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.positions = positions;
+  a.segments = segments;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  return hip_status(gqa::launch_prefill_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t gqa_prefill_cached_workspace(int32_t n, int32_t heads, int32_t kv_heads,
                                     int32_t head_dim) {
   if (n <= 0) return 0;

@@ -76,6 +76,7 @@ struct PrefillArgs {
   const int32_t* table;  // paged: [cache_rows, table_pages]
   int table_pages;
   int num_pages;
+  float* lse;            // optional [p, heads]: natural-log softmax denominators
 };
 
 // Fused projections: x [n, hidden] times the q / k / v weights ([features,
@@ -113,5 +114,28 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 
 size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Backward of the packed prefill (bf16): dq [p, heads, D], dk / dv
+// [p, kv_heads, D] from q, k, v, the forward's out and lse, and dout.
+struct BwdArgs {
+  int p, heads, kv_heads, head_dim;
+  float scale;  // softmax scale (natural)
+  int window;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;  // [p, heads], natural log
+  const int32_t* positions;
+  const int32_t* segments;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* ws;
+  size_t ws_bytes;
+};
+size_t prefill_bwd_workspace_bytes(int p, int heads);
+hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace gqa

@@ -36,62 +36,12 @@
 #include <type_traits>
 #include <utility>
 
+#include "attn_tiles.h"
 #include "common.h"
 #include "internal.h"
 
 namespace gqa {
 
-namespace {
-constexpr int kBK = 64;       // keys per tile
-constexpr int kPrepThreads = 1024;
-constexpr float kNegInf = -__builtin_huge_valf();
-
-struct TileSum {
-  int seg_min, seg_max, pos_min, pos_max;
-};
-
-struct Plan {
-  TileSum* ksum;   // [n_kt]
-  TileSum* qsum;   // [n_qt]
-  int2* qrange;    // [n_qt] first / last key tile to visit
-  int* order;      // [n_qt] query tiles, costliest first
-  int* cost;       // [n_qt] key tiles each query tile visits
-  uint32_t* masks; // [n_qt][n_kg][4]: per group of 64 key tiles, a 64-bit
-                   // "visit" mask then a 64-bit "every pair allowed" mask
-  int n_kt, n_qt, n_kg, tq, head_groups, gw;
-  int max_cost;    // costs are clamped to [0, max_cost] for the ordering
-};
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Read-only views through the constant address space: the prep kernels wrote
-// these arrays before this kernel started and nothing writes them during it,
-// so workgroup-uniform reads may use scalar loads (they then stay out of the
-// vector-memory wait counter that tracks the K/V tile loads).
-typedef __attribute__((address_space(4))) const int ConstInt;
-__device__ __forceinline__ int ld_const(const int* p, long long i) { return ((ConstInt*)p)[i]; }
-__device__ __forceinline__ TileSum ld_const(const TileSum* p, int i) {
-  const int* b = reinterpret_cast<const int*>(p + i);
-  return TileSum{ld_const(b, 0), ld_const(b, 1), ld_const(b, 2), ld_const(b, 3)};
-}
-
-__device__ __forceinline__ bool tiles_meet(const TileSum& q, const TileSum& k, int window) {
-  if (k.seg_max < q.seg_min || k.seg_min > q.seg_max) return false;
-  if (k.pos_min > q.pos_max) return false;
-  if (window > 0 && (long long)q.pos_min - (long long)k.pos_max >= window) return false;
-  return true;
-}
-
-// Every (query, key) pair of the two tiles is allowed: one segment on both
-// sides, every key position at or below every query position, all inside the
-// window, and key tile kt holds 64 real keys.
-__device__ __forceinline__ bool tiles_full(const TileSum& q, const TileSum& k, int kt, int p, int window) {
-  return (kt + 1) * kBK <= p && q.seg_min == q.seg_max && k.seg_min == k.seg_max &&
-         k.seg_min == q.seg_min && k.pos_max <= q.pos_min &&
-         (window <= 0 || (long long)q.pos_max - (long long)k.pos_min < window);
-}
-
-}  // namespace
 
 // ---------------------------------------------------------------------------
 // Prep 1: per-tile [min, max] of segments and positions. One wavefront per
@@ -251,34 +201,6 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_order_kernel(Plan pl) {
 //          on distinct banks.
 //   positions, segments: 64 x 4 bytes each per tile (packed keys).
 // ---------------------------------------------------------------------------
-// Lanes l and l ^ 32 own the two key halves of one query column; these
-// combine their values (one cross-half lane swap, no LDS round trip).
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Calls f(std::integral_constant<int, i>) for i = 0 .. N - 1, unrolled at
-// compile time (every index below selects registers, so none may be a
-// runtime value).
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// Key row feeding accumulator row m of a 32-key block: bits 2 and 3 swapped.
-__device__ __forceinline__ int kappa(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
 template <int D, int NKB, int NPB>
 struct Lds {
   static constexpr int kStride = 2 * D + 16;     // K row stride (bytes)
@@ -295,45 +217,6 @@ struct Lds {
 template <int D>
 __device__ __forceinline__ int vswz(int r) {
   return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
-}
-
-typedef __attribute__((address_space(3))) char LdsByte;
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-template <typename T>
-__device__ __forceinline__ T lds_ld(const LdsByte* p) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
-}
-template <typename T>
-__device__ __forceinline__ void lds_st(LdsByte* p, const T& v) {
-  *reinterpret_cast<__attribute__((address_space(3))) T*>(p) = v;
-}
-
-// Raw buffer descriptor (base, num_records bytes, untyped 32-bit access) as
-// four scalar registers, for the asm loads below.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 raw_rsrc(const void* base, int num_records) {
-  const unsigned long long p = reinterpret_cast<unsigned long long>(base);
-  i32x4 r;
-  r[0] = (int)(uint32_t)p;
-  r[1] = (int)((p >> 32) & 0xffff);
-  r[2] = num_records;
-  r[3] = 0x00020000;
-  return r;
-}
-// Direct buffer-to-LDS load: BYTES (4 or 16) per lane from base + voffset,
-// written at LDS byte address lds + BYTES * lane (zeros for lanes out of
-// range). Issued as asm so that the compiler's wait-counter bookkeeping
-// leaves these loads alone: the kernel waits for them explicitly, a tile or
-// two after issue, and an automatic wait before each LDS read would drain
-// them at once.
-template <int BYTES>
-__device__ __forceinline__ void lds_dma(i32x4 rsrc, uint32_t lds, int voffset) {
-  if constexpr (BYTES == 16)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds), "v"(voffset), "s"(rsrc) : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"(lds), "v"(voffset), "s"(rsrc) : "memory", "m0");
 }
 
 // Wavefronts per workgroup, and how many key tiles ahead of the matrix work
@@ -993,6 +876,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     den = l_tot * f + fast_exp2(s2 - M);
   }
   const float inv = den > 0.f ? f / den : 0.f;
+  if (a.lse != nullptr && q_valid && hf == 0) {
+    // Natural-log softmax denominator at reference 0 (no sink).
+    constexpr float kLn2 = 0.6931471805599453f;
+    a.lse[(long long)q_tok * a.heads + h] = l_tot > 0.f ? (m_use + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
+  }
   if (q_valid) {
     uint16_t* og = static_cast<uint16_t*>(a.out) + ((long long)q_tok * a.heads + h) * D;
 #pragma unroll
@@ -1013,16 +901,20 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
 // ---------------------------------------------------------------------------
 static int group_width(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
 
-size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim) {
-  (void)heads;
-  (void)kv_heads;
-  (void)head_dim;
+size_t prefill_plan_bytes(int p) {
   const size_t n_kt = (size_t)(p + kBK - 1) / kBK;
   const size_t n_qt = (size_t)(p + 31) / 32;  // the smallest query tile
   const size_t n_kg = (n_kt + 63) / 64;
   return align256(n_kt * sizeof(TileSum)) + align256(n_qt * sizeof(TileSum)) +
          align256(n_qt * sizeof(int2)) + 2 * align256(n_qt * sizeof(int)) +
          align256(n_qt * n_kg * 4 * sizeof(uint32_t));
+}
+
+size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim) {
+  (void)heads;
+  (void)kv_heads;
+  (void)head_dim;
+  return prefill_plan_bytes(p);
 }
 
 template <int D, int GW>
@@ -1034,9 +926,8 @@ static void launch_main(const PrefillArgs& a, const Plan& pl, hipStream_t stream
   else prefill_kernel<D, GW, kSrcPacked><<<grid, block, 0, stream>>>(a, pl);
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream) {
   const int G = a.heads / a.kv_heads;
-  Plan pl;
   pl.gw = group_width(G);
   pl.head_groups = G / pl.gw;
   pl.tq = 32 * (kPrefillWaves / pl.gw);
@@ -1065,7 +956,18 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   prefill_order_kernel<<<1, kPrepThreads, 0, stream>>>(pl);
-  e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t prefill_summarize(const PrefillArgs& a, const Plan& pl, hipStream_t stream) {
+  const int n_tiles = pl.n_kt + pl.n_qt;
+  prefill_summarize_kernel<<<dim3((n_tiles + 3) / 4), dim3(256), 0, stream>>>(a, pl);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  Plan pl;
+  const hipError_t e = prefill_prepare(a, pl, stream);
   if (e != hipSuccess) return e;
   if (a.head_dim == 64) {
     if (pl.gw == 4) launch_main<64, 4>(a, pl, stream);

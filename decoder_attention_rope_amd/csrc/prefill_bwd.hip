@@ -1,0 +1,561 @@
+// Backward of the packed prefill attention on bf16 matrix cores (gfx950).
+//
+// `packed<P>` of the Linnet "examples/01-llama" page (src/attention.linnet)
+// is trained through the model's `loss_packed` entry (the same page's model
+// source): token i attends key j iff segments[i] == segments[j] &&
+// positions[j] <= positions[i] (and the window). The gradients of
+// sum(dout * out) follow from the chain rule through the softmax: with
+// p_ij = exp(s_ij - lse_i), s_ij = scale <q_i, k_j>, dp_ij = <dout_i, v_j>
+// and delta_i = <dout_i, out_i> (= sum_j p_ij dp_ij):
+//   dv_j = sum_i p_ij dout_i,   ds_ij = p_ij (dp_ij - delta_i),
+//   dq_i = scale sum_j ds_ij k_j,   dk_j = scale sum_i ds_ij q_i,
+// a KV head's dk, dv summed over the query heads that read it.
+//
+// Design: the forward stores lse (natural-log softmax denominators), so the
+// backward never renormalizes. Three kernels after the forward's prepared
+// walk:
+// * delta: one pass over out and dout.
+// * dQ, one workgroup per query tile and group of query heads, as the
+//   forward: for each visited key tile, S^T = K Q^T and dP^T = V dO^T on the
+//   32x32x16 bf16 MFMA (K and V rows the A operands, q and dout in
+//   registers), P and dS in the accumulator layout (a lane owns one query),
+//   then dQ^T += K^T dS^T with K^T read from the same LDS tile by transposing
+//   8-byte reads (the key order inside a 32-key block is permuted as in the
+//   forward, so dS packs straight into the B operand).
+// * dK / dV, one workgroup per key tile and KV head: each wavefront owns 32
+//   keys (K^T and V^T as B operands in registers) and every other (query
+//   tile, head) pair; S = Q K^T and dP = dO V^T put a lane on one key, then
+//   dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed from
+//   LDS. The two wavefronts of a key half add their sums at the end.
+// Query, dout, K and V tiles go from memory straight into LDS (row r of a
+// 32-row block holding entity kappa(r), rows padded to 2 D + 16 bytes), one
+// tile ahead of the matrix work.
+#include "attn_tiles.h"
+#include "common.h"
+#include "internal.h"
+
+namespace gqa {
+
+namespace {
+constexpr float kLog2eB = 1.4426950408889634f;
+
+// LDS tile of rows of D bf16 values, padded to 2 D + 16 bytes: a K or V tile
+// of 64 keys, or a Q / dout tile of 32 queries.
+template <int D>
+struct BT {
+  static constexpr int kStride = 2 * D + 16;
+  static constexpr int kChunks = D / 8 + 1;  // 16-byte chunks per padded row
+  // 1-KiB direct loads covering `rows` padded rows (the last one may spill
+  // zeros up to the next KiB).
+  static constexpr int loads(int rows) { return (rows * kChunks + 63) / 64; }
+  static constexpr int bytes(int rows) { return 1024 * loads(rows); }
+};
+
+// Lane offset (bytes from the tile's first row) of slot p of a padded tile
+// whose row r holds row kappa(r) of a [*, row_bytes] tensor; pad slots and
+// tensor rows at or past `rows` fetch out of range.
+template <int D>
+__device__ __forceinline__ int padded_off(int p, int rows, int row_bytes) {
+  constexpr int kc = BT<D>::kChunks;
+  const int row = p / kc, ch = p - row * kc;
+  const int src = kappa(row);
+  return (ch == D / 8 || src >= rows) ? 0x40000000 : src * row_bytes + ch * 16;
+}
+
+// Workgroup barrier that neither waits for loads in flight nor lets the
+// compiler move memory accesses across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0xF70); }
+
+// A^T operand (32 dimension rows x 16 entity columns) of a transposed product
+// from a padded tile: two transposing reads of 4 entities each. Lane l of
+// group g = l / 16 supplies the address of entity 8 (g / 2) + (l % 16) / 4
+// (+4) of the 16-entity step, dimensions 32 md + 16 (g % 2) + 4 (l % 4); the
+// step's entities 16 kk .. 16 kk + 15 of a 32-row block sit in rows
+// kappa(...), which keeps every group of 4 in 4 consecutive rows.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const LdsByte* tile, int lane_off, int kk, int md) {
+  constexpr int ks = BT<D>::kStride;
+  const LdsByte* p = tile + lane_off + 16 * kk * ks + 64 * md;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)p);
+  const bf16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p + 8 * ks));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <int D>
+__device__ __forceinline__ int tr_lane_off(int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  return (4 * (g >> 1) + (s >> 2)) * BT<D>::kStride + (16 * (g & 1) + 4 * (s & 3)) * 2;
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// delta[i, h] = <dout[i, h, :], out[i, h, :]> in f32; D / 8 lanes per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, float* delta) {
+  const int cpr = a.head_dim / 8;  // 16-byte chunks per row (8 or 16)
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long total = (long long)a.p * a.heads * cpr;
+  float acc = 0.f;
+  if (idx < total) {
+    const u32x4 o = load16(static_cast<const uint16_t*>(a.out) + idx * 8);
+    const u32x4 g = load16(static_cast<const uint16_t*>(a.dout) + idx * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = __builtin_fmaf(bf16_to_f32((uint16_t)(o[w] & 0xffff)), bf16_to_f32((uint16_t)(g[w] & 0xffff)), acc);
+      acc = __builtin_fmaf(bf16_to_f32((uint16_t)(o[w] >> 16)), bf16_to_f32((uint16_t)(g[w] >> 16)), acc);
+    }
+  }
+  for (int off = 1; off < cpr; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  if (idx < total && (threadIdx.x & (cpr - 1)) == 0) delta[idx / cpr] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Per key tile, the first and last 32-token query tile that can meet it.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_krange_kernel(BwdArgs a, Plan qp, const TileSum* ksum,
+                                                         int2* krange, int n_kt) {
+  const int kt = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (kt >= n_kt) return;
+  const TileSum k = ksum[kt];
+  int first = qp.n_qt, last = -1;
+  for (int qt = lane; qt < qp.n_qt; qt += 64) {
+    if (tiles_meet(qp.qsum[qt], k, a.window)) {
+      first = min(first, qt);
+      last = max(last, qt);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    first = min(first, __shfl_xor(first, off, 64));
+    last = max(last, __shfl_xor(last, off, 64));
+  }
+  if (lane == 0) krange[kt] = make_int2(first, last);
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per query tile and group of query heads (the forward's
+// prepared walk and workgroup shape).
+// ---------------------------------------------------------------------------
+template <int D, int GW>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, const float* delta) {
+  constexpr int SUB = 4 / GW, TQ = 32 * SUB, KS = D / 16, MD = D / 32;
+  using B = BT<D>;
+  constexpr int kTile = B::bytes(kBK);
+  constexpr int kOffV = 2 * kTile, kOffP = 4 * kTile;
+  __shared__ __attribute__((aligned(16))) char smem_raw[4 * kTile + 2 * 512];
+  LdsByte* smem = (LdsByte*)smem_raw;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+  const int G = a.heads / a.kv_heads;
+  const int n_groups = a.kv_heads * pl.head_groups;
+  const int wi = blockIdx.x / n_groups, grp = blockIdx.x % n_groups;
+  const int kh = grp / pl.head_groups, hg = grp % pl.head_groups;
+  const int qt = __builtin_amdgcn_readfirstlane(ld_const(pl.order, wi));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = kh * G + hg * GW + wave % GW;
+  const int qn = lane & 31, hf = lane >> 5;
+  const int P = a.p;
+  const int q_tok = qt * TQ + (wave / GW) * 32 + qn;
+  const bool q_valid = q_tok < P;
+  const int q_ld = q_valid ? q_tok : P - 1;
+  const int my_pos = a.positions[q_ld], my_seg = a.segments[q_ld];
+  const uint32_t wlim = a.window > 0 ? (uint32_t)a.window : 0x80000000u;
+  const float scale_log2 = a.scale * kLog2eB;
+  const float lse2 = a.lse[(long long)q_ld * a.heads + h] * kLog2eB;
+  const float dlt = delta[(long long)q_ld * a.heads + h];
+
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + ((long long)q_ld * a.heads + h) * D;
+  const uint16_t* gg = static_cast<const uint16_t*>(a.dout) + ((long long)q_ld * a.heads + h) * D;
+  u32x4 qf[KS], gf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = load16(qg + ks * 16 + hf * 8);
+    gf[ks] = load16(gg + ks * 16 + hf * 8);
+  }
+  f32x16 dq[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[md][r] = 0.f;
+
+  const int row_bytes = a.kv_heads * D * 2;
+  const int k_rd = qn * B::kStride + hf * 16;
+  const int t_off = tr_lane_off<D>(lane);
+  // Tile loads of key tile kt into buffer b: K and V (B::loads(64) each) and
+  // the positions / segments, spread over the 4 wavefronts.
+  auto load_tile = [&](int kt, int b) {
+    const int n_rows = min(kBK, P - kt * kBK);
+    const long long e0 = (long long)kt * kBK * a.kv_heads * D + (long long)kh * D;
+    const int nrec = (n_rows - 1) * row_bytes + 2 * D;
+    const i32x4 rk = raw_rsrc(static_cast<const uint16_t*>(a.k) + e0, nrec);
+    const i32x4 rv = raw_rsrc(static_cast<const uint16_t*>(a.v) + e0, nrec);
+    for (int i = wave; i < B::loads(kBK); i += 4) {
+      const int off = padded_off<D>(64 * i + lane, kBK, row_bytes);
+      lds_dma<16>(rk, lds0 + b * kTile + 1024 * i, off);
+      lds_dma<16>(rv, lds0 + kOffV + b * kTile + 1024 * i, off);
+    }
+    if (wave == 3) {
+      lds_dma<4>(raw_rsrc(a.positions + (long long)kt * kBK, 4 * n_rows), lds0 + kOffP + b * 512, lane * 4);
+      lds_dma<4>(raw_rsrc(a.segments + (long long)kt * kBK, 4 * n_rows), lds0 + kOffP + b * 512 + 256, lane * 4);
+    }
+  };
+
+  // The visited key tiles in order (both phases of the walk), with their
+  // every-pair-allowed bit.
+  const int2 rng = make_int2(__builtin_amdgcn_readfirstlane(ld_const(reinterpret_cast<const int*>(pl.qrange), 2LL * qt)),
+                             __builtin_amdgcn_readfirstlane(ld_const(reinterpret_cast<const int*>(pl.qrange), 2LL * qt + 1)));
+  auto next_visit = [&](int kt, bool& full) {
+    while (kt <= rng.y) {
+      const int g = kt >> 6;
+      const int* w = reinterpret_cast<const int*>(pl.masks) + ((long long)qt * pl.n_kg + g) * 4;
+      const unsigned long long vis = (unsigned long long)(uint32_t)ld_const(w, 0) |
+                                     ((unsigned long long)(uint32_t)ld_const(w, 1) << 32);
+      const unsigned long long fm = (unsigned long long)(uint32_t)ld_const(w, 2) |
+                                    ((unsigned long long)(uint32_t)ld_const(w, 3) << 32);
+      const unsigned long long m = vis >> (kt & 63);
+      if (m != 0) {
+        const int r = __builtin_amdgcn_readfirstlane(kt + (int)__builtin_ctzll(m));
+        full = ((fm >> (r & 63)) & 1ull) != 0;
+        return r;
+      }
+      kt = (g + 1) << 6;
+    }
+    return rng.y + 1;
+  };
+
+  bool full = false;
+  int kt = next_visit(rng.x, full);
+  int b = 0;
+  if (kt <= rng.y) {
+    load_tile(kt, 0);
+    wait_all_loads();
+    wg_barrier();
+  }
+  while (kt <= rng.y) {
+    bool nfull = false;
+    const int nkt = next_visit(kt + 1, nfull);
+    if (nkt <= rng.y) load_tile(nkt, b ^ 1);
+    const LdsByte* kb = smem + b * kTile;
+    const LdsByte* vb = smem + kOffV + b * kTile;
+    const LdsByte* pb = smem + kOffP + b * 512;
+    const int n_j = P - kt * kBK;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ak = lds_ld<bf16x8>(kb + k_rd + hb * 32 * B::kStride + ks * 32);
+        const bf16x8 av = lds_ld<bf16x8>(vb + k_rd + hb * 32 * B::kStride + ks * 32);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, __builtin_bit_cast(bf16x8, qf[ks]), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, gf[ks]), dp, 0, 0, 0);
+      }
+      // Register r of this lane holds key j = 32 hb + 16 (r / 8) + 8 hf + r % 8.
+      u32x4 dsw[2];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float ds2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int j = 32 * hb + 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
+          bool ok = true;
+          if (!full) {
+            const int kp = lds_ld<int>(pb + j * 4), ksg = lds_ld<int>(pb + 256 + j * 4);
+            ok = (ksg == my_seg) & ((uint32_t)my_pos - (uint32_t)kp < wlim) & (j < n_j);
+          }
+          const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -lse2)) : 0.f;
+          ds2[e] = p * (dp[r + e] - dlt);
+        }
+        dsw[r >> 3][(r & 7) >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          const bf16x8 at = tr_operand<D>(kb + hb * 32 * B::kStride, t_off, kk, md);
+          dq[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, __builtin_bit_cast(bf16x8, dsw[kk]), dq[md], 0, 0, 0);
+        }
+    }
+    wait_all_loads();
+    wg_barrier();
+    kt = nkt;
+    full = nfull;
+    b ^= 1;
+  }
+  wait_all_loads();
+
+  if (q_valid) {
+    uint16_t* og = static_cast<uint16_t*>(a.dq) + ((long long)q_tok * a.heads + h) * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16x2(dq[md][4 * g] * a.scale, dq[md][4 * g + 1] * a.scale);
+        w[1] = pack_bf16x2(dq[md][4 * g + 2] * a.scale, dq[md][4 * g + 3] * a.scale);
+        *reinterpret_cast<u32x2*>(og + 32 * md + 8 * g + 4 * hf) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: one workgroup per key tile and KV head. Wave w owns keys
+// 32 (w & 1) .. +31 of the tile and the (query tile, head) pairs of parity
+// w >> 1; pairs are visited two at a time, both staged in LDS.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs a, Plan qp, const TileSum* ksum,
+                                                          const int2* krange, const float* delta) {
+  constexpr int KS = D / 16, MD = D / 32;
+  using B = BT<D>;
+  constexpr int qTile = B::bytes(32);              // one Q or dout tile (32 queries)
+  // Q, dout, then lse, delta, positions, segments (256 bytes each: a 64-lane
+  // load writes its 32 values and 32 zeros).
+  constexpr int pairBytes = 2 * qTile + 4 * 256;
+  constexpr int stageBytes = 2 * pairBytes;
+  constexpr int combineBytes = 2 * 2 * MD * 16 * 64 * 4;
+  constexpr int ldsBytes = 2 * stageBytes > combineBytes ? 2 * stageBytes : combineBytes;
+  __shared__ __attribute__((aligned(16))) char smem_raw[ldsBytes];
+  LdsByte* smem = (LdsByte*)smem_raw;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+  const int kt = blockIdx.x / a.kv_heads, kh = blockIdx.x % a.kv_heads;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = wave & 1, hp = wave >> 1;
+  const int qn = lane & 31, hf = lane >> 5;
+  const int P = a.p, G = a.heads / a.kv_heads;
+  const int key = kt * kBK + 32 * kb + qn;
+  const bool k_valid = key < P;
+  const int key_ld = k_valid ? key : P - 1;
+  const int pos_k = a.positions[key_ld], seg_k = a.segments[key_ld];
+  const uint32_t wlim = a.window > 0 ? (uint32_t)a.window : 0x80000000u;
+  const float scale_log2 = a.scale * kLog2eB;
+
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + ((long long)key_ld * a.kv_heads + kh) * D;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + ((long long)key_ld * a.kv_heads + kh) * D;
+  u32x4 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = load16(kg + ks * 16 + hf * 8);
+    vf[ks] = load16(vg + ks * 16 + hf * 8);
+  }
+  f32x16 dk[MD], dv[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[md][r] = 0.f;
+      dv[md][r] = 0.f;
+    }
+
+  const int2 rng = make_int2(__builtin_amdgcn_readfirstlane(krange[kt].x), __builtin_amdgcn_readfirstlane(krange[kt].y));
+  const int n_pairs = rng.y >= rng.x ? (rng.y - rng.x + 1) * G : 0;
+  const int n_steps = (n_pairs + 1) / 2;
+  const TileSum ks_sum = ld_const(ksum, kt);
+  const int row_bytes = a.heads * D * 2;
+  const int q_rd = qn * B::kStride + hf * 16;
+  const int t_off = tr_lane_off<D>(lane);
+
+  // Stage the pair `pair` (query tile, head) into slot `slot` of buffer b:
+  // Q and dout rows, lse and delta of the head, positions and segments.
+  auto load_pair = [&](int pair, int slot, int b) {
+    const int qt = rng.x + pair / G, h = kh * G + pair % G;
+    const int n_rows = min(32, P - qt * 32);
+    const long long e0 = ((long long)qt * 32 * a.heads + h) * D;
+    const int nrec = (n_rows - 1) * row_bytes + 2 * D;
+    const i32x4 rq = raw_rsrc(static_cast<const uint16_t*>(a.q) + e0, nrec);
+    const i32x4 rg = raw_rsrc(static_cast<const uint16_t*>(a.dout) + e0, nrec);
+    const uint32_t base = lds0 + b * stageBytes + slot * pairBytes;
+    for (int i = wave; i < B::loads(32); i += 4) {
+      const int off = padded_off<D>(64 * i + lane, n_rows, row_bytes);
+      lds_dma<16>(rq, base + 1024 * i, off);
+      lds_dma<16>(rg, base + qTile + 1024 * i, off);
+    }
+    if (wave == 0 || wave == 1) {
+      // lse or delta of head h for the 32 queries (stride heads floats).
+      const float* src = wave == 0 ? a.lse : delta;
+      const i32x4 r = raw_rsrc(src + (long long)qt * 32 * a.heads + h, 4 * ((n_rows - 1) * a.heads + 1));
+      lds_dma<4>(r, base + 2 * qTile + 256 * wave, lane < 32 ? lane * a.heads * 4 : 0x40000000);
+    } else {
+      const int32_t* src = wave == 2 ? a.positions : a.segments;
+      const i32x4 r = raw_rsrc(src + (long long)qt * 32, 4 * n_rows);
+      lds_dma<4>(r, base + 2 * qTile + 256 * wave, lane < 32 ? lane * 4 : 0x40000000);
+    }
+  };
+
+  if (n_steps > 0) {
+    load_pair(0, 0, 0);
+    if (n_pairs > 1) load_pair(1, 1, 0);
+    wait_all_loads();
+    wg_barrier();
+  }
+  for (int step = 0; step < n_steps; ++step) {
+    const int b = step & 1;
+    if (step + 1 < n_steps) {
+      load_pair(2 * step + 2, 0, b ^ 1);
+      if (2 * step + 3 < n_pairs) load_pair(2 * step + 3, 1, b ^ 1);
+    }
+    const int pair = 2 * step + hp;
+    const int qt = rng.x + pair / G;
+    if (pair < n_pairs) {
+      const TileSum q_sum = ld_const(qp.qsum, qt);
+      if (tiles_meet(q_sum, ks_sum, a.window)) {
+        const bool full = tiles_full(q_sum, ks_sum, kt, P, a.window) && (qt + 1) * 32 <= P;
+        const LdsByte* pbase = smem + b * stageBytes + hp * pairBytes;
+        const LdsByte* qb = pbase;
+        const LdsByte* gb = pbase + qTile;
+        const LdsByte* misc = pbase + 2 * qTile;  // lse, delta, positions, segments
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 aq = lds_ld<bf16x8>(qb + q_rd + ks * 32);
+          const bf16x8 ag = lds_ld<bf16x8>(gb + q_rd + ks * 32);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, __builtin_bit_cast(bf16x8, kf[ks]), s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, __builtin_bit_cast(bf16x8, vf[ks]), dp, 0, 0, 0);
+        }
+        // Register r of this lane holds query iq = 16 (r / 8) + 8 hf + r % 8
+        // of the tile and this lane's key.
+        const int n_q = P - qt * 32;
+        u32x4 pp[2], pds[2];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float p2[2], d2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
+            const float l2 = lds_ld<float>(misc + iq * 4) * kLog2eB;
+            const float dl = lds_ld<float>(misc + 256 + iq * 4);
+            bool ok = k_valid;
+            if (!full) {
+              const int qp_ = lds_ld<int>(misc + 512 + iq * 4), qs = lds_ld<int>(misc + 768 + iq * 4);
+              ok = ok & (qs == seg_k) & ((uint32_t)qp_ - (uint32_t)pos_k < wlim) & (iq < n_q);
+            }
+            const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
+            p2[e] = p;
+            d2[e] = p * (dp[r + e] - dl);
+          }
+          pp[r >> 3][(r & 7) >> 1] = pack_bf16x2(p2[0], p2[1]);
+          pds[r >> 3][(r & 7) >> 1] = pack_bf16x2(d2[0], d2[1]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int md = 0; md < MD; ++md) {
+            const bf16x8 ag = tr_operand<D>(gb, t_off, kk, md);
+            dv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, __builtin_bit_cast(bf16x8, pp[kk]), dv[md], 0, 0, 0);
+            const bf16x8 aq = tr_operand<D>(qb, t_off, kk, md);
+            dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, __builtin_bit_cast(bf16x8, pds[kk]), dk[md], 0, 0, 0);
+          }
+      }
+    }
+    wait_all_loads();
+    wg_barrier();
+  }
+  wait_all_loads();
+  wg_barrier();
+
+  // The two wavefronts of a key half add their sums: the odd-pair ones put
+  // theirs in LDS, the even-pair ones read, add and write.
+  LdsByte* cb = smem + kb * (2 * MD * 16 * 64 * 4);
+  if (hp == 1) {
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        lds_st(cb + ((md * 16 + r) * 64 + lane) * 4, dk[md][r]);
+        lds_st(cb + (((MD + md) * 16 + r) * 64 + lane) * 4, dv[md][r]);
+      }
+  }
+  wg_barrier();
+  if (hp == 0 && k_valid) {
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk[md][r] += lds_ld<float>(cb + ((md * 16 + r) * 64 + lane) * 4);
+        dv[md][r] += lds_ld<float>(cb + (((MD + md) * 16 + r) * 64 + lane) * 4);
+      }
+    uint16_t* dkg = static_cast<uint16_t*>(a.dk) + ((long long)key * a.kv_heads + kh) * D;
+    uint16_t* dvg = static_cast<uint16_t*>(a.dv) + ((long long)key * a.kv_heads + kh) * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 wk, wv;
+        wk[0] = pack_bf16x2(dk[md][4 * g] * a.scale, dk[md][4 * g + 1] * a.scale);
+        wk[1] = pack_bf16x2(dk[md][4 * g + 2] * a.scale, dk[md][4 * g + 3] * a.scale);
+        wv[0] = pack_bf16x2(dv[md][4 * g], dv[md][4 * g + 1]);
+        wv[1] = pack_bf16x2(dv[md][4 * g + 2], dv[md][4 * g + 3]);
+        *reinterpret_cast<u32x2*>(dkg + 32 * md + 8 * g + 4 * hf) = wk;
+        *reinterpret_cast<u32x2*>(dvg + 32 * md + 8 * g + 4 * hf) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+size_t prefill_bwd_workspace_bytes(int p, int heads) {
+  const size_t n_kt = (size_t)(p + kBK - 1) / kBK;
+  const size_t n_q32 = (size_t)(p + 31) / 32;
+  return prefill_plan_bytes(p) + align256(n_q32 * sizeof(TileSum)) + align256(n_kt * sizeof(int2)) +
+         align256((size_t)p * heads * sizeof(float));
+}
+
+template <int D>
+static hipError_t launch_bwd_main(const BwdArgs& a, const Plan& pl, const Plan& qp, const int2* krange,
+                                  const float* delta, hipStream_t stream) {
+  const int n_groups = a.kv_heads * pl.head_groups;
+  const dim3 gq(pl.n_qt * n_groups), blk(256);
+  if (pl.gw == 4) bwd_dq_kernel<D, 4><<<gq, blk, 0, stream>>>(a, pl, delta);
+  else if (pl.gw == 2) bwd_dq_kernel<D, 2><<<gq, blk, 0, stream>>>(a, pl, delta);
+  else bwd_dq_kernel<D, 1><<<gq, blk, 0, stream>>>(a, pl, delta);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_dkdv_kernel<D><<<dim3(pl.n_kt * a.kv_heads), blk, 0, stream>>>(a, qp, pl.ksum, krange, delta);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t stream) {
+  PrefillArgs pa{};
+  pa.p = a.p;
+  pa.heads = a.heads;
+  pa.kv_heads = a.kv_heads;
+  pa.head_dim = a.head_dim;
+  pa.window = a.window;
+  pa.positions = a.positions;
+  pa.segments = a.segments;
+  pa.ws = a.ws;
+  pa.src = kSrcPacked;
+  Plan pl;
+  hipError_t e = prefill_prepare(pa, pl, stream);
+  if (e != hipSuccess) return e;
+  char* ws = static_cast<char*>(a.ws) + prefill_plan_bytes(a.p);
+  const size_t n_q32 = (size_t)(a.p + 31) / 32;
+  // Summaries of 32-token query tiles (the key-side walk's unit).
+  Plan qp = pl;
+  qp.tq = 32;
+  qp.n_qt = (int)n_q32;
+  qp.n_kt = 0;
+  qp.qsum = reinterpret_cast<TileSum*>(ws);
+  ws += align256(n_q32 * sizeof(TileSum));
+  int2* krange = reinterpret_cast<int2*>(ws);
+  ws += align256((size_t)pl.n_kt * sizeof(int2));
+  float* delta = reinterpret_cast<float*>(ws);
+  e = prefill_summarize(pa, qp, stream);
+  if (e != hipSuccess) return e;
+  bwd_krange_kernel<<<dim3((pl.n_kt + 3) / 4), dim3(256), 0, stream>>>(a, qp, pl.ksum, krange, pl.n_kt);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long chunks = (long long)a.p * a.heads * (a.head_dim / 8);
+  bwd_delta_kernel<<<dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream>>>(a, delta);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return a.head_dim == 64 ? launch_bwd_main<64>(a, pl, qp, krange, delta, stream)
+                          : launch_bwd_main<128>(a, pl, qp, krange, delta, stream);
+}
+
+}  // namespace gqa

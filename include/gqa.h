@@ -180,6 +180,48 @@ size_t gqa_prefill_packed_workspace(int32_t p, int32_t heads, int32_t kv_heads,
                                     int32_t head_dim);
 
 /*
+ * gqa_prefill_packed_lse -- gqa_prefill_packed for training: the same
+ * attention (no sinks), and also each (token, head)'s natural-log softmax
+ * denominator lse = ln sum_j exp(scale <q_i, k_j>) over the keys the `own`
+ * mask and the window keep (-inf when there are none), which the backward
+ * reads. The training entry `loss_packed` of the Linnet "examples/01-llama"
+ * page's model differentiates through this attention.
+ *   lse: [p, heads] f32 device memory (written); other arguments, the
+ *   workspace and errors as gqa_prefill_packed.
+ */
+int gqa_prefill_packed_lse(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                           int32_t dtype, float scale, int32_t window, const void* q,
+                           const void* k, const void* v, const int32_t* positions,
+                           const int32_t* segments, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * gqa_prefill_packed_backward -- gradients of sum(dout * out) for the packed
+ * attention (gqa_prefill_packed_lse, no sinks): with p_ij = exp(s_ij -
+ * lse_i), s_ij = scale <q_i, k_j> over the kept keys, dp_ij = <dout_i, v_j>
+ * and delta_i = <dout_i, out_i>:
+ *   dv_j = sum_i p_ij dout_i, ds_ij = p_ij (dp_ij - delta_i),
+ *   dq_i = scale sum_j ds_ij k_j, dk_j = scale sum_i ds_ij q_i,
+ * a KV head's dk, dv summed over the query heads that read it.
+ *   q, out, dout, dq [p, heads, D]; k, v, dk, dv [p, kv_heads, D] of T;
+ *   lse [p, heads] f32 as written by gqa_prefill_packed_lse on the same
+ *   q, k, v, positions, segments, scale and window; dq, dk, dv are written
+ *   (every entry; keys no query attends get 0). Built for T = bf16, D in
+ *   {64, 128}; bf16 matrix cores with f32 accumulation, one rounding to bf16.
+ *   workspace: at least gqa_prefill_packed_backward_workspace(...) bytes,
+ *   256-byte aligned. Errors as gqa_prefill_packed.
+ */
+int gqa_prefill_packed_backward(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                int32_t dtype, float scale, int32_t window, const void* q,
+                                const void* k, const void* v, const void* out, const void* dout,
+                                const float* lse, const int32_t* positions,
+                                const int32_t* segments, void* dq, void* dk, void* dv,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+size_t gqa_prefill_packed_backward_workspace(int32_t p, int32_t heads, int32_t kv_heads,
+                                             int32_t head_dim);
+
+/*
  * gqa_prefill_cached -- chunked prefill over a cached prefix: the attention
  * of `prefill<S>(x, pos)` with pos > 0 (contiguous cache) and of
  * `prefill_paged` (paged pool) of the GroupedQueryAttention block, llama-

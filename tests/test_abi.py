@@ -229,3 +229,37 @@ def test_workspace_sizes(g):
     assert 0 < a < b
     assert g.gqa_prefill_packed_workspace(16384, 32, 8, 128) > g.gqa_prefill_packed_workspace(
         1024, 32, 8, 128) > 0
+
+
+def test_training_entries_argument_checks(g):
+    bad_arg, unsup, ws_err = _codes(g)
+    nb_f = g.gqa_prefill_packed_workspace(100, 8, 2, 64)
+    nb_b = g.gqa_prefill_packed_backward_workspace(100, 8, 2, 64)
+    assert nb_b > nb_f > 0 and g.gqa_prefill_packed_backward_workspace(0, 8, 2, 64) == 0
+
+    def fwd(status, p=100, dtype=0, lse=8, q=8, ws=256, wsb=None, window=0):
+        _expect(g, status, g.gqa_prefill_packed_lse, p, 8, 2, 64, dtype, 0.0, window, q, 8, 8, 8,
+                8, 8, lse, ws, nb_f if wsb is None else wsb)
+
+    fwd(g.GQA_OK)
+    fwd(g.GQA_OK, p=0, ws=None, wsb=0)
+    fwd(bad_arg, lse=None)
+    fwd(bad_arg, q=None)
+    fwd(bad_arg, window=-1)
+    fwd(unsup, dtype=1)
+    fwd(ws_err, wsb=16)
+
+    def bwd(status, p=100, dtype=0, lse=8, dout=8, dk=8, heads=8, ws=256, wsb=None, scale=0.0):
+        _expect(g, status, g.gqa_prefill_packed_backward, p, heads, 2, 64, dtype, scale, 0, 8, 8, 8,
+                8, dout, lse, 8, 8, 8, dk, 8, ws, nb_b if wsb is None else wsb)
+
+    bwd(g.GQA_OK)
+    bwd(g.GQA_OK, p=0, ws=None, wsb=0)
+    bwd(bad_arg, lse=None)
+    bwd(bad_arg, dout=None)
+    bwd(bad_arg, dk=None)
+    bwd(bad_arg, heads=7)          # not a multiple of kv_heads = 2
+    bwd(bad_arg, scale=float("nan"))
+    bwd(unsup, dtype=1)
+    bwd(ws_err, wsb=16)
+    bwd(ws_err, ws=257)
