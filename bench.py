@@ -332,6 +332,39 @@ def main():
                 "workload": f"{P} tokens x hidden {hid} -> (32 + 8 + 8) x 128, rope, contiguous cache"}
     del gx, gwq, gwk, gwv, gwcat, g_q
 
+    # Training pair on the packed prefill batch: the forward with log-sum-exp,
+    # then the backward (dq, dk, dv) against a seeded dout. Algorithmic work
+    # of the backward: five products the size of one of the forward's two
+    # (S and P recomputed, dP, dV, dK, dQ -> 2.5x the forward's flops).
+    b_dout = W.device_normal((P, H, D), SEED_PREFILL, "extra", bf16)
+    b_lse = torch.empty((P, H), dtype=torch.float32, device=dev)
+    b_out = torch.empty((P, H, D), dtype=bf16, device=dev)
+    b_dq = torch.empty((P, H, D), dtype=bf16, device=dev)
+    b_dk = torch.empty((P, KVH, D), dtype=bf16, device=dev)
+    b_dv = torch.empty((P, KVH, D), dtype=bf16, device=dev)
+    b_nb = gqa.gqa_prefill_packed_backward_workspace(P, H, KVH, D)
+    b_ws = torch.empty(max(b_nb, 256), dtype=torch.uint8, device=dev)
+
+    def fwd_lse():
+        gqa.gqa_prefill_packed_lse(P, H, KVH, D, gqa.GQA_BF16, 0.0, 0, pq, pk, pv, p_pos, p_seg, b_out,
+                                   b_lse, p_ws, pws_n)
+
+    def bwd():
+        gqa.gqa_prefill_packed_backward(P, H, KVH, D, gqa.GQA_BF16, 0.0, 0, pq, pk, pv, b_out, b_dout,
+                                        b_lse, p_pos, p_seg, b_dq, b_dk, b_dv, b_ws, b_nb)
+
+    fwd_lse()
+    fl_s = timed(fwd_lse)
+    bw_s = timed(bwd)
+    pairs_b = int(np.sum(seg_len * (seg_len + 1) // 2))
+    bw_flops = int(2.5 * 4 * D * H * pairs_b)
+    bwd_roof = {"bound": "mfma", "achieved": bw_flops / bw_s / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": bw_flops / bw_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                "traffic": None, "algorithmic_flops": bw_flops, "avg_us": bw_s * 1e6,
+                "forward_with_lse_us": fl_s * 1e6,
+                "workload": f"packed prefill batch above ({P} tokens), dq + dk + dv"}
+    del b_dout, b_lse, b_out, b_dq, b_dk, b_dv, b_ws
+
     # ---------------- algorithmic work ----------------
     kv_bytes = int(np.sum(lengths)) * KVH * D * 2 * 2          # K + V of attended keys
     qo_bytes = 2 * rows * H * D * 2                              # q in, out
@@ -410,6 +443,7 @@ def main():
         "roofline": roof,
         "rooflines": {"decode_paged": dec_roof, "prefill_packed": pre_roof},
         "next_rows": {"prefill_cached_paged": chunk_roof, "step_paged": step_roof,
+                      "prefill_packed_backward": bwd_roof,
                       "qkv_rope_write": qkv_roof},
         "per_op_us": {k: v * 1e3 for k, v in per_op_ms.items()},
         "wall_s_timed": wall,
