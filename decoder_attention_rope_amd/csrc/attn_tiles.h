@@ -15,6 +15,7 @@ namespace gqa {
 
 constexpr int kBK = 64;       // keys per tile
 constexpr int kPrepThreads = 1024;
+constexpr int kMaskWords = 6;  // 32-bit words per (query tile, group of 64 key tiles)
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct TileSum {
@@ -27,8 +28,9 @@ struct Plan {
   int2* qrange;    // [n_qt] first / last key tile to visit
   int* order;      // [n_qt] query tiles, costliest first
   int* cost;       // [n_qt] key tiles each query tile visits
-  uint32_t* masks; // [n_qt][n_kg][4]: per group of 64 key tiles, a 64-bit
-                   // "visit" mask then a 64-bit "every pair allowed" mask
+  uint32_t* masks; // [n_qt][n_kg][kMaskWords]: per group of 64 key tiles,
+                   // 64-bit masks "visit", "every pair allowed" and "one
+                   // segment" (see tiles_oneseg)
   int n_kt, n_qt, n_kg, tq, head_groups, gw;
   int max_cost;    // costs are clamped to [0, max_cost] for the ordering
 };
@@ -62,12 +64,23 @@ __device__ __forceinline__ bool tiles_full(const TileSum& q, const TileSum& k, i
          (window <= 0 || (long long)q.pos_max - (long long)k.pos_min < window);
 }
 
+// Both tiles lie in one and the same segment and key tile kt holds 64 real
+// keys: a pair is then allowed iff its positions (and the window) allow it,
+// so the per-element mask may skip the segment compare.
+__device__ __forceinline__ bool tiles_oneseg(const TileSum& q, const TileSum& k, int kt, int p) {
+  return (kt + 1) * kBK <= p && q.seg_min == q.seg_max && k.seg_min == k.seg_max && k.seg_min == q.seg_min;
+}
+
+// Maximum of floats without the canonicalizing moves fmaxf needs (v_maximum3
+// on gfx950); a NaN input propagates.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 
 // Lanes l and l ^ 32 own the two key halves of one query column; these
 // combine their values (one cross-half lane swap, no LDS round trip).
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

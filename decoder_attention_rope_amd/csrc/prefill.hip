@@ -27,7 +27,8 @@
 //   S^T of one tile next to the P.V of the previous one.
 // * Tiles that cannot hold an allowed key are skipped using per-tile
 //   [min, max] summaries of segments and positions; tiles in which every pair
-//   is allowed skip the per-element mask. The exact `own` predicate is
+//   is allowed skip the per-element mask, and tiles whose keys and queries all
+//   lie in one segment test positions only. The exact `own` predicate is
 //   evaluated everywhere else, so any segment order or id is handled.
 // * Three small prep kernels compute the per-tile summaries and each query
 //   tile's visited key-tile range and cost (one wavefront per tile), then
@@ -106,11 +107,12 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(PrefillArgs a, Plan p
   int first = pl.n_kt, last = -1, cnt = 0;
   for (int g = 0; g < pl.n_kg; ++g) {
     const int kt = g * 64 + lane;
-    bool meet = false, full = false;
+    bool meet = false, full = false, one = false;
     if (kt < pl.n_kt) {
       const TileSum k = pl.ksum[kt];
       meet = tiles_meet(q, k, a.window);
       full = meet && tiles_full(q, k, kt, a.p, a.window);
+      one = meet && tiles_oneseg(q, k, kt, a.p);
     }
     if (meet) {
       first = min(first, kt);
@@ -119,9 +121,10 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(PrefillArgs a, Plan p
     }
     const unsigned long long vm = __builtin_amdgcn_ballot_w64(meet);
     const unsigned long long fm = __builtin_amdgcn_ballot_w64(full);
-    if (lane < 4) {
-      const unsigned long long w = lane < 2 ? vm : fm;
-      pl.masks[((size_t)qt * pl.n_kg + g) * 4 + lane] = (uint32_t)(w >> (32 * (lane & 1)));
+    const unsigned long long om = __builtin_amdgcn_ballot_w64(one);
+    if (lane < kMaskWords) {
+      const unsigned long long w = lane < 2 ? vm : lane < 4 ? fm : om;
+      pl.masks[((size_t)qt * pl.n_kg + g) * kMaskWords + lane] = (uint32_t)(w >> (32 * (lane & 1)));
     }
   }
 #pragma unroll
@@ -232,7 +235,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   constexpr int NW = kPrefillWaves;
   constexpr int AHEAD = kPrefillAhead;
   constexpr int NKB = AHEAD + 1;  // K (and V) buffers
-  constexpr int NPB = AHEAD + 2;  // position buffers
+  constexpr int NPB = 4;          // position buffers (AHEAD + 2 used; a power of two)
+  static_assert(AHEAD + 2 <= NPB, "position buffers");
   constexpr int SUB = NW / GW;  // query sub-tiles of 32 per workgroup
   constexpr int TQ = 32 * SUB;  // query tokens per workgroup
   constexpr int KS = D / 16;    // k-steps of QK^T over the head dim
@@ -347,8 +351,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
 
   // A key tile: tile index kt (64 keys) of cache row r, at pool page `page`;
   // full: every pair with the query tile is allowed.
+  // one: packed keys of a single segment, the query tile's (mask by
+  // positions only).
   struct TileRef {
-    int kt, r, page, rows, full;  // rows: cache slots of the tile anyone may see
+    int kt, r, page, rows, full, one;  // rows: cache slots of the tile anyone may see
   };
   // Buffer resource over one operand (K or V) of a key tile: 64 key slots of
   // one cache plane, or 64 packed tokens at KV head kh.
@@ -366,20 +372,22 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     return raw_rsrc(static_cast<const char*>(base) + 2 * e0, (n_rows - 1) * row_bytes + 2 * D);
   };
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  // Load u of a K set (tile t into K buffer kb and position buffer pb).
+  // Load u of a K set (tile t into K buffer kb and position buffer pb). The
+  // one extra load per wavefront: the last K chunk (wave 0), the key
+  // positions (wave 1) or segments (wave 2) of packed keys.
   struct KSet {
-    i32x4 rk, rp, rs;
+    i32x4 rk, rx;
   };
+  const int* x_src = wave == 1 ? a.positions : a.segments;
+  const int x_lds = wave == 1 ? 0 : kBK * 4;
   auto k_set = [&](TileRef t) {
     KSet s;
     s.rk = tile_src(t, a.k);
     if constexpr (SRC == kSrcPacked) {
       const int n_rows = min(kBK, P - t.kt * kBK);
-      s.rp = raw_rsrc(a.positions + (long long)t.kt * kBK, 4 * n_rows);
-      s.rs = raw_rsrc(a.segments + (long long)t.kt * kBK, 4 * n_rows);
+      s.rx = raw_rsrc(x_src + (long long)t.kt * kBK, 4 * n_rows);
     } else {
-      s.rp = s.rk;
-      s.rs = s.rk;
+      s.rx = s.rk;
     }
     return s;
   };
@@ -390,10 +398,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     } else {
       if (wave == 0) {
         lds_dma<16>(s.rk, lds0 + L::kOff(kb) + 1024 * (L::kChunks - 1), k_voff[KU]);
-      } else if (SRC == kSrcPacked && wave == 1) {
-        lds_dma<4>(s.rp, lds0 + L::posOff(pb), lane * 4);
-      } else if (SRC == kSrcPacked && wave == 2) {
-        lds_dma<4>(s.rs, lds0 + L::posOff(pb) + kBK * 4, lane * 4);
+      } else if (SRC == kSrcPacked && wave < 3) {
+        lds_dma<4>(s.rx, lds0 + L::posOff(pb) + x_lds, lane * 4);
       }
     }
   };
@@ -420,18 +426,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   // not depend on the order of the key tiles), so each phase runs one
   // specialized loop body.
   int vis_g = -1;
-  unsigned long long vis_m = 0, full_m = 0;
+  unsigned long long vis_m = 0, full_m = 0, one_m = 0;
   auto next_in = [&](int kt, int phase) {
     while (kt <= rng.y) {
       const int g = kt >> 6;
       if (g != vis_g) {
-        const int* w = reinterpret_cast<const int*>(pl.masks) + ((long long)qt * pl.n_kg + g) * 4;
+        const int* w = reinterpret_cast<const int*>(pl.masks) + ((long long)qt * pl.n_kg + g) * kMaskWords;
         vis_m = (unsigned long long)(uint32_t)ld_const(w, 0) | ((unsigned long long)(uint32_t)ld_const(w, 1) << 32);
         full_m = (unsigned long long)(uint32_t)ld_const(w, 2) | ((unsigned long long)(uint32_t)ld_const(w, 3) << 32);
+        one_m = (unsigned long long)(uint32_t)ld_const(w, 4) | ((unsigned long long)(uint32_t)ld_const(w, 5) << 32);
         vis_g = g;
       }
       const unsigned long long m = (phase == 0 ? full_m : (vis_m & ~full_m)) >> (kt & 63);
-      if (m != 0) return __builtin_amdgcn_readfirstlane(kt + (int)__builtin_ctzll(m));
+      if (m != 0) return __builtin_amdgcn_readfirstlane(kt + (int)__builtin_ctzll(m));  // in group vis_g
       kt = (g + 1) << 6;
     }
     return rng.y + 1;
@@ -529,7 +536,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   };
   bool c_started = false;
   auto cache_next = [&](int& phase) {
-    TileRef t{-1, 0, 0, 0};
+    TileRef t{-1, 0, 0, 0, 0, 0};
     if (!c_started) {
       c_started = true;
       c_phase = c_single ? 0 : 1;
@@ -561,7 +568,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
         page = page_of(c_row, kt);
         if (page < 0 || page >= a.num_pages) continue;
       }
-      t = TileRef{kt, c_row, page, min(kBK, c_last - kt * kBK + 1)};
+      t = TileRef{kt, c_row, page, min(kBK, c_last - kt * kBK + 1), 0, 0};
       break;
     }
     phase = c_phase;
@@ -638,16 +645,31 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   //          (slice 4 + k: pack pair k - 2 to bf16 and add it to the sums,
   //          exponentiate pair k - 1, scale pair k), so no instruction waits
   //          on one issued in the same slice.
-  auto soft_slice = [&](const LdsByte* pb, int lo_j, int hi_j, int n_j, auto hbc, auto cc, bool masked) {
+  // mode: 0 every pair allowed, 1 packed keys of the query tile's one
+  // segment (positions and the window decide), 2 the full predicate.
+  auto soft_slice = [&](const LdsByte* pb, int lo_j, int hi_j, int n_j, auto hbc, auto cc, int mode) {
     constexpr int hb = decltype(hbc)::value;
     constexpr int c = decltype(cc)::value;
     if constexpr (c < 2) {
-      if (__builtin_expect(masked, 0)) {
+      if (__builtin_expect(mode != 0, 0)) {
         // The literal own predicate (and the window) per element; rows
         // 8c .. 8c + 7 are the 8 consecutive keys jb + 8 hf + e.
         constexpr int jb = 32 * hb + 16 * c;
         if constexpr (SRC == kSrcPacked) {
           const LdsByte* pp = pb + (jb + 8 * hf) * 4;
+          if (mode == 1) {
+            // Every key and query of the two tiles is in one segment and the
+            // key tile holds 64 real keys.
+#pragma unroll
+            for (int q4 = 0; q4 < 2; ++q4) {
+              const u32x4 kp = lds_ld<u32x4>(pp + 16 * q4);
+#pragma unroll
+              for (int e4 = 0; e4 < 4; ++e4) {
+                const int e = 4 * q4 + e4;
+                s[hb][8 * c + e] = ((uint32_t)my_pos - kp[e4] < wlim) ? s[hb][8 * c + e] : kNegInf;
+              }
+            }
+          } else {
           // Keys past P (zeros in LDS) are excluded by index: e < e_end.
           const int e_end = n_j - jb - 8 * hf;
 #pragma unroll
@@ -660,6 +682,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
               s[hb][8 * c + e] = ok ? s[hb][8 * c + e] : kNegInf;
             }
           }
+          }
         } else {
           // Key slot kt * 64 + jb + 8 hf + e of the tile's row is visible
           // for e in [e_lo, e_hi].
@@ -668,11 +691,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
           for (int e = 0; e < 8; ++e) s[hb][8 * c + e] = ((e >= e_lo) & (e <= e_hi)) ? s[hb][8 * c + e] : kNegInf;
         }
       }
-      const float m0 = fmaxf(fmaxf(s[hb][8 * c], s[hb][8 * c + 1]), s[hb][8 * c + 2]);
-      const float m1 = fmaxf(fmaxf(s[hb][8 * c + 3], s[hb][8 * c + 4]), s[hb][8 * c + 5]);
-      const float m2 = fmaxf(s[hb][8 * c + 6], s[hb][8 * c + 7]);
-      const float mc = fmaxf(fmaxf(m0, m1), m2);
-      tmax = c == 0 ? mc : fmaxf(tmax, mc);
+      const float m0 = vmax3(s[hb][8 * c], s[hb][8 * c + 1], s[hb][8 * c + 2]);
+      const float m1 = vmax3(s[hb][8 * c + 3], s[hb][8 * c + 4], s[hb][8 * c + 5]);
+      const float m2 = c == 0 ? vmax(s[hb][8 * c + 6], s[hb][8 * c + 7]) : vmax3(s[hb][8 * c + 6], s[hb][8 * c + 7], tmax);
+      tmax = vmax3(m0, m1, m2);
       // Keep this slice's work in its step (the compiler would merge it
       // into the next slice, past the mask branch).
       asm volatile("" : "+v"(tmax));
@@ -687,16 +709,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
       m_use = (m_new == kNegInf) ? 0.f : m_new;
       alpha = fast_exp2(m_run - m_use);
       m_run = m_new;
-      psa = 0.f;
-      psb = 0.f;
       asm volatile("" : "+v"(m_use), "+v"(alpha), "+v"(m_run));
     } else {
       constexpr int k = c - 4;
       if constexpr (k >= 2) {
         constexpr int r = 2 * (k - 2);
         pw[2 * hb + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(ea0, ea1);
-        psa += ea0;
-        psb += ea1;
+        psa = k == 2 ? ea0 : psa + ea0;
+        psb = k == 2 ? ea1 : psb + ea1;
         // Materialize here: without the anchors the compiler sinks this work
         // past the rescale branch, next to its use, out of the MFMA shadow.
         asm volatile("" ::"v"(pw[2 * hb + (r >> 3)][(r & 7) >> 1]));
@@ -739,8 +759,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     TileRef t;
     if constexpr (SRC == kSrcPacked) {
       const int kt = advance(last_kt < 0 ? rng.x : last_kt + 1, wphase);
-      t = TileRef{kt, 0, 0, 0, 0};
-      if (kt <= rng.y) last_kt = kt;
+      t = TileRef{kt, 0, 0, 0, 0, 0};
+      if (kt <= rng.y) {
+        last_kt = kt;
+        t.one = (int)((one_m >> (kt & 63)) & 1ull);
+      }
     } else {
       t = cache_next(wphase);
     }
@@ -754,14 +777,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   // (the previous one) exists (the softmax of its second half and its P.V
   // run). Unless `masked`, every pair of both tiles is allowed (a uniform
   // branch: one loop body serves both kinds of slot).
-  TileRef t_gen{-1, 0, 0, 0, 0};
-  auto slot = [&](bool masked, auto dosc, auto doprevc, TileRef t, TileRef tp, TileRef kn, TileRef vn, int T) {
+  TileRef t_gen{-1, 0, 0, 0, 0, 0};
+  auto mode_of = [](TileRef t) { return t.full ? 0 : t.one ? 1 : 2; };
+  auto slot = [&](int mode, auto dosc, auto doprevc, TileRef t, TileRef tp, TileRef kn, TileRef vn, int T) {
     constexpr bool DO_S = decltype(dosc)::value;
     constexpr bool DO_PREV = decltype(doprevc)::value;
-    const LdsByte* kb = smem + L::kOff(T % NKB) + k_rd;
-    const LdsByte* vb = smem + L::vOff((T + NKB - 1) % NKB);
-    const LdsByte* pb_t = smem + L::posOff(T % NPB);
-    const LdsByte* pb_p = smem + L::posOff((T + NPB - 1) % NPB);
+    const unsigned Tu = T;
+    const LdsByte* kb = smem + L::kOff(Tu % NKB) + k_rd;
+    const LdsByte* vb = smem + L::vOff((Tu + NKB - 1) % NKB);
+    const LdsByte* pb_t = smem + L::posOff(Tu % NPB);
+    const LdsByte* pb_p = smem + L::posOff((Tu + NPB - 1) % NPB);
     // Cache keys: this lane's visible slots relative to each tile; packed
     // keys: the real keys of each tile.
     const int lo_t = my_lo - t.kt * kBK;
@@ -787,8 +812,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
         if constexpr (decltype(has_mfma(gn{}))::value) ring[(g + 4) & 3] = operand(kb, vb, gn{});
       }
       if constexpr (DO_S && h == 0 && i < NLOAD) {
-        if constexpr (i <= KU) k_load(ks, (T + AHEAD) % NKB, (T + AHEAD) % NPB, std::integral_constant<int, i>{});
-        else v_load(rv, (T + AHEAD - 1) % NKB, std::integral_constant<int, i - KU - 1>{});
+        if constexpr (i <= KU) k_load(ks, (Tu + AHEAD) % NKB, (Tu + AHEAD) % NPB, std::integral_constant<int, i>{});
+        else v_load(rv, (Tu + AHEAD - 1) % NKB, std::integral_constant<int, i - KU - 1>{});
       }
       if constexpr (DO_S && h == 1 && i == 0) t_gen = gen();
       // Half-slot 0 runs the softmax of tile tp's second half, half-slot 1
@@ -800,7 +825,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
           constexpr int c = decltype(cc)::value;
           if constexpr (2 + c * (HS - 2) / NSOFT == i)
             soft_slice(h == 0 ? pb_p : pb_t, h == 0 ? lo_p : lo_t, h == 0 ? hi_p : hi_t, h == 0 ? n_p : n_t,
-                       std::integral_constant<int, 1 - h>{}, cc, masked);
+                       std::integral_constant<int, 1 - h>{}, cc, mode);
         });
       }
       if constexpr (soft && i == HS - 1) rescale(alpha);
@@ -849,19 +874,20 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
       wait_loads(extra_load);
       barrier();
     }
-    slot(true, T_{}, F_{}, cur, cur, kn_of(), vn_of(), 0);
+    slot(mode_of(cur), T_{}, F_{}, cur, cur, kn_of(), vn_of(), 0);
     TileRef prev;
     shift(prev);
     int T = 1;
     // Full tiles come first, so a slot whose tile is full has a full
-    // previous tile too.
+    // previous tile too; a slot's mask mode covers both of its tiles (a
+    // mode that masks more is always correct).
     while (valid(cur)) {
-      slot(!cur.full, T_{}, T_{}, cur, prev, kn_of(), vn_of(), T);
+      slot(max(mode_of(cur), mode_of(prev)), T_{}, T_{}, cur, prev, kn_of(), vn_of(), T);
       shift(prev);
       ++T;
     }
     // Drain: the last tile's second half and its P.V.
-    slot(true, F_{}, T_{}, prev, prev, prev, prev, T);
+    slot(mode_of(prev), F_{}, T_{}, prev, prev, prev, prev, T);
   }
   // No tile load may still be writing this workgroup's LDS when it exits.
   __builtin_amdgcn_s_waitcnt(0xF70);
@@ -907,7 +933,7 @@ size_t prefill_plan_bytes(int p) {
   const size_t n_kg = (n_kt + 63) / 64;
   return align256(n_kt * sizeof(TileSum)) + align256(n_qt * sizeof(TileSum)) +
          align256(n_qt * sizeof(int2)) + 2 * align256(n_qt * sizeof(int)) +
-         align256(n_qt * n_kg * 4 * sizeof(uint32_t));
+         align256(n_qt * n_kg * kMaskWords * sizeof(uint32_t));
 }
 
 size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim) {

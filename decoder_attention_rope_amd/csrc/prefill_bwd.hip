@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
   auto next_visit = [&](int kt, bool& full) {
     while (kt <= rng.y) {
       const int g = kt >> 6;
-      const int* w = reinterpret_cast<const int*>(pl.masks) + ((long long)qt * pl.n_kg + g) * 4;
+      const int* w = reinterpret_cast<const int*>(pl.masks) + ((long long)qt * pl.n_kg + g) * kMaskWords;
       const unsigned long long vis = (unsigned long long)(uint32_t)ld_const(w, 0) |
                                      ((unsigned long long)(uint32_t)ld_const(w, 1) << 32);
       const unsigned long long fm = (unsigned long long)(uint32_t)ld_const(w, 2) |
