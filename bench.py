@@ -251,7 +251,7 @@ def main():
     c_tflops = c_flops / c_s / 1e12
     chunk_roof = {"bound": "mfma", "achieved": c_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                   "unit": "TFLOP/s", "frac": c_tflops / MFMA_BF16_PEAK_TFLOPS,
-                  "traffic": traffic_for("prefill_cached_paged", ["prefill.hip", "common.h"]),
+                  "traffic": traffic_for("prefill_cached_paged", ["prefill.hip", "attn_tiles.h", "common.h"]),
                   "algorithmic_flops": c_flops, "avg_us": c_s * 1e6,
                   "workload": f"{ec['rows']} rows, prefixes U[{ec['pre_lo']}, {ec['pre_hi']}] "
                               f"({int(c_pre.sum())} keys), chunk {ec['chunk']}, paged"}
@@ -382,7 +382,7 @@ def main():
                 "algorithmic_bytes": decode_bytes, "avg_us": dec_s * 1e6}
     pre_roof = {"bound": "mfma", "achieved": prefill_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": prefill_tflops / MFMA_BF16_PEAK_TFLOPS,
-                "traffic": traffic_for("prefill_packed", ["prefill.hip", "common.h"]),
+                "traffic": traffic_for("prefill_packed", ["prefill.hip", "attn_tiles.h", "common.h"]),
                 "algorithmic_flops": prefill_flops, "avg_us": pre_s * 1e6}
     dominant = "prefill_packed" if pre_s >= dec_s else "decode_paged"
     roof = dict(pre_roof if dominant == "prefill_packed" else dec_roof)
