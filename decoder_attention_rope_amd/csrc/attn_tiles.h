@@ -151,5 +151,9 @@ hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream);
 // Summaries of pl's query tiles (pl.tq tokens) and, if pl.n_kt > 0, key tiles.
 hipError_t prefill_summarize(const PrefillArgs& a, const Plan& pl, hipStream_t stream);
 size_t prefill_plan_bytes(int p);
+// pl.order[0 .. pl.n_qt) = the indices 0 .. pl.n_qt - 1 by pl.cost (each in
+// [0, pl.max_cost]), costliest first (one workgroup; identity order when
+// max_cost is too large for its bins).
+hipError_t prefill_order(const Plan& pl, hipStream_t stream);
 
 }  // namespace gqa

@@ -985,6 +985,11 @@ hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t prefill_order(const Plan& pl, hipStream_t stream) {
+  prefill_order_kernel<<<1, kPrepThreads, 0, stream>>>(pl);
+  return hipGetLastError();
+}
+
 hipError_t prefill_summarize(const PrefillArgs& a, const Plan& pl, hipStream_t stream) {
   const int n_tiles = pl.n_kt + pl.n_qt;
   prefill_summarize_kernel<<<dim3((n_tiles + 3) / 4), dim3(256), 0, stream>>>(a, pl);

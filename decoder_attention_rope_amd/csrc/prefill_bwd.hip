@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, float* delta)
 // Per key tile, the first and last 32-token query tile that can meet it.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_krange_kernel(BwdArgs a, Plan qp, const TileSum* ksum,
-                                                         int2* krange, int n_kt) {
+                                                         int2* krange, int* kcost, int n_kt) {
   const int kt = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (kt >= n_kt) return;
@@ -131,7 +131,10 @@ __global__ __launch_bounds__(256) void bwd_krange_kernel(BwdArgs a, Plan qp, con
     first = min(first, __shfl_xor(first, off, 64));
     last = max(last, __shfl_xor(last, off, 64));
   }
-  if (lane == 0) krange[kt] = make_int2(first, last);
+  if (lane == 0) {
+    krange[kt] = make_int2(first, last);
+    kcost[kt] = last >= first ? last - first + 1 : 0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -307,7 +310,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs a, Plan qp, const TileSum* ksum,
-                                                          const int2* krange, const float* delta) {
+                                                          const int2* krange, const int* korder,
+                                                          const float* delta) {
   constexpr int KS = D / 16, MD = D / 32;
   using B = BT<D>;
   constexpr int qTile = B::bytes(32);              // one Q or dout tile (32 queries)
@@ -321,7 +325,10 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
   LdsByte* smem = (LdsByte*)smem_raw;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-  const int kt = blockIdx.x / a.kv_heads, kh = blockIdx.x % a.kv_heads;
+  // Key tiles costliest first (the most query tiles to visit), so the long
+  // ones do not start last; workgroup i * kv_heads + kh takes KV head kh.
+  const int kt = __builtin_amdgcn_readfirstlane(ld_const(korder, blockIdx.x / a.kv_heads));
+  const int kh = blockIdx.x % a.kv_heads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = wave & 1, hp = wave >> 1;
@@ -386,9 +393,12 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
     }
   };
 
+  // A step's second slot past the last pair stages that last pair again
+  // (finite data; its products are masked to zero), so every step runs the
+  // same straight-line body and the accumulators stay in place.
   if (n_steps > 0) {
     load_pair(0, 0, 0);
-    if (n_pairs > 1) load_pair(1, 1, 0);
+    load_pair(min(1, n_pairs - 1), 1, 0);
     wait_all_loads();
     wg_barrier();
   }
@@ -396,14 +406,17 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
     const int b = step & 1;
     if (step + 1 < n_steps) {
       load_pair(2 * step + 2, 0, b ^ 1);
-      if (2 * step + 3 < n_pairs) load_pair(2 * step + 3, 1, b ^ 1);
+      load_pair(min(2 * step + 3, n_pairs - 1), 1, b ^ 1);
     }
     const int pair = 2 * step + hp;
-    const int qt = rng.x + pair / G;
-    if (pair < n_pairs) {
+    const int qt = rng.x + min(pair, n_pairs - 1) / G;
+    {
       const TileSum q_sum = ld_const(qp.qsum, qt);
-      if (tiles_meet(q_sum, ks_sum, a.window)) {
-        const bool full = tiles_full(q_sum, ks_sum, kt, P, a.window) && (qt + 1) * 32 <= P;
+      // A pair that cannot meet the key tile (or lies past the last pair)
+      // contributes zeros.
+      const bool meet = pair < n_pairs && tiles_meet(q_sum, ks_sum, a.window);
+      {
+        const bool full = meet && tiles_full(q_sum, ks_sum, kt, P, a.window) && (qt + 1) * 32 <= P;
         const LdsByte* pbase = smem + b * stageBytes + hp * pairBytes;
         const LdsByte* qb = pbase;
         const LdsByte* gb = pbase + qTile;
@@ -428,14 +441,14 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
             const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
             const float l2 = lds_ld<float>(misc + iq * 4) * kLog2eB;
             const float dl = lds_ld<float>(misc + 256 + iq * 4);
-            bool ok = k_valid;
+            bool ok = k_valid & meet;
             if (!full) {
               const int qp_ = lds_ld<int>(misc + 512 + iq * 4), qs = lds_ld<int>(misc + 768 + iq * 4);
               ok = ok & (qs == seg_k) & ((uint32_t)qp_ - (uint32_t)pos_k < wlim) & (iq < n_q);
             }
             const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
             p2[e] = p;
-            d2[e] = p * (dp[r + e] - dl);
+            d2[e] = ok ? p * (dp[r + e] - dl) : 0.f;
           }
           pp[r >> 3][(r & 7) >> 1] = pack_bf16x2(p2[0], p2[1]);
           pds[r >> 3][(r & 7) >> 1] = pack_bf16x2(d2[0], d2[1]);
@@ -502,12 +515,12 @@ size_t prefill_bwd_workspace_bytes(int p, int heads) {
   const size_t n_kt = (size_t)(p + kBK - 1) / kBK;
   const size_t n_q32 = (size_t)(p + 31) / 32;
   return prefill_plan_bytes(p) + align256(n_q32 * sizeof(TileSum)) + align256(n_kt * sizeof(int2)) +
-         align256((size_t)p * heads * sizeof(float));
+         2 * align256(n_kt * sizeof(int)) + align256((size_t)p * heads * sizeof(float));
 }
 
 template <int D>
 static hipError_t launch_bwd_main(const BwdArgs& a, const Plan& pl, const Plan& qp, const int2* krange,
-                                  const float* delta, hipStream_t stream) {
+                                  const int* korder, const float* delta, hipStream_t stream) {
   const int n_groups = a.kv_heads * pl.head_groups;
   const dim3 gq(pl.n_qt * n_groups), blk(256);
   if (pl.gw == 4) bwd_dq_kernel<D, 4><<<gq, blk, 0, stream>>>(a, pl, delta);
@@ -515,7 +528,7 @@ static hipError_t launch_bwd_main(const BwdArgs& a, const Plan& pl, const Plan& 
   else bwd_dq_kernel<D, 1><<<gq, blk, 0, stream>>>(a, pl, delta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_dkdv_kernel<D><<<dim3(pl.n_kt * a.kv_heads), blk, 0, stream>>>(a, qp, pl.ksum, krange, delta);
+  bwd_dkdv_kernel<D><<<dim3(pl.n_kt * a.kv_heads), blk, 0, stream>>>(a, qp, pl.ksum, krange, korder, delta);
   return hipGetLastError();
 }
 
@@ -544,18 +557,29 @@ hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t stream) {
   ws += align256(n_q32 * sizeof(TileSum));
   int2* krange = reinterpret_cast<int2*>(ws);
   ws += align256((size_t)pl.n_kt * sizeof(int2));
+  // Key-tile costs and their costliest-first order (the prefill's counting
+  // sort over key tiles instead of query tiles).
+  Plan kp = pl;
+  kp.n_qt = pl.n_kt;
+  kp.cost = reinterpret_cast<int*>(ws);
+  ws += align256((size_t)pl.n_kt * sizeof(int));
+  kp.order = reinterpret_cast<int*>(ws);
+  ws += align256((size_t)pl.n_kt * sizeof(int));
+  kp.max_cost = (int)n_q32;
   float* delta = reinterpret_cast<float*>(ws);
   e = prefill_summarize(pa, qp, stream);
   if (e != hipSuccess) return e;
-  bwd_krange_kernel<<<dim3((pl.n_kt + 3) / 4), dim3(256), 0, stream>>>(a, qp, pl.ksum, krange, pl.n_kt);
+  bwd_krange_kernel<<<dim3((pl.n_kt + 3) / 4), dim3(256), 0, stream>>>(a, qp, pl.ksum, krange, kp.cost, pl.n_kt);
   e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = prefill_order(kp, stream);
   if (e != hipSuccess) return e;
   const long long chunks = (long long)a.p * a.heads * (a.head_dim / 8);
   bwd_delta_kernel<<<dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream>>>(a, delta);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return a.head_dim == 64 ? launch_bwd_main<64>(a, pl, qp, krange, delta, stream)
-                          : launch_bwd_main<128>(a, pl, qp, krange, delta, stream);
+  return a.head_dim == 64 ? launch_bwd_main<64>(a, pl, qp, krange, kp.order, delta, stream)
+                          : launch_bwd_main<128>(a, pl, qp, krange, kp.order, delta, stream);
 }
 
 }  // namespace gqa
