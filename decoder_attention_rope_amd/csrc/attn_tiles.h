@@ -16,6 +16,7 @@ namespace gqa {
 constexpr int kBK = 64;       // keys per tile
 constexpr int kPrepThreads = 1024;
 constexpr int kMaskWords = 6;  // 32-bit words per (query tile, group of 64 key tiles)
+constexpr int kRecInts = 16;   // ints per start record (64 bytes)
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct TileSum {
@@ -31,6 +32,11 @@ struct Plan {
   uint32_t* masks; // [n_qt][n_kg][kMaskWords]: per group of 64 key tiles,
                    // 64-bit masks "visit", "every pair allowed" and "one
                    // segment" (see tiles_oneseg)
+  int* rec;        // [n_qt][kRecInts] or null: per ordered slot i, the start
+                   // of its walk in one record -- query tile order[i], its
+                   // visited key-tile range, the index of the group of 64 key
+                   // tiles holding the first one (-1 if none) and that
+                   // group's kMaskWords mask words
   int n_kt, n_qt, n_kg, tq, head_groups, gw;
   int max_cost;    // costs are clamped to [0, max_cost] for the ordering
 };

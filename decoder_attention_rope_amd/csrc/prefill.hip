@@ -153,8 +153,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_order_kernel(Plan pl) {
   const int nb = pl.max_cost + 1;  // costs 0 .. max_cost
   if (nb > kMaxCostBins) {
     for (int i = tid; i < pl.n_qt; i += kPrepThreads) pl.order[i] = i;
-    return;
-  }
+  } else {
   for (int i = tid; i < nb; i += kPrepThreads) start[i] = 0;
   __syncthreads();
   for (int i = tid; i < pl.n_qt; i += kPrepThreads) atomicAdd(&start[pl.max_cost - pl.cost[i]], 1);
@@ -183,6 +182,23 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_order_kernel(Plan pl) {
   __syncthreads();
   for (int i = tid; i < pl.n_qt; i += kPrepThreads)
     pl.order[atomicAdd(&start[pl.max_cost - pl.cost[i]], 1)] = i;
+  }
+  if (pl.rec == nullptr) return;
+  // Start records: the walk's first scalar loads, in one place per slot.
+  __syncthreads();
+  for (int i = tid; i < pl.n_qt; i += kPrepThreads) {
+    const int qt = pl.order[i];
+    const int2 r = pl.qrange[qt];
+    const int g0 = (pl.n_kg > 0 && r.x <= r.y) ? r.x >> 6 : -1;
+    int* rec = pl.rec + (size_t)i * kRecInts;
+    rec[0] = qt;
+    rec[1] = r.x;
+    rec[2] = r.y;
+    rec[3] = g0;
+    for (int w = 0; w < kMaskWords; ++w)
+      rec[4 + w] = g0 >= 0 ? (int)pl.masks[((size_t)qt * pl.n_kg + g0) * kMaskWords + w] : 0;
+    for (int w = 4 + kMaskWords; w < kRecInts; ++w) rec[w] = 0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -255,7 +271,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   const int hg = grp % pl.head_groups;
   // Tile indices are workgroup-uniform: keep them (and the summary loads that
   // depend on them) on the scalar unit.
-  const int qt = __builtin_amdgcn_readfirstlane(ld_const(pl.order, wi));
+  const int* rec = pl.rec + (long long)wi * kRecInts;
+  const int qt = __builtin_amdgcn_readfirstlane(ld_const(rec, 0));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -283,11 +300,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   u32x4 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = load16(qg + ((long long)q_ld * a.heads + h) * D + ks * 16 + hf * 8);
-  // Retire these loads before the loop: inside it the only vector loads in
-  // flight are the next tile's, so the wait counters stay exact.
+  // These loads are retired before the loop (with the first tile's): inside
+  // it the only vector loads in flight are the next tile's, so the wait
+  // counters stay exact.
+  auto retire_q = [&]() {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
-  asm volatile("" ::"v"(my_pos), "v"(my_seg));
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+    asm volatile("" ::"v"(my_pos), "v"(my_seg));
+  };
 
   f32x16 o[MD];
 #pragma unroll
@@ -297,8 +317,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   float m_run = kNegInf;
   float l_run = 0.f;
 
-  int2 rng = make_int2(ld_const(reinterpret_cast<const int*>(pl.qrange), 2LL * qt),
-                       ld_const(reinterpret_cast<const int*>(pl.qrange), 2LL * qt + 1));
+  int2 rng = make_int2(ld_const(rec, 1), ld_const(rec, 2));
   rng.x = __builtin_amdgcn_readfirstlane(rng.x);
   rng.y = __builtin_amdgcn_readfirstlane(rng.y);
 
@@ -425,8 +444,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   // which every pair is allowed, phase 1 the others (the online softmax does
   // not depend on the order of the key tiles), so each phase runs one
   // specialized loop body.
-  int vis_g = -1;
-  unsigned long long vis_m = 0, full_m = 0, one_m = 0;
+  // The masks of the first group come with the start record.
+  int vis_g = __builtin_amdgcn_readfirstlane(ld_const(rec, 3));
+  unsigned long long vis_m = (unsigned long long)(uint32_t)ld_const(rec, 4) | ((unsigned long long)(uint32_t)ld_const(rec, 5) << 32);
+  unsigned long long full_m = (unsigned long long)(uint32_t)ld_const(rec, 6) | ((unsigned long long)(uint32_t)ld_const(rec, 7) << 32);
+  unsigned long long one_m = (unsigned long long)(uint32_t)ld_const(rec, 8) | ((unsigned long long)(uint32_t)ld_const(rec, 9) << 32);
   auto next_in = [&](int kt, int phase) {
     while (kt <= rng.y) {
       const int g = kt >> 6;
@@ -871,6 +893,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
         const i32x4 r0 = tile_src(cur, a.v);
         static_for<VU>([&](auto uc) { v_load(r0, 0, uc); });
       }
+      retire_q();
       wait_loads(extra_load);
       barrier();
     }
@@ -933,7 +956,7 @@ size_t prefill_plan_bytes(int p) {
   const size_t n_kg = (n_kt + 63) / 64;
   return align256(n_kt * sizeof(TileSum)) + align256(n_qt * sizeof(TileSum)) +
          align256(n_qt * sizeof(int2)) + 2 * align256(n_qt * sizeof(int)) +
-         align256(n_qt * n_kg * kMaskWords * sizeof(uint32_t));
+         align256(n_qt * n_kg * kMaskWords * sizeof(uint32_t)) + align256(n_qt * kRecInts * sizeof(int));
 }
 
 size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim) {
@@ -973,6 +996,9 @@ hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream) {
   pl.cost = reinterpret_cast<int*>(ws + n_kt_b + q_b + r_b + align256(n_qt_max * sizeof(int)));
   pl.n_kg = (pl.n_kt + 63) / 64;
   pl.masks = reinterpret_cast<uint32_t*>(ws + n_kt_b + q_b + r_b + 2 * align256(n_qt_max * sizeof(int)));
+  const size_t n_kg_max = ((a.p + kBK - 1) / kBK + 63) / 64;
+  pl.rec = reinterpret_cast<int*>(reinterpret_cast<char*>(pl.masks) +
+                                  align256(n_qt_max * n_kg_max * kMaskWords * sizeof(uint32_t)));
 
   const int n_tiles = pl.n_kt + pl.n_qt;
   prefill_summarize_kernel<<<dim3((n_tiles + 3) / 4), dim3(256), 0, stream>>>(a, pl);

@@ -560,6 +560,7 @@ hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t stream) {
   // Key-tile costs and their costliest-first order (the prefill's counting
   // sort over key tiles instead of query tiles).
   Plan kp = pl;
+  kp.rec = nullptr;
   kp.n_qt = pl.n_kt;
   kp.cost = reinterpret_cast<int*>(ws);
   ws += align256((size_t)pl.n_kt * sizeof(int));
