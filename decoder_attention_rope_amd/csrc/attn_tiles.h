@@ -19,8 +19,11 @@ constexpr int kMaskWords = 6;  // 32-bit words per (query tile, group of 64 key 
 constexpr int kRecInts = 16;   // ints per start record (64 bytes)
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// Per tile of tokens: [min, max] of segments and positions, and the smallest
+// position among the tokens of segment seg_min (pos_first) and of segment
+// seg_max (pos_last).
 struct TileSum {
-  int seg_min, seg_max, pos_min, pos_max;
+  int seg_min, seg_max, pos_min, pos_max, pos_first, pos_last, pad0, pad1;
 };
 
 struct Plan {
@@ -51,12 +54,21 @@ typedef __attribute__((address_space(4))) const int ConstInt;
 __device__ __forceinline__ int ld_const(const int* p, long long i) { return ((ConstInt*)p)[i]; }
 __device__ __forceinline__ TileSum ld_const(const TileSum* p, int i) {
   const int* b = reinterpret_cast<const int*>(p + i);
-  return TileSum{ld_const(b, 0), ld_const(b, 1), ld_const(b, 2), ld_const(b, 3)};
+  return TileSum{ld_const(b, 0), ld_const(b, 1), ld_const(b, 2), ld_const(b, 3), ld_const(b, 4), ld_const(b, 5), 0, 0};
 }
 
+// Whether a query tile and a key tile may hold an allowed pair (a superset
+// test: the walk visits these, the per-element mask is exact). When the two
+// tiles can share only the key tile's first (or last) segment, only that
+// segment's keys count: a key tile that straddles the end of a segment is
+// not visited by the segment's early queries.
 __device__ __forceinline__ bool tiles_meet(const TileSum& q, const TileSum& k, int window) {
   if (k.seg_max < q.seg_min || k.seg_min > q.seg_max) return false;
-  if (k.pos_min > q.pos_max) return false;
+  // Plain values first: a conditional between two fields of one struct
+  // would select an address and keep the struct in memory.
+  const int p_first = k.pos_first, p_last = k.pos_last, p_min = k.pos_min;
+  const int kp = q.seg_max == k.seg_min ? p_first : q.seg_min == k.seg_max ? p_last : p_min;
+  if (kp > q.pos_max) return false;
   if (window > 0 && (long long)q.pos_min - (long long)k.pos_max >= window) return false;
   return true;
 }

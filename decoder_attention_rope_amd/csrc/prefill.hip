@@ -45,9 +45,10 @@ namespace gqa {
 
 
 // ---------------------------------------------------------------------------
-// Prep 1: per-tile [min, max] of segments and positions. One wavefront per
-// tile: key tiles (64 tokens) first, then query tiles (tq tokens); lanes read
-// consecutive tokens and reduce with shuffles.
+// Prep 1: per-tile [min, max] of segments and positions, and the smallest
+// position of the first and of the last segment. One wavefront per tile: key
+// tiles (64 tokens) first, then query tiles (tq <= 128 tokens); each lane
+// holds at most two tokens and the wavefront reduces with shuffles.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void prefill_summarize_kernel(PrefillArgs a, Plan pl) {
   const int wave = threadIdx.x >> 6;
@@ -55,17 +56,16 @@ __global__ __launch_bounds__(256) void prefill_summarize_kernel(PrefillArgs a, P
   const int ti = blockIdx.x * 4 + wave;
   if (ti >= pl.n_kt + pl.n_qt) return;
   const bool is_k = ti < pl.n_kt;
-  const int len = is_k ? kBK : pl.tq;
+  const int len = is_k ? kBK : pl.tq;  // at most 128: two tokens per lane
   const int lo = is_k ? ti * kBK : (ti - pl.n_kt) * pl.tq;
   const int hi = min(a.p, lo + len);
-  int smin = 0x7fffffff, smax = (int)0x80000000, pmin = 0x7fffffff, pmax = (int)0x80000000;
-  for (int t = lo + lane; t < hi; t += 64) {
-    const int sg = a.segments ? a.segments[t] : 0, ps = a.positions[t];
-    smin = min(smin, sg);
-    smax = max(smax, sg);
-    pmin = min(pmin, ps);
-    pmax = max(pmax, ps);
-  }
+  const int t0 = lo + lane, t1 = lo + 64 + lane;
+  const bool h0 = t0 < hi, h1 = t1 < min(hi, lo + len);
+  const int sg0 = h0 ? (a.segments ? a.segments[t0] : 0) : 0, ps0 = h0 ? a.positions[t0] : 0;
+  const int sg1 = h1 ? (a.segments ? a.segments[t1] : 0) : 0, ps1 = h1 ? a.positions[t1] : 0;
+  constexpr int kMaxI = 0x7fffffff, kMinI = (int)0x80000000;
+  int smin = min(h0 ? sg0 : kMaxI, h1 ? sg1 : kMaxI), smax = max(h0 ? sg0 : kMinI, h1 ? sg1 : kMinI);
+  int pmin = min(h0 ? ps0 : kMaxI, h1 ? ps1 : kMaxI), pmax = max(h0 ? ps0 : kMinI, h1 ? ps1 : kMinI);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     smin = min(smin, __shfl_xor(smin, off, 64));
@@ -73,8 +73,16 @@ __global__ __launch_bounds__(256) void prefill_summarize_kernel(PrefillArgs a, P
     pmin = min(pmin, __shfl_xor(pmin, off, 64));
     pmax = max(pmax, __shfl_xor(pmax, off, 64));
   }
+  // Smallest positions within the first and the last segment.
+  int pfirst = min((h0 && sg0 == smin) ? ps0 : kMaxI, (h1 && sg1 == smin) ? ps1 : kMaxI);
+  int plast = min((h0 && sg0 == smax) ? ps0 : kMaxI, (h1 && sg1 == smax) ? ps1 : kMaxI);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    pfirst = min(pfirst, __shfl_xor(pfirst, off, 64));
+    plast = min(plast, __shfl_xor(plast, off, 64));
+  }
   if (lane == 0) {
-    const TileSum sum{smin, smax, pmin, pmax};
+    const TileSum sum{smin, smax, pmin, pmax, pfirst, plast, 0, 0};
     if (is_k) pl.ksum[ti] = sum;
     else pl.qsum[ti - pl.n_kt] = sum;
   }
