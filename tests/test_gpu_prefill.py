@@ -77,6 +77,27 @@ def test_prefill_arbitrary_order_and_ids():
         assert_close(f64(out), ref, "bf16", f"prefill shuffled/duplicates W={window}")
 
 
+def test_prefill_descending_ids_offset_positions():
+    """Key tiles that straddle segment boundaries with segment ids in
+    descending order (a tile's smallest id sits in its later tokens) and
+    positions that start at a per-segment offset: the tile walk may skip a
+    key tile only when no pair in it is allowed."""
+    heads, kvh, d = 32, 8, 128
+    g = W.streams(4343)
+    lengths, pos, seg = W.segment_layout(700, 20, 150, g["index"])
+    n = len(lengths)
+    seg = (n - 1 - seg).astype(np.int32)
+    offs = g["index"].integers(0, 300, n).astype(np.int32)
+    pos = (pos + offs[n - 1 - seg]).astype(np.int32)
+    dv, hv, (sk, sk64), _ = make_inputs(4343, len(pos), heads, kvh, d)
+    o = oracle.default()
+    for window, sinks in ((0, None), (48, sk)):
+        print(f"[case] prefill descending ids W={window}", flush=True)
+        out = run_prefill(*dv, pos, seg, heads, kvh, d, window, sinks)
+        ref = o.packed(*hv, pos, seg, window=window, sinks=None if sinks is None else sk64)
+        assert_close(f64(out), ref, "bf16", f"prefill descending ids W={window}")
+
+
 def test_prefill_llama8b_packed_full_sampled():
     wl = W.LLAMA8B_PACKED
     p = wl.extra["p"]
