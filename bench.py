@@ -41,12 +41,181 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the absolute numbers of the three other workload configurations")
     ap.add_argument("--cpu-sample-rows", type=int, default=64)
     ap.add_argument("--cpu-sample-queries", type=int, default=16384)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch's copy kernel), for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters to bytes")
     return ap.parse_args()
+
+
+def other_configs(gqa, W, torch, np, stream, reps):
+    """Absolute numbers for the three other workload configurations (tiny
+    Llama example, GPT-2 f32 decode_rows, gpt-oss SinkAttention): each step
+    of the path timed with HIP events on the library's stream, inputs
+    resident in HBM. Context beside the benchmark line, not part of it."""
+    dev, bf16, f32 = "cuda", torch.bfloat16, torch.float32
+    CONTIG = gqa.GQA_CACHE_CONTIGUOUS
+
+    def ev_time(fn, n_rep):
+        """Mean microseconds per call over n_rep back-to-back calls (after
+        warm-up calls), bracketed by one pair of events."""
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n_rep):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n_rep
+
+    out = {}
+    # ---- tiny Llama example: prefill S=128 then 16 decode steps, MaxSeq 512 ----
+    wl = W.TINY_LLAMA
+    H, KVH, D, S, NS, MS = wl.heads, wl.kv_heads, wl.head_dim, wl.extra["prefill"], \
+        wl.extra["decode_steps"], wl.extra["max_seq"]
+    n = S + NS
+    q = W.device_normal((n, H, D), 1, "q", bf16)
+    k = W.device_normal((n, KVH, D), 1, "k", bf16)
+    v = W.device_normal((n, KVH, D), 1, "v", bf16)
+    pos = torch.arange(n, dtype=torch.int32, device=dev)
+    seg = torch.zeros(S, dtype=torch.int32, device=dev)
+    rows = torch.zeros(n, dtype=torch.int32, device=dev)
+    tab = torch.empty((2, MS, D // 2), dtype=bf16, device=dev)
+    ck = torch.zeros((1, KVH, MS, D), dtype=bf16, device=dev)
+    cv = torch.zeros_like(ck)
+    o_p = torch.empty((S, H, D), dtype=bf16, device=dev)
+    o_d = torch.empty((1, H, D), dtype=bf16, device=dev)
+    nbp = gqa.gqa_prefill_packed_workspace(S, H, KVH, D)
+    wsp = torch.empty(max(nbp, 256), dtype=torch.uint8, device=dev)
+    nbd = gqa.gqa_decode_rows_workspace(1, H, KVH, D, MS)
+    wsd = torch.empty(max(nbd, 256), dtype=torch.uint8, device=dev)
+    gqa.gqa_rope_table(D, MS, wl.theta, gqa.GQA_BF16, tab)
+
+    def tiny_prefill():
+        gqa.gqa_rope_write_kv(S, H, KVH, D, gqa.GQA_BF16, q[:S], k[:S], v[:S], pos[:S], tab, MS,
+                              CONTIG, ck, cv, 1, MS, rows[:S], None, None, 0, 0)
+        gqa.gqa_prefill_packed(S, H, KVH, D, gqa.GQA_BF16, 0.0, 0, None, q[:S], k[:S], v[:S],
+                               pos[:S], seg, o_p, wsp, nbp)
+
+    def tiny_decode():
+        for i in range(S, n):
+            gqa.gqa_rope_write_kv(1, H, KVH, D, gqa.GQA_BF16, q[i:i + 1], k[i:i + 1], v[i:i + 1],
+                                  pos[i:i + 1], tab, MS, CONTIG, ck, cv, 1, MS, rows[i:i + 1],
+                                  None, None, 0, 0)
+            gqa.gqa_decode_rows(1, H, KVH, D, gqa.GQA_BF16, 0.0, 0, None, q[i:i + 1], ck, cv, MS,
+                                pos[i:i + 1], o_d, wsd, nbd)
+
+    t_p = ev_time(tiny_prefill, reps)
+    t_d = ev_time(tiny_decode, reps)
+    dec_bytes = sum((p_ + 1) * KVH * D * 2 * 2 for p_ in range(S, n))
+    out["tiny_llama"] = {
+        "workload": wl.name, "prefill_us": t_p, "prefill_flops": 4 * D * H * S * (S + 1) // 2,
+        "prefill_tflops": 4 * D * H * S * (S + 1) // 2 / t_p / 1e6,
+        "decode_us_per_step": t_d / NS, "decode_kv_bytes_per_step": dec_bytes // NS,
+        "decode_gbs": dec_bytes / t_d / 1e3,
+        "note": "prefill = rope + KV write + attention; a decode step = rope + KV write + "
+                "decode_rows of one token; latency-bound at this size"}
+    del q, k, v, ck, cv
+
+    # ---- GPT-2 MHA decode_rows, f32, Batch 32, cache [32, 12, 1024, 64] ----
+    wl = W.GPT2_DECODE_ROWS
+    H, KVH, D, B, MS = wl.heads, wl.kv_heads, wl.head_dim, wl.extra["batch"], wl.extra["max_seq"]
+    g = W.streams(2)
+    dpos = W.uniform_positions(B, 0, MS - 1, g["extra"])
+    d_pos = torch.from_numpy(dpos).to(dev)
+    # The K + V working set (~100 MB attended, 201 MB allocated) fits the
+    # 256 MB Infinity Cache: six cache copies rotate so each call reads HBM.
+    copies = [(W.device_normal((B, KVH, MS, D), 2, "pool_k", f32) + c,
+               W.device_normal((B, KVH, MS, D), 2, "pool_v", f32) + c) for c in range(6)]
+    q2 = W.device_normal((B, H, D), 2, "q", f32)
+    o2 = torch.empty((B, H, D), dtype=f32, device=dev)
+    nb2 = gqa.gqa_decode_rows_workspace(B, H, KVH, D, MS)
+    ws2 = torch.empty(max(nb2, 256), dtype=torch.uint8, device=dev)
+    it = [0]
+
+    def gpt2_decode():
+        ck_, cv_ = copies[it[0] % len(copies)]
+        it[0] += 1
+        gqa.gqa_decode_rows(B, H, KVH, D, gqa.GQA_F32, 0.0, 0, None, q2, ck_, cv_, MS, d_pos, o2,
+                            ws2, nb2)
+
+    t2 = ev_time(gpt2_decode, 10 * len(copies))
+    b2 = int(np.sum(dpos.astype(np.int64) + 1)) * KVH * D * 4 * 2 + 2 * B * H * D * 4
+    out["gpt2_decode_rows_f32"] = {
+        "workload": wl.name, "avg_us": t2, "algorithmic_bytes": b2, "gbs": b2 / t2 / 1e3,
+        "frac_of_hbm_peak": b2 / t2 / 1e3 / HBM_PEAK_GBS,
+        "note": "six cache copies rotate between calls (the working set would otherwise be "
+                "served by the Infinity Cache)"}
+    del copies
+
+    # ---- gpt-oss-20b SinkAttention: prefill 4096 + 256 decode steps, W 128 / full ----
+    wl = W.GPT_OSS_SINK
+    H, KVH, D, S, NS, MS = wl.heads, wl.kv_heads, wl.head_dim, wl.extra["prefill"], \
+        wl.extra["decode_steps"], wl.extra["max_seq"]
+    n = S + NS
+    tab5 = torch.empty((2, MS, D // 2), dtype=bf16, device=dev)
+    gqa.gqa_rope_table(D, MS, wl.theta, gqa.GQA_BF16, tab5)
+    pos5 = torch.arange(n, dtype=torch.int32, device=dev)
+    seg5 = torch.zeros(S, dtype=torch.int32, device=dev)
+    rows5 = torch.zeros(n, dtype=torch.int32, device=dev)
+    nbp5 = gqa.gqa_prefill_packed_workspace(S, H, KVH, D)
+    wsp5 = torch.empty(max(nbp5, 256), dtype=torch.uint8, device=dev)
+    nbd5 = gqa.gqa_decode_rows_workspace(1, H, KVH, D, MS)
+    wsd5 = torch.empty(max(nbd5, 256), dtype=torch.uint8, device=dev)
+    for layer, win in enumerate(wl.extra["windows"]):
+        q = W.device_normal((n, H, D), 5, "q", bf16)
+        k = W.device_normal((n, KVH, D), 5, "k", bf16)
+        v = W.device_normal((n, KVH, D), 5, "v", bf16)
+        sinks = W.device_normal((H,), 5 + layer, "sinks", bf16)
+        ck = torch.zeros((1, KVH, MS, D), dtype=bf16, device=dev)
+        cv = torch.zeros_like(ck)
+        o_p = torch.empty((S, H, D), dtype=bf16, device=dev)
+        o_d = torch.empty((1, H, D), dtype=bf16, device=dev)
+
+        def oss_prefill():
+            gqa.gqa_rope_write_kv(S, H, KVH, D, gqa.GQA_BF16, q[:S], k[:S], v[:S], pos5[:S], tab5,
+                                  MS, CONTIG, ck, cv, 1, MS, rows5[:S], None, None, 0, 0)
+            gqa.gqa_prefill_packed(S, H, KVH, D, gqa.GQA_BF16, 0.0, win, sinks, q[:S], k[:S], v[:S],
+                                   pos5[:S], seg5, o_p, wsp5, nbp5)
+
+        def oss_attn_only():
+            gqa.gqa_prefill_packed(S, H, KVH, D, gqa.GQA_BF16, 0.0, win, sinks, q[:S], k[:S], v[:S],
+                                   pos5[:S], seg5, o_p, wsp5, nbp5)
+
+        def oss_decode():
+            for i in range(S, n):
+                gqa.gqa_rope_write_kv(1, H, KVH, D, gqa.GQA_BF16, q[i:i + 1], k[i:i + 1],
+                                      v[i:i + 1], pos5[i:i + 1], tab5, MS, CONTIG, ck, cv, 1, MS,
+                                      rows5[i:i + 1], None, None, 0, 0)
+                gqa.gqa_decode_rows(1, H, KVH, D, gqa.GQA_BF16, 0.0, win, sinks, q[i:i + 1], ck, cv,
+                                    MS, pos5[i:i + 1], o_d, wsd5, nbd5)
+
+        t_p = ev_time(oss_prefill, reps)
+        t_a = ev_time(oss_attn_only, reps)
+        t_d = ev_time(oss_decode, 2)
+        if win > 0:
+            pairs = sum(min(i + 1, win) for i in range(S))
+            kv = sum(min(p_ + 1, win) for p_ in range(S, n))
+        else:
+            pairs = S * (S + 1) // 2
+            kv = sum(p_ + 1 for p_ in range(S, n))
+        fl = 4 * D * H * pairs
+        kvb = kv * KVH * D * 2 * 2
+        out[f"gpt_oss_layer{layer}_window{win}"] = {
+            "workload": f"{wl.name}: layer {layer}, window {win or 'none'}", "prefill_us": t_p,
+            "attention_us": t_a, "prefill_flops": fl, "attention_tflops": fl / t_a / 1e6,
+            "attention_frac_of_mfma_peak": fl / t_a / 1e6 / MFMA_BF16_PEAK_TFLOPS,
+            "decode_loop_us": t_d, "decode_us_per_step": t_d / NS,
+            "decode_kv_bytes_per_step": kvb // NS, "decode_gbs": kvb / t_d / 1e3,
+            "note": "prefill = rope + KV write + attention (attention alone beside it); a decode "
+                    "step = rope + KV write + decode_rows of one token (launch-bound)"}
+        del q, k, v, ck, cv
+    return out
 
 
 def copy_calibration():
@@ -204,6 +373,8 @@ def main():
     wall = time.perf_counter() - t0
     per_op_ms = {n: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in evs]))
                  for i, n in enumerate(names)}
+    per_op_pct = {n: [float(np.percentile([ev[i].elapsed_time(ev[i + 1]) * 1e3 for ev in evs], p_))
+                      for p_ in (10, 50, 90)] for i, n in enumerate(names)}
     step_ms = float(np.mean([ev[0].elapsed_time(ev[5]) for ev in evs]))
 
     # ---------------- next row: chunked prefill over a paged prefix ----------------
@@ -365,6 +536,9 @@ def main():
                 "workload": f"packed prefill batch above ({P} tokens), dq + dk + dv"}
     del b_dout, b_lse, b_out, b_dq, b_dk, b_dv, b_ws
 
+    # ---------------- the other workload configurations (context) ----------------
+    others = None if args.no_other_configs else other_configs(gqa, W, torch, np, stream, 20)
+
     # ---------------- algorithmic work ----------------
     kv_bytes = int(np.sum(lengths)) * KVH * D * 2 * 2          # K + V of attended keys
     qo_bytes = 2 * rows * H * D * 2                              # q in, out
@@ -446,6 +620,8 @@ def main():
                       "prefill_packed_backward": bwd_roof,
                       "qkv_rope_write": qkv_roof},
         "per_op_us": {k: v * 1e3 for k, v in per_op_ms.items()},
+        "per_op_us_p10_p50_p90": per_op_pct,
+        "other_configs": others,
         "wall_s_timed": wall,
         "cpu_baseline": cpu,
     }
