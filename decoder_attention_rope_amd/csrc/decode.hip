@@ -78,32 +78,42 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(DecodeArgs a) {
     Elem<T>::to_f32(load16(qp), qr[h]);
   }
 
-  // Phase 1: scaled scores (log2 domain) of every key of the split.
-  for (int base = 0; base < n; base += TPP) {
-    const int i = base + tk;
-    float dot[GC];
+  // Phase 1: scaled scores (log2 domain) of every key of the split. The
+  // loads of UNR passes are issued before any of them is used, so that many
+  // memory round trips overlap.
+  constexpr int UNR = 8;
+  for (int base = 0; base < n; base += TPP * UNR) {
+    u32x4 raw[UNR];
+    bool valid[UNR];
 #pragma unroll
-    for (int h = 0; h < GC; ++h) dot[h] = 0.f;
-    bool valid = false;
-    if (i < n) {
-      const T* kp = row_ptr<T, D, PAGED>(a, a.k, r, kh, t0 + i);
-      if (kp != nullptr) {
-        valid = true;
+    for (int u = 0; u < UNR; ++u) {
+      const int i = base + u * TPP + tk;
+      const T* kp = i < n ? row_ptr<T, D, PAGED>(a, a.k, r, kh, t0 + i) : nullptr;
+      valid[u] = kp != nullptr;
+      raw[u] = valid[u] ? load16(kp + sub * EPL) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = base + u * TPP + tk;
+      float dot[GC];
+#pragma unroll
+      for (int h = 0; h < GC; ++h) dot[h] = 0.f;
+      if (valid[u]) {
         float x[EPL];
-        Elem<T>::to_f32(load16(kp + sub * EPL), x);
+        Elem<T>::to_f32(raw[u], x);
 #pragma unroll
         for (int h = 0; h < GC; ++h)
 #pragma unroll
           for (int e = 0; e < EPL; ++e) dot[h] += qr[h][e] * x[e];
       }
-    }
 #pragma unroll
-    for (int off = LPT / 2; off >= 1; off >>= 1)
+      for (int off = LPT / 2; off >= 1; off >>= 1)
 #pragma unroll
-      for (int h = 0; h < GC; ++h) dot[h] += __shfl_xor(dot[h], off, 64);
-    if (sub == 0 && i < n) {
+        for (int h = 0; h < GC; ++h) dot[h] += __shfl_xor(dot[h], off, 64);
+      if (sub == 0 && i < n) {
 #pragma unroll
-      for (int h = 0; h < GC; ++h) sc[h][i] = valid ? dot[h] * a.scale_log2 : kNegInf;
+        for (int h = 0; h < GC; ++h) sc[h][i] = valid[u] ? dot[h] * a.scale_log2 : kNegInf;
+      }
     }
   }
   __syncthreads();
@@ -133,13 +143,23 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(DecodeArgs a) {
   for (int h = 0; h < GC; ++h)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  for (int base = 0; base < n; base += TPP) {
-    const int i = base + tk;
-    if (i < n) {
-      const T* vp = row_ptr<T, D, PAGED>(a, a.v, r, kh, t0 + i);
-      if (vp != nullptr) {  // keys of invalid pages were never scored
+  for (int base = 0; base < n; base += TPP * UNR) {
+    u32x4 raw[UNR];
+    bool valid[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = base + u * TPP + tk;
+      // Keys of invalid pages were never scored.
+      const T* vp = i < n ? row_ptr<T, D, PAGED>(a, a.v, r, kh, t0 + i) : nullptr;
+      valid[u] = vp != nullptr;
+      raw[u] = valid[u] ? load16(vp + sub * EPL) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (valid[u]) {
+        const int i = base + u * TPP + tk;
         float x[EPL];
-        Elem<T>::to_f32(load16(vp + sub * EPL), x);
+        Elem<T>::to_f32(raw[u], x);
 #pragma unroll
         for (int h = 0; h < GC; ++h) {
           const float p = sc[h][i];
