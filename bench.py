@@ -73,6 +73,41 @@ def other_configs(gqa, W, torch, np, stream, reps):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / n_rep
 
+    def graph_time(fn, result, inputs, n_rep=20):
+        """Mean microseconds per replay of fn captured in a HIP graph (no host
+        launch cost), or None if a replay's result differs from the eager one
+        (three replays, checked bit for bit, with host synchronization between).
+        fn rotates q and k in place, so `inputs` are restored before the eager
+        reference and before each checked replay."""
+        saved = [x.clone() for x in inputs]
+
+        def restore():
+            for x, x0 in zip(inputs, saved):
+                x.copy_(x0)
+
+        restore()
+        fn()
+        torch.cuda.synchronize()
+        ref = result.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        for _ in range(3):
+            restore()
+            result.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(result.view(torch.int16), ref.view(torch.int16)):
+                return None
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gs = torch.cuda.current_stream()
+        e0.record(gs)
+        for _ in range(n_rep):
+            graph.replay()
+        e1.record(gs)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n_rep
+
     out = {}
     # ---- tiny Llama example: prefill S=128 then 16 decode steps, MaxSeq 512 ----
     wl = W.TINY_LLAMA
@@ -112,14 +147,18 @@ def other_configs(gqa, W, torch, np, stream, reps):
 
     t_p = ev_time(tiny_prefill, reps)
     t_d = ev_time(tiny_decode, reps)
+    t_dg = graph_time(tiny_decode, o_d, [q, k])
     dec_bytes = sum((p_ + 1) * KVH * D * 2 * 2 for p_ in range(S, n))
     out["tiny_llama"] = {
         "workload": wl.name, "prefill_us": t_p, "prefill_flops": 4 * D * H * S * (S + 1) // 2,
         "prefill_tflops": 4 * D * H * S * (S + 1) // 2 / t_p / 1e6,
         "decode_us_per_step": t_d / NS, "decode_kv_bytes_per_step": dec_bytes // NS,
         "decode_gbs": dec_bytes / t_d / 1e3,
+        "decode_us_per_step_graph": None if t_dg is None else t_dg / NS,
+        "decode_gbs_graph": None if t_dg is None else dec_bytes / t_dg / 1e3,
         "note": "prefill = rope + KV write + attention; a decode step = rope + KV write + "
-                "decode_rows of one token; latency-bound at this size"}
+                "decode_rows of one token, launched from Python (host-bound) and, in "
+                "decode_us_per_step_graph, replayed from a HIP graph of the 16 steps"}
     del q, k, v, ck, cv
 
     # ---- GPT-2 MHA decode_rows, f32, Batch 32, cache [32, 12, 1024, 64] ----
@@ -198,6 +237,7 @@ def other_configs(gqa, W, torch, np, stream, reps):
         t_p = ev_time(oss_prefill, reps)
         t_a = ev_time(oss_attn_only, reps)
         t_d = ev_time(oss_decode, 2)
+        t_dg = graph_time(oss_decode, o_d, [q, k], 5)
         if win > 0:
             pairs = sum(min(i + 1, win) for i in range(S))
             kv = sum(min(p_ + 1, win) for p_ in range(S, n))
@@ -211,9 +251,13 @@ def other_configs(gqa, W, torch, np, stream, reps):
             "attention_us": t_a, "prefill_flops": fl, "attention_tflops": fl / t_a / 1e6,
             "attention_frac_of_mfma_peak": fl / t_a / 1e6 / MFMA_BF16_PEAK_TFLOPS,
             "decode_loop_us": t_d, "decode_us_per_step": t_d / NS,
+            "decode_us_per_step_graph": None if t_dg is None else t_dg / NS,
             "decode_kv_bytes_per_step": kvb // NS, "decode_gbs": kvb / t_d / 1e3,
+            "decode_gbs_graph": None if t_dg is None else kvb / t_dg / 1e3,
             "note": "prefill = rope + KV write + attention (attention alone beside it); a decode "
-                    "step = rope + KV write + decode_rows of one token (launch-bound)"}
+                    "step = rope + KV write + decode_rows of one token, launched from Python "
+                    "(host-bound) and, in decode_us_per_step_graph, replayed from a HIP graph "
+                    "of the 256 steps"}
         del q, k, v, ck, cv
     return out
 
