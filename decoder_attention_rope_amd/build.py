@@ -27,9 +27,17 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source flags. The backward's dK/dV kernel keeps its accumulators in
+# plain VGPRs (it fits in 256); the compiler's default accumulator-register
+# form made it copy accumulators between register files every step.
+SOURCE_FLAGS = {
+    "prefill_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON_FLAGS + SOURCE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -320,7 +320,11 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
   constexpr int pairBytes = 2 * qTile + 4 * 256;
   constexpr int stageBytes = 2 * pairBytes;
   constexpr int combineBytes = 2 * 2 * MD * 16 * 64 * 4;
-  constexpr int ldsBytes = 2 * stageBytes > combineBytes ? 2 * stageBytes : combineBytes;
+  // The key tile's K and V rows (64 each, padded), after the stages: read as
+  // the B operands of S and dP every step instead of held in registers.
+  constexpr int kvOff = 2 * stageBytes;
+  constexpr int kvTile = B::bytes(64);
+  constexpr int ldsBytes = kvOff + 2 * kvTile > combineBytes ? kvOff + 2 * kvTile : combineBytes;
   __shared__ __attribute__((aligned(16))) char smem_raw[ldsBytes];
   LdsByte* smem = (LdsByte*)smem_raw;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
@@ -341,14 +345,25 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
   const uint32_t wlim = a.window > 0 ? (uint32_t)a.window : 0x80000000u;
   const float scale_log2 = a.scale * kLog2eB;
 
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + ((long long)key_ld * a.kv_heads + kh) * D;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + ((long long)key_ld * a.kv_heads + kh) * D;
-  u32x4 kf[KS], vf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = load16(kg + ks * 16 + hf * 8);
-    vf[ks] = load16(vg + ks * 16 + hf * 8);
+  // Stage K and V of the key tile: row r of each padded tile holds key
+  // kt * 64 + r at KV head kh (rows past P and the pad chunks read zeros).
+  {
+    const int n_rows = min(kBK, P - kt * kBK);
+    const int rb = a.kv_heads * D * 2;
+    const long long e0 = ((long long)kt * kBK * a.kv_heads + kh) * D;
+    const int nrec = (n_rows - 1) * rb + 2 * D;
+    const i32x4 rk = raw_rsrc(static_cast<const uint16_t*>(a.k) + e0, nrec);
+    const i32x4 rv = raw_rsrc(static_cast<const uint16_t*>(a.v) + e0, nrec);
+    for (int i = wave; i < B::loads(64); i += 4) {
+      const int p = 64 * i + lane;
+      const int row = p / B::kChunks, ch = p - row * B::kChunks;
+      const int off = (ch == D / 8 || row >= n_rows) ? 0x40000000 : row * rb + ch * 16;
+      lds_dma<16>(rk, lds0 + kvOff + 1024 * i, off);
+      lds_dma<16>(rv, lds0 + kvOff + kvTile + 1024 * i, off);
+    }
   }
+  // This lane's B-operand reads: key 32 kb + qn, dimensions 16 ks + 8 hf ...
+  const int kv_rd = kvOff + (32 * kb + qn) * B::kStride + hf * 16;
   f32x16 dk[MD], dv[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md)
@@ -421,17 +436,44 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
         const LdsByte* qb = pbase;
         const LdsByte* gb = pbase + qTile;
         const LdsByte* misc = pbase + 2 * qTile;  // lse, delta, positions, segments
+        // S = Q K^T and dP = dO V^T; the four operands of a k-step are read
+        // from LDS two k-steps ahead of its MFMAs (a ring of three sets), and
+        // a scheduling fence keeps that order, so LDS latency hides behind
+        // the MFMAs of the steps in between.
         f32x16 s = {}, dp = {};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 aq = lds_ld<bf16x8>(qb + q_rd + ks * 32);
-          const bf16x8 ag = lds_ld<bf16x8>(gb + q_rd + ks * 32);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, __builtin_bit_cast(bf16x8, kf[ks]), s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, __builtin_bit_cast(bf16x8, vf[ks]), dp, 0, 0, 0);
-        }
+        bf16x8 ra[3][4];
+        auto ld_ks = [&](auto kc) {
+          constexpr int ks = decltype(kc)::value;
+          bf16x8* o = ra[ks % 3];
+          o[0] = lds_ld<bf16x8>(qb + q_rd + ks * 32);
+          o[1] = lds_ld<bf16x8>(gb + q_rd + ks * 32);
+          o[2] = lds_ld<bf16x8>(smem + kv_rd + ks * 32);
+          o[3] = lds_ld<bf16x8>(smem + kv_rd + kvTile + ks * 32);
+        };
+        ld_ks(std::integral_constant<int, 0>{});
+        if constexpr (KS > 1) ld_ks(std::integral_constant<int, 1>{});
+        static_for<KS>([&](auto kc) {
+          constexpr int ks = decltype(kc)::value;
+          if constexpr (ks + 2 < KS) ld_ks(std::integral_constant<int, ks + 2>{});
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][0], ra[ks % 3][2], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][1], ra[ks % 3][3], dp, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        });
         // Register r of this lane holds query iq = 16 (r / 8) + 8 hf + r % 8
-        // of the tile and this lane's key.
+        // of the tile and this lane's key; lse and delta of those queries
+        // come as four 16-byte reads each.
         const int n_q = P - qt * 32;
+        float lse_r[16], dl_r[16];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
+          const u32x4 lw = lds_ld<u32x4>(misc + iq0 * 4), dw = lds_ld<u32x4>(misc + 256 + iq0 * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lse_r[4 * c + e] = __uint_as_float(lw[e]);
+            dl_r[4 * c + e] = __uint_as_float(dw[e]);
+          }
+        }
         u32x4 pp[2], pds[2];
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
@@ -439,8 +481,8 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
-            const float l2 = lds_ld<float>(misc + iq * 4) * kLog2eB;
-            const float dl = lds_ld<float>(misc + 256 + iq * 4);
+            const float l2 = lse_r[r + e] * kLog2eB;
+            const float dl = dl_r[r + e];
             bool ok = k_valid & meet;
             if (!full) {
               const int qp_ = lds_ld<int>(misc + 512 + iq * 4), qs = lds_ld<int>(misc + 768 + iq * 4);
@@ -453,15 +495,27 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
           pp[r >> 3][(r & 7) >> 1] = pack_bf16x2(p2[0], p2[1]);
           pds[r >> 3][(r & 7) >> 1] = pack_bf16x2(d2[0], d2[1]);
         }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int md = 0; md < MD; ++md) {
-            const bf16x8 ag = tr_operand<D>(gb, t_off, kk, md);
-            dv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, __builtin_bit_cast(bf16x8, pp[kk]), dv[md], 0, 0, 0);
-            const bf16x8 aq = tr_operand<D>(qb, t_off, kk, md);
-            dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, __builtin_bit_cast(bf16x8, pds[kk]), dk[md], 0, 0, 0);
-          }
+        // dV^T += dO^T P and dK^T += Q^T dS: MFMA j (kk = j / 2 MD, md =
+        // (j / 2) % MD, dV for even j, dK for odd) takes its transposed
+        // operand from a ring of four read three MFMAs ahead.
+        constexpr int NJ = 4 * MD;
+        bf16x8 rt[4];
+        auto tr_j = [&](auto jc) {
+          constexpr int j = decltype(jc)::value, kk = j / (2 * MD), md = (j / 2) % MD;
+          rt[j & 3] = tr_operand<D>((j & 1) ? qb : gb, t_off, kk, md);
+        };
+        tr_j(std::integral_constant<int, 0>{});
+        tr_j(std::integral_constant<int, 1>{});
+        tr_j(std::integral_constant<int, 2>{});
+        static_for<NJ>([&](auto jc) {
+          constexpr int j = decltype(jc)::value, kk = j / (2 * MD), md = (j / 2) % MD;
+          if constexpr (j + 3 < NJ) tr_j(std::integral_constant<int, j + 3>{});
+          if constexpr (j & 1)
+            dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rt[j & 3], __builtin_bit_cast(bf16x8, pds[kk]), dk[md], 0, 0, 0);
+          else
+            dv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rt[j & 3], __builtin_bit_cast(bf16x8, pp[kk]), dv[md], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
     }
     wait_all_loads();
