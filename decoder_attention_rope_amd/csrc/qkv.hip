@@ -22,6 +22,9 @@
 // * Epilogue: accumulators + bias, rounded to bf16, go through LDS so a thread
 //   holds both halves (d, d + D/2) of a head chunk; the rotation is exact in
 //   fp64 and rounded once to T (the same helper as the rope pass).
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 #include "internal.h"
 #include "rope_common.h"
@@ -44,6 +47,16 @@ __device__ __forceinline__ T lds_get(const LdsB* p) {
 template <typename T>
 __device__ __forceinline__ void lds_put(LdsB* p, const T& v) {
   *reinterpret_cast<__attribute__((address_space(3))) T*>(p) = v;
+}
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N - 1 (register
+// indices below must be compile-time constants).
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_impl(f, std::make_integer_sequence<int, N>{});
 }
 }  // namespace
 
@@ -118,17 +131,28 @@ __global__ __launch_bounds__(256, 2) void qkv_kernel(QkvArgs a) {
     if (t + 1 < n_slabs) load_slab((t + 1) * kBK);
     const LdsB* sa = smem + buf * 2 * kSlab + (wm * 64) * kRow + rd;
     const LdsB* sb = smem + buf * 2 * kSlab + kSlab + (wn * 64) * kRow + rd;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const bf16x8 a0 = lds_get<bf16x8>(sa + ks * 32);
-      const bf16x8 a1 = lds_get<bf16x8>(sa + 32 * kRow + ks * 32);
-      const bf16x8 b0 = lds_get<bf16x8>(sb + ks * 32);
-      const bf16x8 b1 = lds_get<bf16x8>(sb + 32 * kRow + ks * 32);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
-    }
+    // Operands of k-step ks + 1 are read while the MFMAs of ks run (a ring
+    // of two sets), each step fenced so the order holds.
+    bf16x8 op[2][4];
+    auto ld_ks = [&](auto kc) {
+      constexpr int ks = decltype(kc)::value;
+      bf16x8* o = op[ks & 1];
+      o[0] = lds_get<bf16x8>(sa + ks * 32);
+      o[1] = lds_get<bf16x8>(sa + 32 * kRow + ks * 32);
+      o[2] = lds_get<bf16x8>(sb + ks * 32);
+      o[3] = lds_get<bf16x8>(sb + 32 * kRow + ks * 32);
+    };
+    ld_ks(std::integral_constant<int, 0>{});
+    unroll<kBK / 16>([&](auto kc) {
+      constexpr int ks = decltype(kc)::value;
+      if constexpr (ks + 1 < kBK / 16) ld_ks(std::integral_constant<int, ks + 1>{});
+      const bf16x8* o = op[ks & 1];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[0], o[2], acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[0], o[3], acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[1], o[2], acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[1], o[3], acc[1][1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     if (t + 1 < n_slabs) store_slab(buf ^ 1);
     __syncthreads();
   }
