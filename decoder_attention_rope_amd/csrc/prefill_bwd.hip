@@ -28,8 +28,9 @@
 //   dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed from
 //   LDS. The two wavefronts of a key half add their sums at the end.
 // Query, dout, K and V tiles go from memory straight into LDS (row r of a
-// 32-row block holding entity kappa(r), rows padded to 2 D + 16 bytes), one
-// tile ahead of the matrix work.
+// 32-row block holding entity kappa(r)), one tile ahead of the matrix work.
+// Tiles read only row-wise have rows padded to 2 D + 16 bytes; tiles that are
+// also read transposed have unpadded rows with XOR-swizzled 16-byte chunks.
 #include "attn_tiles.h"
 #include "common.h"
 #include "internal.h"
@@ -39,8 +40,8 @@ namespace gqa {
 namespace {
 constexpr float kLog2eB = 1.4426950408889634f;
 
-// LDS tile of rows of D bf16 values, padded to 2 D + 16 bytes: a K or V tile
-// of 64 keys, or a Q / dout tile of 32 queries.
+// LDS tile of rows of D bf16 values, padded to 2 D + 16 bytes (the dK/dV
+// kernel's K and V tiles of 64 keys, read row-wise only).
 template <int D>
 struct BT {
   static constexpr int kStride = 2 * D + 16;
@@ -62,31 +63,68 @@ __device__ __forceinline__ int padded_off(int p, int rows, int row_bytes) {
   return (ch == D / 8 || src >= rows) ? 0x40000000 : src * row_bytes + ch * 16;
 }
 
+// Swizzled LDS tile of rows of D bf16 values (the dK/dV kernel's Q and dout
+// tiles, the dQ kernel's K and V tiles): row stride 2 D bytes, 16-byte chunk
+// c of row r stored at chunk c ^ swz(r). Rows are read two ways: 16 lanes
+// reading one chunk of 16 consecutive rows (row-wise operands of S and dP),
+// and 32 lanes reading 4
+// consecutive rows (aligned to 4) x 64 bytes (transposing reads); swz makes
+// both touch every bank once (D = 128: one row is one pass over the 64
+// banks; D = 64: two rows are).
+template <int D>
+struct ST {
+  static constexpr int kStride = 2 * D;
+  static constexpr int kChunks = D / 8;
+  static constexpr int loads(int rows) { return rows * kChunks / 64; }
+  static constexpr int bytes(int rows) { return rows * kStride; }
+  __device__ static __forceinline__ int swz(int r) {
+    return D >= 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  }
+};
+// Source offset of slot p (16-byte LDS chunk) of a swizzled tile whose row r
+// holds row kappa(r) of a [*, row_bytes] tensor; rows at or past `rows`
+// fetch out of range.
+template <int D>
+__device__ __forceinline__ int swz_off(int p, int rows, int row_bytes) {
+  const int row = p / ST<D>::kChunks, pc = p % ST<D>::kChunks;
+  const int src = kappa(row);
+  return src >= rows ? 0x40000000 : src * row_bytes + ((pc ^ ST<D>::swz(row)) << 4);
+}
+// A^T operand (32 dimension rows x 16 entity columns) of a transposed
+// product: two transposing reads of 4 entities each. Lane l of group
+// g = l / 16 supplies the address of LDS row 4 (g / 2) + (l % 16) / 4 (+8 for
+// the second read), dimensions 32 md + 16 (g % 2) + 4 (l % 4) .. +3; rows
+// hold entities kappa(row), which keeps every group of 4 entities in 4
+// consecutive rows. Step kk adds 16 rows, which leaves swz unchanged, so the
+// per-lane offsets are computed once.
+template <int D>
+__device__ __forceinline__ void swz_tr_offs(int lane, int (*off)[2]) {
+  constexpr int MD = D / 32;
+  const int g = lane >> 4, s = lane & 15;
+  const int r0 = 4 * (g >> 1) + (s >> 2);
+#pragma unroll
+  for (int md = 0; md < MD; ++md) {
+    const int c = 4 * md + 2 * (g & 1) + ((s & 3) >> 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = r0 + 8 * h;
+      off[md][h] = r * ST<D>::kStride + ((c ^ ST<D>::swz(r)) << 4) + 8 * (s & 1);
+    }
+  }
+}
+template <int D>
+__device__ __forceinline__ bf16x8 swz_tr_operand(const LdsByte* tile, const int (*off)[2], int kk, int md) {
+  const LdsByte* p = tile + 16 * kk * ST<D>::kStride;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p + off[md][0]));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p + off[md][1]));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Workgroup barrier that neither waits for loads in flight nor lets the
 // compiler move memory accesses across it.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0xF70); }
 
-// A^T operand (32 dimension rows x 16 entity columns) of a transposed product
-// from a padded tile: two transposing reads of 4 entities each. Lane l of
-// group g = l / 16 supplies the address of entity 8 (g / 2) + (l % 16) / 4
-// (+4) of the 16-entity step, dimensions 32 md + 16 (g % 2) + 4 (l % 4); the
-// step's entities 16 kk .. 16 kk + 15 of a 32-row block sit in rows
-// kappa(...), which keeps every group of 4 in 4 consecutive rows.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_operand(const LdsByte* tile, int lane_off, int kk, int md) {
-  constexpr int ks = BT<D>::kStride;
-  const LdsByte* p = tile + lane_off + 16 * kk * ks + 64 * md;
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)p);
-  const bf16x4 hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p + 8 * ks));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-template <int D>
-__device__ __forceinline__ int tr_lane_off(int lane) {
-  const int g = lane >> 4, s = lane & 15;
-  return (4 * (g >> 1) + (s >> 2)) * BT<D>::kStride + (16 * (g & 1) + 4 * (s & 3)) * 2;
-}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -145,7 +183,8 @@ template <int D, int GW>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, const float* delta) {
   constexpr int SUB = 4 / GW, TQ = 32 * SUB, KS = D / 16, MD = D / 32;
   using B = BT<D>;
-  constexpr int kTile = B::bytes(kBK);
+  using SKT = ST<D>;
+  constexpr int kTile = SKT::bytes(kBK);  // K and V tiles swizzled (K is also read transposed)
   constexpr int kOffV = 2 * kTile, kOffP = 4 * kTile;
   __shared__ __attribute__((aligned(16))) char smem_raw[4 * kTile + 2 * 512];
   LdsByte* smem = (LdsByte*)smem_raw;
@@ -185,9 +224,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
     for (int r = 0; r < 16; ++r) dq[md][r] = 0.f;
 
   const int row_bytes = a.kv_heads * D * 2;
-  const int k_rd = qn * B::kStride + hf * 16;
-  const int t_off = tr_lane_off<D>(lane);
-  // Tile loads of key tile kt into buffer b: K and V (B::loads(64) each) and
+  // Row-wise reads: row qn (+32 hb), chunk 2 ks + hf stored at 2 ks ^ k_xc.
+  const int k_row = qn * SKT::kStride;
+  const int k_xc = hf ^ SKT::swz(qn);
+  int t_offs[MD][2];
+  swz_tr_offs<D>(lane, t_offs);
+  // Tile loads of key tile kt into buffer b: K and V (SKT::loads(64) each) and
   // the positions / segments, spread over the 4 wavefronts.
   auto load_tile = [&](int kt, int b) {
     const int n_rows = min(kBK, P - kt * kBK);
@@ -195,10 +237,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
     const int nrec = (n_rows - 1) * row_bytes + 2 * D;
     const i32x4 rk = raw_rsrc(static_cast<const uint16_t*>(a.k) + e0, nrec);
     const i32x4 rv = raw_rsrc(static_cast<const uint16_t*>(a.v) + e0, nrec);
-    for (int i = wave; i < B::loads(kBK); i += 4) {
-      const int off = padded_off<D>(64 * i + lane, kBK, row_bytes);
-      lds_dma<16>(rk, lds0 + b * kTile + 1024 * i, off);
-      lds_dma<16>(rv, lds0 + kOffV + b * kTile + 1024 * i, off);
+    for (int i = wave; i < SKT::loads(kBK); i += 4) {
+      const int off = swz_off<D>(64 * i + lane, kBK, row_bytes);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + b * kTile + 1024 * i);
+      lds_dma<16>(rk, dst, off);
+      lds_dma<16>(rv, dst + kOffV, off);
     }
     if (wave == 3) {
       lds_dma<4>(raw_rsrc(a.positions + (long long)kt * kBK, 4 * n_rows), lds0 + kOffP + b * 512, lane * 4);
@@ -250,8 +293,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ak = lds_ld<bf16x8>(kb + k_rd + hb * 32 * B::kStride + ks * 32);
-        const bf16x8 av = lds_ld<bf16x8>(vb + k_rd + hb * 32 * B::kStride + ks * 32);
+        const int ko = k_row + hb * 32 * SKT::kStride + (((2 * ks) ^ k_xc) << 4);
+        const bf16x8 ak = lds_ld<bf16x8>(kb + ko);
+        const bf16x8 av = lds_ld<bf16x8>(vb + ko);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, __builtin_bit_cast(bf16x8, qf[ks]), s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, gf[ks]), dp, 0, 0, 0);
       }
@@ -277,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
-          const bf16x8 at = tr_operand<D>(kb + hb * 32 * B::kStride, t_off, kk, md);
+          const bf16x8 at = swz_tr_operand<D>(kb + hb * 32 * SKT::kStride, t_offs, kk, md);
           dq[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, __builtin_bit_cast(bf16x8, dsw[kk]), dq[md], 0, 0, 0);
         }
     }
@@ -314,7 +358,8 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
                                                           const float* delta) {
   constexpr int KS = D / 16, MD = D / 32;
   using B = BT<D>;
-  constexpr int qTile = B::bytes(32);              // one Q or dout tile (32 queries)
+  using SQT = ST<D>;
+  constexpr int qTile = SQT::bytes(32);            // one Q or dout tile (32 queries, swizzled)
   // Q, dout, then lse, delta, positions, segments (256 bytes each: a 64-lane
   // load writes its 32 values and 32 zeros).
   constexpr int pairBytes = 2 * qTile + 4 * 256;
@@ -378,8 +423,12 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
   const int n_steps = (n_pairs + 1) / 2;
   const TileSum ks_sum = ld_const(ksum, kt);
   const int row_bytes = a.heads * D * 2;
-  const int q_rd = qn * B::kStride + hf * 16;
-  const int t_off = tr_lane_off<D>(lane);
+  // A-operand reads of the Q and dout tiles: row qn, chunk 2 ks + hf stored
+  // at (2 ks + hf) ^ swz(qn) = 2 ks ^ (hf ^ swz(qn)).
+  const int q_row = qn * SQT::kStride;
+  const int q_xc = hf ^ SQT::swz(qn);
+  int t_offs[MD][2];
+  swz_tr_offs<D>(lane, t_offs);
 
   // Stage the pair `pair` (query tile, head) into slot `slot` of buffer b:
   // Q and dout rows, lse and delta of the head, positions and segments.
@@ -391,10 +440,11 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
     const i32x4 rq = raw_rsrc(static_cast<const uint16_t*>(a.q) + e0, nrec);
     const i32x4 rg = raw_rsrc(static_cast<const uint16_t*>(a.dout) + e0, nrec);
     const uint32_t base = lds0 + b * stageBytes + slot * pairBytes;
-    for (int i = wave; i < B::loads(32); i += 4) {
-      const int off = padded_off<D>(64 * i + lane, n_rows, row_bytes);
-      lds_dma<16>(rq, base + 1024 * i, off);
-      lds_dma<16>(rg, base + qTile + 1024 * i, off);
+    for (int i = wave; i < SQT::loads(32); i += 4) {
+      const int off = swz_off<D>(64 * i + lane, n_rows, row_bytes);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(base + 1024 * i);
+      lds_dma<16>(rq, dst, off);
+      lds_dma<16>(rg, dst + qTile, off);
     }
     if (wave == 0 || wave == 1) {
       // lse or delta of head h for the 32 queries (stride heads floats).
@@ -445,8 +495,9 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
         auto ld_ks = [&](auto kc) {
           constexpr int ks = decltype(kc)::value;
           bf16x8* o = ra[ks % 3];
-          o[0] = lds_ld<bf16x8>(qb + q_rd + ks * 32);
-          o[1] = lds_ld<bf16x8>(gb + q_rd + ks * 32);
+          const int qo = q_row + (((2 * ks) ^ q_xc) << 4);
+          o[0] = lds_ld<bf16x8>(qb + qo);
+          o[1] = lds_ld<bf16x8>(gb + qo);
           o[2] = lds_ld<bf16x8>(smem + kv_rd + ks * 32);
           o[3] = lds_ld<bf16x8>(smem + kv_rd + kvTile + ks * 32);
         };
@@ -502,7 +553,7 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
         bf16x8 rt[4];
         auto tr_j = [&](auto jc) {
           constexpr int j = decltype(jc)::value, kk = j / (2 * MD), md = (j / 2) % MD;
-          rt[j & 3] = tr_operand<D>((j & 1) ? qb : gb, t_off, kk, md);
+          rt[j & 3] = swz_tr_operand<D>((j & 1) ? qb : gb, t_offs, kk, md);
         };
         tr_j(std::integral_constant<int, 0>{});
         tr_j(std::integral_constant<int, 1>{});
