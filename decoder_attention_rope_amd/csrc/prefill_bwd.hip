@@ -348,14 +348,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: one workgroup per key tile and KV head. Wave w owns keys
-// 32 (w & 1) .. +31 of the tile and the (query tile, head) pairs of parity
-// w >> 1; pairs are visited two at a time, both staged in LDS.
+// dK / dV: one workgroup per key tile and KV head, 8 wavefronts. Wave w owns
+// keys 32 (w & 1) .. +31 of the tile, the (query tile, head) pairs of parity
+// (w >> 1) & 1, and one of the two sums: dV (w < 4: S, P, dV^T += dO^T P) or
+// dK (w >= 4: S, dP, dS, dK^T += Q^T dS). Each wave holds one accumulator set,
+// so two waves share a SIMD; the dV waves recompute S. Pairs are visited two
+// at a time, both staged in LDS.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs a, Plan qp, const TileSum* ksum,
-                                                          const int2* krange, const int* korder,
-                                                          const float* delta) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, const TileSum* ksum,
+                                                         const int2* krange, const int* korder,
+                                                         const float* delta) {
   constexpr int KS = D / 16, MD = D / 32;
   using B = BT<D>;
   using SQT = ST<D>;
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
   // load writes its 32 values and 32 zeros).
   constexpr int pairBytes = 2 * qTile + 4 * 256;
   constexpr int stageBytes = 2 * pairBytes;
-  constexpr int combineBytes = 2 * 2 * MD * 16 * 64 * 4;
+  constexpr int combineBytes = 4 * MD * 16 * 64 * 4;
   // The key tile's K and V rows (64 each, padded), after the stages: read as
   // the B operands of S and dP every step instead of held in registers.
   constexpr int kvOff = 2 * stageBytes;
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
   const int kh = blockIdx.x % a.kv_heads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kb = wave & 1, hp = wave >> 1;
+  const int kb = wave & 1, hp = (wave >> 1) & 1;
   const int qn = lane & 31, hf = lane >> 5;
   const int P = a.p, G = a.heads / a.kv_heads;
   const int key = kt * kBK + 32 * kb + qn;
@@ -399,24 +402,17 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
     const int nrec = (n_rows - 1) * rb + 2 * D;
     const i32x4 rk = raw_rsrc(static_cast<const uint16_t*>(a.k) + e0, nrec);
     const i32x4 rv = raw_rsrc(static_cast<const uint16_t*>(a.v) + e0, nrec);
-    for (int i = wave; i < B::loads(64); i += 4) {
+    for (int i = wave; i < B::loads(64); i += 8) {
       const int p = 64 * i + lane;
       const int row = p / B::kChunks, ch = p - row * B::kChunks;
       const int off = (ch == D / 8 || row >= n_rows) ? 0x40000000 : row * rb + ch * 16;
-      lds_dma<16>(rk, lds0 + kvOff + 1024 * i, off);
-      lds_dma<16>(rv, lds0 + kvOff + kvTile + 1024 * i, off);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + kvOff + 1024 * i);
+      lds_dma<16>(rk, dst, off);
+      lds_dma<16>(rv, dst + kvTile, off);
     }
   }
   // This lane's B-operand reads: key 32 kb + qn, dimensions 16 ks + 8 hf ...
   const int kv_rd = kvOff + (32 * kb + qn) * B::kStride + hf * 16;
-  f32x16 dk[MD], dv[MD];
-#pragma unroll
-  for (int md = 0; md < MD; ++md)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[md][r] = 0.f;
-      dv[md][r] = 0.f;
-    }
 
   const int2 rng = make_int2(__builtin_amdgcn_readfirstlane(krange[kt].x), __builtin_amdgcn_readfirstlane(krange[kt].y));
   const int n_pairs = rng.y >= rng.x ? (rng.y - rng.x + 1) * G : 0;
@@ -440,177 +436,184 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
     const i32x4 rq = raw_rsrc(static_cast<const uint16_t*>(a.q) + e0, nrec);
     const i32x4 rg = raw_rsrc(static_cast<const uint16_t*>(a.dout) + e0, nrec);
     const uint32_t base = lds0 + b * stageBytes + slot * pairBytes;
-    for (int i = wave; i < SQT::loads(32); i += 4) {
+    for (int i = wave; i < SQT::loads(32); i += 8) {
       const int off = swz_off<D>(64 * i + lane, n_rows, row_bytes);
       const uint32_t dst = __builtin_amdgcn_readfirstlane(base + 1024 * i);
       lds_dma<16>(rq, dst, off);
       lds_dma<16>(rg, dst + qTile, off);
     }
-    if (wave == 0 || wave == 1) {
-      // lse or delta of head h for the 32 queries (stride heads floats).
-      const float* src = wave == 0 ? a.lse : delta;
+    // Waves 4..7: lse, delta (stride heads floats), positions, segments.
+    const int mw = wave - 4;
+    const uint32_t mdst = __builtin_amdgcn_readfirstlane(base + 2 * qTile + 256 * (mw & 3));
+    if (mw == 0 || mw == 1) {
+      const float* src = mw == 0 ? a.lse : delta;
       const i32x4 r = raw_rsrc(src + (long long)qt * 32 * a.heads + h, 4 * ((n_rows - 1) * a.heads + 1));
-      lds_dma<4>(r, base + 2 * qTile + 256 * wave, lane < 32 ? lane * a.heads * 4 : 0x40000000);
-    } else {
-      const int32_t* src = wave == 2 ? a.positions : a.segments;
+      lds_dma<4>(r, mdst, lane < 32 ? lane * a.heads * 4 : 0x40000000);
+    } else if (mw == 2 || mw == 3) {
+      const int32_t* src = mw == 2 ? a.positions : a.segments;
       const i32x4 r = raw_rsrc(src + (long long)qt * 32, 4 * n_rows);
-      lds_dma<4>(r, base + 2 * qTile + 256 * wave, lane < 32 ? lane * 4 : 0x40000000);
+      lds_dma<4>(r, mdst, lane < 32 ? lane * 4 : 0x40000000);
     }
   };
 
-  // A step's second slot past the last pair stages that last pair again
-  // (finite data; its products are masked to zero), so every step runs the
-  // same straight-line body and the accumulators stay in place.
-  if (n_steps > 0) {
-    load_pair(0, 0, 0);
-    load_pair(min(1, n_pairs - 1), 1, 0);
-    wait_all_loads();
-    wg_barrier();
-  }
-  for (int step = 0; step < n_steps; ++step) {
-    const int b = step & 1;
-    if (step + 1 < n_steps) {
-      load_pair(2 * step + 2, 0, b ^ 1);
-      load_pair(min(2 * step + 3, n_pairs - 1), 1, b ^ 1);
+  // ROLE 0: dV; ROLE 1: dK. The step body is the same for both up to S; the
+  // dK waves also form dP and dS.
+  auto run = [&](auto role_c) {
+    constexpr int ROLE = decltype(role_c)::value;
+    f32x16 acc[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[md][r] = 0.f;
+
+    // A step's second slot past the last pair stages that last pair again
+    // (finite data; its products are masked to zero), so every step runs the
+    // same straight-line body and the accumulators stay in place.
+    if (n_steps > 0) {
+      load_pair(0, 0, 0);
+      load_pair(min(1, n_pairs - 1), 1, 0);
+      wait_all_loads();
+      wg_barrier();
     }
-    const int pair = 2 * step + hp;
-    const int qt = rng.x + min(pair, n_pairs - 1) / G;
-    {
+    for (int step = 0; step < n_steps; ++step) {
+      const int b = step & 1;
+      if (step + 1 < n_steps) {
+        load_pair(2 * step + 2, 0, b ^ 1);
+        load_pair(min(2 * step + 3, n_pairs - 1), 1, b ^ 1);
+      }
+      const int pair = 2 * step + hp;
+      const int qt = rng.x + min(pair, n_pairs - 1) / G;
       const TileSum q_sum = ld_const(qp.qsum, qt);
       // A pair that cannot meet the key tile (or lies past the last pair)
       // contributes zeros.
       const bool meet = pair < n_pairs && tiles_meet(q_sum, ks_sum, a.window);
-      {
-        const bool full = meet && tiles_full(q_sum, ks_sum, kt, P, a.window) && (qt + 1) * 32 <= P;
-        const LdsByte* pbase = smem + b * stageBytes + hp * pairBytes;
-        const LdsByte* qb = pbase;
-        const LdsByte* gb = pbase + qTile;
-        const LdsByte* misc = pbase + 2 * qTile;  // lse, delta, positions, segments
-        // S = Q K^T and dP = dO V^T; the four operands of a k-step are read
-        // from LDS two k-steps ahead of its MFMAs (a ring of three sets), and
-        // a scheduling fence keeps that order, so LDS latency hides behind
-        // the MFMAs of the steps in between.
-        f32x16 s = {}, dp = {};
-        bf16x8 ra[3][4];
-        auto ld_ks = [&](auto kc) {
-          constexpr int ks = decltype(kc)::value;
-          bf16x8* o = ra[ks % 3];
-          const int qo = q_row + (((2 * ks) ^ q_xc) << 4);
-          o[0] = lds_ld<bf16x8>(qb + qo);
-          o[1] = lds_ld<bf16x8>(gb + qo);
-          o[2] = lds_ld<bf16x8>(smem + kv_rd + ks * 32);
+      const bool full = meet && tiles_full(q_sum, ks_sum, kt, P, a.window) && (qt + 1) * 32 <= P;
+      const LdsByte* pbase = smem + b * stageBytes + hp * pairBytes;
+      const LdsByte* qb = pbase;
+      const LdsByte* gb = pbase + qTile;
+      const LdsByte* misc = pbase + 2 * qTile;  // lse, delta, positions, segments
+      // S = Q K^T (and dP = dO V^T for dK); the operands of a k-step are read
+      // from LDS two k-steps ahead of its MFMAs (a ring of three sets), and a
+      // scheduling fence keeps that order, so LDS latency hides behind the
+      // MFMAs of the steps in between.
+      constexpr int NO = ROLE ? 4 : 2;
+      f32x16 s = {}, dp = {};
+      bf16x8 ra[3][NO];
+      auto ld_ks = [&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        bf16x8* o = ra[ks % 3];
+        const int qo = q_row + (((2 * ks) ^ q_xc) << 4);
+        o[0] = lds_ld<bf16x8>(qb + qo);
+        o[1] = lds_ld<bf16x8>(smem + kv_rd + ks * 32);
+        if constexpr (ROLE) {
+          o[2] = lds_ld<bf16x8>(gb + qo);
           o[3] = lds_ld<bf16x8>(smem + kv_rd + kvTile + ks * 32);
-        };
-        ld_ks(std::integral_constant<int, 0>{});
-        if constexpr (KS > 1) ld_ks(std::integral_constant<int, 1>{});
-        static_for<KS>([&](auto kc) {
-          constexpr int ks = decltype(kc)::value;
-          if constexpr (ks + 2 < KS) ld_ks(std::integral_constant<int, ks + 2>{});
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][0], ra[ks % 3][2], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][1], ra[ks % 3][3], dp, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        });
-        // Register r of this lane holds query iq = 16 (r / 8) + 8 hf + r % 8
-        // of the tile and this lane's key; lse and delta of those queries
-        // come as four 16-byte reads each.
-        const int n_q = P - qt * 32;
-        float lse_r[16], dl_r[16];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
-          const u32x4 lw = lds_ld<u32x4>(misc + iq0 * 4), dw = lds_ld<u32x4>(misc + 256 + iq0 * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            lse_r[4 * c + e] = __uint_as_float(lw[e]);
-            dl_r[4 * c + e] = __uint_as_float(dw[e]);
-          }
         }
-        u32x4 pp[2], pds[2];
+      };
+      ld_ks(std::integral_constant<int, 0>{});
+      if constexpr (KS > 1) ld_ks(std::integral_constant<int, 1>{});
+      static_for<KS>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        if constexpr (ks + 2 < KS) ld_ks(std::integral_constant<int, ks + 2>{});
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][0], ra[ks % 3][1], s, 0, 0, 0);
+        if constexpr (ROLE)
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][2], ra[ks % 3][3], dp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // Register r of this lane holds query iq = 16 (r / 8) + 8 hf + r % 8
+      // of the tile and this lane's key; lse (and delta) of those queries
+      // come as four 16-byte reads each.
+      const int n_q = P - qt * 32;
+      float lse_r[16], dl_r[16];
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float p2[2], d2[2];
+      for (int c = 0; c < 4; ++c) {
+        const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
+        const u32x4 lw = lds_ld<u32x4>(misc + iq0 * 4);
+        u32x4 dw = {};
+        if constexpr (ROLE) dw = lds_ld<u32x4>(misc + 256 + iq0 * 4);
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
-            const float l2 = lse_r[r + e] * kLog2eB;
-            const float dl = dl_r[r + e];
-            bool ok = k_valid & meet;
-            if (!full) {
-              const int qp_ = lds_ld<int>(misc + 512 + iq * 4), qs = lds_ld<int>(misc + 768 + iq * 4);
-              ok = ok & (qs == seg_k) & ((uint32_t)qp_ - (uint32_t)pos_k < wlim) & (iq < n_q);
-            }
-            const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
-            p2[e] = p;
-            d2[e] = ok ? p * (dp[r + e] - dl) : 0.f;
-          }
-          pp[r >> 3][(r & 7) >> 1] = pack_bf16x2(p2[0], p2[1]);
-          pds[r >> 3][(r & 7) >> 1] = pack_bf16x2(d2[0], d2[1]);
+        for (int e = 0; e < 4; ++e) {
+          lse_r[4 * c + e] = __uint_as_float(lw[e]);
+          dl_r[4 * c + e] = __uint_as_float(dw[e]);
         }
-        // dV^T += dO^T P and dK^T += Q^T dS: MFMA j (kk = j / 2 MD, md =
-        // (j / 2) % MD, dV for even j, dK for odd) takes its transposed
-        // operand from a ring of four read three MFMAs ahead.
-        constexpr int NJ = 4 * MD;
-        bf16x8 rt[4];
-        auto tr_j = [&](auto jc) {
-          constexpr int j = decltype(jc)::value, kk = j / (2 * MD), md = (j / 2) % MD;
-          rt[j & 3] = swz_tr_operand<D>((j & 1) ? qb : gb, t_offs, kk, md);
-        };
-        tr_j(std::integral_constant<int, 0>{});
-        tr_j(std::integral_constant<int, 1>{});
-        tr_j(std::integral_constant<int, 2>{});
-        static_for<NJ>([&](auto jc) {
-          constexpr int j = decltype(jc)::value, kk = j / (2 * MD), md = (j / 2) % MD;
-          if constexpr (j + 3 < NJ) tr_j(std::integral_constant<int, j + 3>{});
-          if constexpr (j & 1)
-            dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rt[j & 3], __builtin_bit_cast(bf16x8, pds[kk]), dk[md], 0, 0, 0);
-          else
-            dv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rt[j & 3], __builtin_bit_cast(bf16x8, pp[kk]), dv[md], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        });
       }
+      // The B operand of this role's sum: P for dV, dS for dK (bf16, two
+      // 16-query halves).
+      u32x4 pb[2];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float v2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
+          const float l2 = lse_r[r + e] * kLog2eB;
+          bool ok = k_valid & meet;
+          if (!full) {
+            const int qp_ = lds_ld<int>(misc + 512 + iq * 4), qs = lds_ld<int>(misc + 768 + iq * 4);
+            ok = ok & (qs == seg_k) & ((uint32_t)qp_ - (uint32_t)pos_k < wlim) & (iq < n_q);
+          }
+          const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
+          if constexpr (ROLE) v2[e] = ok ? p * (dp[r + e] - dl_r[r + e]) : 0.f;
+          else v2[e] = p;
+        }
+        pb[r >> 3][(r & 7) >> 1] = pack_bf16x2(v2[0], v2[1]);
+      }
+      // dV^T += dO^T P (ROLE 0) or dK^T += Q^T dS (ROLE 1): MFMA j (kk = j /
+      // MD, md = j % MD) takes its transposed operand from a ring of four
+      // read three MFMAs ahead.
+      constexpr int NJ = 2 * MD;
+      const LdsByte* tb = ROLE ? qb : gb;
+      bf16x8 rt[4];
+      auto tr_j = [&](auto jc) {
+        constexpr int j = decltype(jc)::value, kk = j / MD, md = j % MD;
+        rt[j & 3] = swz_tr_operand<D>(tb, t_offs, kk, md);
+      };
+      tr_j(std::integral_constant<int, 0>{});
+      tr_j(std::integral_constant<int, 1>{});
+      tr_j(std::integral_constant<int, 2>{});
+      static_for<NJ>([&](auto jc) {
+        constexpr int j = decltype(jc)::value, kk = j / MD, md = j % MD;
+        if constexpr (j + 3 < NJ) tr_j(std::integral_constant<int, j + 3>{});
+        acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rt[j & 3], __builtin_bit_cast(bf16x8, pb[kk]), acc[md], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      wait_all_loads();
+      wg_barrier();
     }
     wait_all_loads();
     wg_barrier();
-  }
-  wait_all_loads();
-  wg_barrier();
 
-  // The two wavefronts of a key half add their sums: the odd-pair ones put
-  // theirs in LDS, the even-pair ones read, add and write.
-  LdsByte* cb = smem + kb * (2 * MD * 16 * 64 * 4);
-  if (hp == 1) {
+    // The two parity wavefronts of a (key half, role) add their sums: the
+    // odd-pair one puts its sum in LDS, the even-pair one reads, adds and
+    // writes (dK scaled).
+    LdsByte* cb = smem + (2 * ROLE + kb) * (MD * 16 * 64 * 4);
+    if (hp == 1) {
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
+      for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        lds_st(cb + ((md * 16 + r) * 64 + lane) * 4, dk[md][r]);
-        lds_st(cb + (((MD + md) * 16 + r) * 64 + lane) * 4, dv[md][r]);
-      }
-  }
-  wg_barrier();
-  if (hp == 0 && k_valid) {
+        for (int r = 0; r < 16; ++r) lds_st(cb + ((md * 16 + r) * 64 + lane) * 4, acc[md][r]);
+    }
+    wg_barrier();
+    if (hp == 0 && k_valid) {
+      const float f = ROLE ? a.scale : 1.f;
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
+      for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dk[md][r] += lds_ld<float>(cb + ((md * 16 + r) * 64 + lane) * 4);
-        dv[md][r] += lds_ld<float>(cb + (((MD + md) * 16 + r) * 64 + lane) * 4);
-      }
-    uint16_t* dkg = static_cast<uint16_t*>(a.dk) + ((long long)key * a.kv_heads + kh) * D;
-    uint16_t* dvg = static_cast<uint16_t*>(a.dv) + ((long long)key * a.kv_heads + kh) * D;
+        for (int r = 0; r < 16; ++r) acc[md][r] = (acc[md][r] + lds_ld<float>(cb + ((md * 16 + r) * 64 + lane) * 4)) * f;
+      uint16_t* og = static_cast<uint16_t*>(ROLE ? a.dk : a.dv) + ((long long)key * a.kv_heads + kh) * D;
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
+      for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 wk, wv;
-        wk[0] = pack_bf16x2(dk[md][4 * g] * a.scale, dk[md][4 * g + 1] * a.scale);
-        wk[1] = pack_bf16x2(dk[md][4 * g + 2] * a.scale, dk[md][4 * g + 3] * a.scale);
-        wv[0] = pack_bf16x2(dv[md][4 * g], dv[md][4 * g + 1]);
-        wv[1] = pack_bf16x2(dv[md][4 * g + 2], dv[md][4 * g + 3]);
-        *reinterpret_cast<u32x2*>(dkg + 32 * md + 8 * g + 4 * hf) = wk;
-        *reinterpret_cast<u32x2*>(dvg + 32 * md + 8 * g + 4 * hf) = wv;
-      }
-  }
+        for (int g = 0; g < 4; ++g) {
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[md][4 * g], acc[md][4 * g + 1]);
+          w[1] = pack_bf16x2(acc[md][4 * g + 2], acc[md][4 * g + 3]);
+          *reinterpret_cast<u32x2*>(og + 32 * md + 8 * g + 4 * hf) = w;
+        }
+    }
+  };
+  if (wave >= 4) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 0>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -633,7 +636,7 @@ static hipError_t launch_bwd_main(const BwdArgs& a, const Plan& pl, const Plan& 
   else bwd_dq_kernel<D, 1><<<gq, blk, 0, stream>>>(a, pl, delta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_dkdv_kernel<D><<<dim3(pl.n_kt * a.kv_heads), blk, 0, stream>>>(a, qp, pl.ksum, krange, korder, delta);
+  bwd_dkdv_kernel<D><<<dim3(pl.n_kt * a.kv_heads), dim3(512), 0, stream>>>(a, qp, pl.ksum, krange, korder, delta);
   return hipGetLastError();
 }
 
