@@ -300,22 +300,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, gf[ks]), dp, 0, 0, 0);
       }
       // Register r of this lane holds key j = 32 hb + 16 (r / 8) + 8 hf + r % 8.
+      // Keys come in runs of four: their positions and segments are read
+      // 16 bytes at a time (a masked tile only).
       u32x4 dsw[2];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float ds2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int j = 32 * hb + 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
-          bool ok = true;
-          if (!full) {
-            const int kp = lds_ld<int>(pb + j * 4), ksg = lds_ld<int>(pb + 256 + j * 4);
-            ok = (ksg == my_seg) & ((uint32_t)my_pos - (uint32_t)kp < wlim) & (j < n_j);
-          }
-          const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -lse2)) : 0.f;
-          ds2[e] = p * (dp[r + e] - dlt);
+      for (int r4 = 0; r4 < 16; r4 += 4) {
+        const int j0 = 32 * hb + 16 * (r4 >> 3) + 8 * hf + (r4 & 7);
+        u32x4 kpw = {}, ksw = {};
+        if (!full) {
+          kpw = lds_ld<u32x4>(pb + j0 * 4);
+          ksw = lds_ld<u32x4>(pb + 256 + j0 * 4);
         }
-        dsw[r >> 3][(r & 7) >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+#pragma unroll
+        for (int r = r4; r < r4 + 4; r += 2) {
+          float ds2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int j = j0 + (r + e - r4);
+            bool ok = true;
+            if (!full)
+              ok = ((int)ksw[r + e - r4] == my_seg) & ((uint32_t)my_pos - kpw[r + e - r4] < wlim) & (j < n_j);
+            const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -lse2)) : 0.f;
+            ds2[e] = p * (dp[r + e] - dlt);
+          }
+          dsw[r >> 3][(r & 7) >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+        }
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
@@ -537,6 +546,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
           dl_r[4 * c + e] = __uint_as_float(dw[e]);
         }
       }
+      // Positions and segments of the same queries, for a masked pair.
+      int qpos_r[16], qseg_r[16];
+      if (!full) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
+          const u32x4 pw = lds_ld<u32x4>(misc + 512 + iq0 * 4), sw = lds_ld<u32x4>(misc + 768 + iq0 * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            qpos_r[4 * c + e] = (int)pw[e];
+            qseg_r[4 * c + e] = (int)sw[e];
+          }
+        }
+      }
       // The B operand of this role's sum: P for dV, dS for dK (bf16, two
       // 16-query halves).
       u32x4 pb[2];
@@ -548,10 +571,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
           const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
           const float l2 = lse_r[r + e] * kLog2eB;
           bool ok = k_valid & meet;
-          if (!full) {
-            const int qp_ = lds_ld<int>(misc + 512 + iq * 4), qs = lds_ld<int>(misc + 768 + iq * 4);
-            ok = ok & (qs == seg_k) & ((uint32_t)qp_ - (uint32_t)pos_k < wlim) & (iq < n_q);
-          }
+          if (!full)
+            ok = ok & (qseg_r[r + e] == seg_k) & ((uint32_t)qpos_r[r + e] - (uint32_t)pos_k < wlim) & (iq < n_q);
           const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
           if constexpr (ROLE) v2[e] = ok ? p * (dp[r + e] - dl_r[r + e]) : 0.f;
           else v2[e] = p;
