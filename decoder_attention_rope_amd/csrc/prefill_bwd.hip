@@ -359,10 +359,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
 // ---------------------------------------------------------------------------
 // dK / dV: one workgroup per key tile and KV head, 8 wavefronts. Wave w owns
 // keys 32 (w & 1) .. +31 of the tile, the (query tile, head) pairs of parity
-// (w >> 1) & 1, and one of the two sums: dV (w < 4: S, P, dV^T += dO^T P) or
-// dK (w >= 4: S, dP, dS, dK^T += Q^T dS). Each wave holds one accumulator set,
-// so two waves share a SIMD; the dV waves recompute S. Pairs are visited two
-// at a time, both staged in LDS.
+// (w >> 1) & 1, and one of the two sums: dK (w >= 4: S, dP, P, dS,
+// dK^T += Q^T dS) or dV (w < 4: dV^T += dO^T P, with P passed through LDS by
+// the dK wave of the same keys and pairs, one step later). Each wave holds
+// one accumulator set, so two waves share a SIMD. Pairs are visited two at a
+// time, both staged in LDS (a ring of three stages).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, const TileSum* ksum,
@@ -379,9 +380,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
   constexpr int combineBytes = 4 * MD * 16 * 64 * 4;
   // The key tile's K and V rows (64 each, padded), after the stages: read as
   // the B operands of S and dP every step instead of held in registers.
-  constexpr int kvOff = 2 * stageBytes;
+  constexpr int kvOff = 3 * stageBytes;
   constexpr int kvTile = B::bytes(64);
-  constexpr int ldsBytes = kvOff + 2 * kvTile > combineBytes ? kvOff + 2 * kvTile : combineBytes;
+  // Then P of the dK waves for the dV waves: two buffers of 4 slots (key
+  // half, pair parity) of 64 lanes x 32 bytes.
+  constexpr int pOff = kvOff + 2 * kvTile;
+  constexpr int pBufBytes = 4 * 64 * 32;
+  constexpr int ldsBytes = pOff + 2 * pBufBytes > combineBytes ? pOff + 2 * pBufBytes : combineBytes;
   __shared__ __attribute__((aligned(16))) char smem_raw[ldsBytes];
   LdsByte* smem = (LdsByte*)smem_raw;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
@@ -465,8 +470,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
     }
   };
 
-  // ROLE 0: dV; ROLE 1: dK. The step body is the same for both up to S; the
-  // dK waves also form dP and dS.
+  // ROLE 1 (dK waves): S, dP, P, dS and dK^T += Q^T dS for the pair of this
+  // step; P goes to LDS. ROLE 0 (dV waves): one step behind, dV^T += dO^T P
+  // with P read back and dO^T from the previous step's stage.
   auto run = [&](auto role_c) {
     constexpr int ROLE = decltype(role_c)::value;
     f32x16 acc[MD];
@@ -475,115 +481,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[md][r] = 0.f;
 
-    // A step's second slot past the last pair stages that last pair again
-    // (finite data; its products are masked to zero), so every step runs the
-    // same straight-line body and the accumulators stay in place.
-    if (n_steps > 0) {
-      load_pair(0, 0, 0);
-      load_pair(min(1, n_pairs - 1), 1, 0);
-      wait_all_loads();
-      wg_barrier();
-    }
-    for (int step = 0; step < n_steps; ++step) {
-      const int b = step & 1;
-      if (step + 1 < n_steps) {
-        load_pair(2 * step + 2, 0, b ^ 1);
-        load_pair(min(2 * step + 3, n_pairs - 1), 1, b ^ 1);
-      }
-      const int pair = 2 * step + hp;
-      const int qt = rng.x + min(pair, n_pairs - 1) / G;
-      const TileSum q_sum = ld_const(qp.qsum, qt);
-      // A pair that cannot meet the key tile (or lies past the last pair)
-      // contributes zeros.
-      const bool meet = pair < n_pairs && tiles_meet(q_sum, ks_sum, a.window);
-      const bool full = meet && tiles_full(q_sum, ks_sum, kt, P, a.window) && (qt + 1) * 32 <= P;
-      const LdsByte* pbase = smem + b * stageBytes + hp * pairBytes;
-      const LdsByte* qb = pbase;
-      const LdsByte* gb = pbase + qTile;
-      const LdsByte* misc = pbase + 2 * qTile;  // lse, delta, positions, segments
-      // S = Q K^T (and dP = dO V^T for dK); the operands of a k-step are read
-      // from LDS two k-steps ahead of its MFMAs (a ring of three sets), and a
-      // scheduling fence keeps that order, so LDS latency hides behind the
-      // MFMAs of the steps in between.
-      constexpr int NO = ROLE ? 4 : 2;
-      f32x16 s = {}, dp = {};
-      bf16x8 ra[3][NO];
-      auto ld_ks = [&](auto kc) {
-        constexpr int ks = decltype(kc)::value;
-        bf16x8* o = ra[ks % 3];
-        const int qo = q_row + (((2 * ks) ^ q_xc) << 4);
-        o[0] = lds_ld<bf16x8>(qb + qo);
-        o[1] = lds_ld<bf16x8>(smem + kv_rd + ks * 32);
-        if constexpr (ROLE) {
-          o[2] = lds_ld<bf16x8>(gb + qo);
-          o[3] = lds_ld<bf16x8>(smem + kv_rd + kvTile + ks * 32);
-        }
-      };
-      ld_ks(std::integral_constant<int, 0>{});
-      if constexpr (KS > 1) ld_ks(std::integral_constant<int, 1>{});
-      static_for<KS>([&](auto kc) {
-        constexpr int ks = decltype(kc)::value;
-        if constexpr (ks + 2 < KS) ld_ks(std::integral_constant<int, ks + 2>{});
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][0], ra[ks % 3][1], s, 0, 0, 0);
-        if constexpr (ROLE)
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][2], ra[ks % 3][3], dp, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      // Register r of this lane holds query iq = 16 (r / 8) + 8 hf + r % 8
-      // of the tile and this lane's key; lse (and delta) of those queries
-      // come as four 16-byte reads each.
-      const int n_q = P - qt * 32;
-      float lse_r[16], dl_r[16];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
-        const u32x4 lw = lds_ld<u32x4>(misc + iq0 * 4);
-        u32x4 dw = {};
-        if constexpr (ROLE) dw = lds_ld<u32x4>(misc + 256 + iq0 * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lse_r[4 * c + e] = __uint_as_float(lw[e]);
-          dl_r[4 * c + e] = __uint_as_float(dw[e]);
-        }
-      }
-      // Positions and segments of the same queries, for a masked pair.
-      int qpos_r[16], qseg_r[16];
-      if (!full) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
-          const u32x4 pw = lds_ld<u32x4>(misc + 512 + iq0 * 4), sw = lds_ld<u32x4>(misc + 768 + iq0 * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            qpos_r[4 * c + e] = (int)pw[e];
-            qseg_r[4 * c + e] = (int)sw[e];
-          }
-        }
-      }
-      // The B operand of this role's sum: P for dV, dS for dK (bf16, two
-      // 16-query halves).
-      u32x4 pb[2];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float v2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
-          const float l2 = lse_r[r + e] * kLog2eB;
-          bool ok = k_valid & meet;
-          if (!full)
-            ok = ok & (qseg_r[r + e] == seg_k) & ((uint32_t)qpos_r[r + e] - (uint32_t)pos_k < wlim) & (iq < n_q);
-          const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
-          if constexpr (ROLE) v2[e] = ok ? p * (dp[r + e] - dl_r[r + e]) : 0.f;
-          else v2[e] = p;
-        }
-        pb[r >> 3][(r & 7) >> 1] = pack_bf16x2(v2[0], v2[1]);
-      }
-      // dV^T += dO^T P (ROLE 0) or dK^T += Q^T dS (ROLE 1): MFMA j (kk = j /
-      // MD, md = j % MD) takes its transposed operand from a ring of four
-      // read three MFMAs ahead.
+    // acc += T^T X over the 32 queries of a pair: MFMA j (kk = j / MD, md =
+    // j % MD) takes its transposed operand (T^T, from the tile at tb) from a
+    // ring of four read three MFMAs ahead; X (P or dS, bf16) is in registers.
+    auto acc_mfma = [&](const LdsByte* tb, const u32x4 (&x)[2]) {
       constexpr int NJ = 2 * MD;
-      const LdsByte* tb = ROLE ? qb : gb;
       bf16x8 rt[4];
       auto tr_j = [&](auto jc) {
         constexpr int j = decltype(jc)::value, kk = j / MD, md = j % MD;
@@ -595,11 +497,142 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
       static_for<NJ>([&](auto jc) {
         constexpr int j = decltype(jc)::value, kk = j / MD, md = j % MD;
         if constexpr (j + 3 < NJ) tr_j(std::integral_constant<int, j + 3>{});
-        acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rt[j & 3], __builtin_bit_cast(bf16x8, pb[kk]), acc[md], 0, 0, 0);
+        acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rt[j & 3], __builtin_bit_cast(bf16x8, x[kk]), acc[md], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       });
+    };
+    // This lane's 32 bytes of P in slot (kb, hp) of P buffer pbuf.
+    auto p_slot = [&](int pbuf) { return pOff + pbuf * pBufBytes + ((2 * hp + kb) * 64 + lane) * 32; };
+
+    // Stages form a ring of three: step s reads stage s % 3 (the dV waves
+    // stage (s - 1) % 3), while the pairs of step s + 1 load into stage
+    // (s + 1) % 3, last read in step s - 1. P of step s goes to P buffer
+    // s % 2, read in step s + 1. A step's second slot past the last pair
+    // stages that last pair again (finite data; its products are masked to
+    // zero), so every step runs the same straight-line body and the
+    // accumulators stay in place.
+    if (n_steps > 0) {
+      load_pair(0, 0, 0);
+      load_pair(min(1, n_pairs - 1), 1, 0);
       wait_all_loads();
       wg_barrier();
+    }
+    int b = 0;  // stage of this step
+    for (int step = 0; step < n_steps; ++step) {
+      const int bn = b == 2 ? 0 : b + 1, bp = b == 0 ? 2 : b - 1;
+      if (step + 1 < n_steps) {
+        load_pair(2 * step + 2, 0, bn);
+        load_pair(min(2 * step + 3, n_pairs - 1), 1, bn);
+      }
+      if constexpr (ROLE) {
+        const int pair = 2 * step + hp;
+        const int qt = rng.x + min(pair, n_pairs - 1) / G;
+        const TileSum q_sum = ld_const(qp.qsum, qt);
+        // A pair that cannot meet the key tile (or lies past the last pair)
+        // contributes zeros.
+        const bool meet = pair < n_pairs && tiles_meet(q_sum, ks_sum, a.window);
+        const bool full = meet && tiles_full(q_sum, ks_sum, kt, P, a.window) && (qt + 1) * 32 <= P;
+        const LdsByte* pbase = smem + b * stageBytes + hp * pairBytes;
+        const LdsByte* qb = pbase;
+        const LdsByte* gb = pbase + qTile;
+        const LdsByte* misc = pbase + 2 * qTile;  // lse, delta, positions, segments
+        // S = Q K^T and dP = dO V^T; the four operands of a k-step are read
+        // from LDS two k-steps ahead of its MFMAs (a ring of three sets), and
+        // a scheduling fence keeps that order, so LDS latency hides behind
+        // the MFMAs of the steps in between.
+        f32x16 s = {}, dp = {};
+        bf16x8 ra[3][4];
+        auto ld_ks = [&](auto kc) {
+          constexpr int ks = decltype(kc)::value;
+          bf16x8* o = ra[ks % 3];
+          const int qo = q_row + (((2 * ks) ^ q_xc) << 4);
+          o[0] = lds_ld<bf16x8>(qb + qo);
+          o[1] = lds_ld<bf16x8>(smem + kv_rd + ks * 32);
+          o[2] = lds_ld<bf16x8>(gb + qo);
+          o[3] = lds_ld<bf16x8>(smem + kv_rd + kvTile + ks * 32);
+        };
+        ld_ks(std::integral_constant<int, 0>{});
+        if constexpr (KS > 1) ld_ks(std::integral_constant<int, 1>{});
+        static_for<KS>([&](auto kc) {
+          constexpr int ks = decltype(kc)::value;
+          if constexpr (ks + 2 < KS) ld_ks(std::integral_constant<int, ks + 2>{});
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][0], ra[ks % 3][1], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][2], ra[ks % 3][3], dp, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        // Register r of this lane holds query iq = 16 (r / 8) + 8 hf + r % 8
+        // of the tile and this lane's key; lse and delta of those queries
+        // come as four 16-byte reads each.
+        const int n_q = P - qt * 32;
+        float lse_r[16], dl_r[16];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
+          const u32x4 lw = lds_ld<u32x4>(misc + iq0 * 4), dw = lds_ld<u32x4>(misc + 256 + iq0 * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lse_r[4 * c + e] = __uint_as_float(lw[e]);
+            dl_r[4 * c + e] = __uint_as_float(dw[e]);
+          }
+        }
+        // Positions and segments of the same queries, for a masked pair.
+        int qpos_r[16], qseg_r[16];
+        if (!full) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
+            const u32x4 pw = lds_ld<u32x4>(misc + 512 + iq0 * 4), sw = lds_ld<u32x4>(misc + 768 + iq0 * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              qpos_r[4 * c + e] = (int)pw[e];
+              qseg_r[4 * c + e] = (int)sw[e];
+            }
+          }
+        }
+        // P and dS in bf16, two 16-query halves each; P goes to LDS for the
+        // dV wave of the same keys and pairs.
+        u32x4 pp[2], pds[2];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float p2[2], d2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
+            const float l2 = lse_r[r + e] * kLog2eB;
+            bool ok = k_valid & meet;
+            if (!full)
+              ok = ok & (qseg_r[r + e] == seg_k) & ((uint32_t)qpos_r[r + e] - (uint32_t)pos_k < wlim) & (iq < n_q);
+            const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
+            p2[e] = p;
+            d2[e] = ok ? p * (dp[r + e] - dl_r[r + e]) : 0.f;
+          }
+          pp[r >> 3][(r & 7) >> 1] = pack_bf16x2(p2[0], p2[1]);
+          pds[r >> 3][(r & 7) >> 1] = pack_bf16x2(d2[0], d2[1]);
+        }
+        const int po = p_slot(step & 1);
+        lds_st(smem + po, pp[0]);
+        lds_st(smem + po + 16, pp[1]);
+        acc_mfma(qb, pds);
+      } else {
+        if (step > 0) {
+          const int po = p_slot((step - 1) & 1);
+          const u32x4 pp[2] = {lds_ld<u32x4>(smem + po), lds_ld<u32x4>(smem + po + 16)};
+          acc_mfma(smem + bp * stageBytes + hp * pairBytes + qTile, pp);
+        }
+      }
+      wait_all_loads();
+      wg_barrier();
+      b = bn;
+    }
+    // The dV waves' last pair (its stage is the last one read: nothing
+    // loads into it any more).
+    if constexpr (!ROLE) {
+      if (n_steps > 0) {
+        const int bp = b == 0 ? 2 : b - 1;
+        const int po = p_slot((n_steps - 1) & 1);
+        const u32x4 pp[2] = {lds_ld<u32x4>(smem + po), lds_ld<u32x4>(smem + po + 16)};
+        acc_mfma(smem + bp * stageBytes + hp * pairBytes + qTile, pp);
+      }
     }
     wait_all_loads();
     wg_barrier();
