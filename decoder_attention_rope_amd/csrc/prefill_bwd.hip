@@ -357,35 +357,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: one workgroup per key tile and KV head, 8 wavefronts. Wave w owns
-// keys 32 (w & 1) .. +31 of the tile, the (query tile, head) pairs of parity
-// (w >> 1) & 1, and one of the two sums: dK (w >= 4: S, dP, P, dS,
-// dK^T += Q^T dS) or dV (w < 4: dV^T += dO^T P, with P passed through LDS by
-// the dK wave of the same keys and pairs, one step later). Each wave holds
-// one accumulator set, so two waves share a SIMD. Pairs are visited two at a
-// time, both staged in LDS (a ring of three stages).
+// dK / dV: one workgroup per key tile and KV head, 8 wavefronts in producer /
+// consumer pairs. Wave w owns keys 32 (w & 1) .. +31 of the tile and the
+// (query tile, head) pairs of parity (w >> 1) & 1. A producer (w >= 4) holds
+// K^T and V^T of its keys in registers and forms S = Q K^T, dP = dO V^T,
+// P and dS = P (dP - delta) for each pair, passing P and dS (bf16) through
+// LDS. Its consumer (w - 4, on the same SIMD) takes them one step later and
+// accumulates dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
+// transposed from that step's stage. Pairs are visited two at a time, both
+// staged in LDS (a ring of three stages).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, const TileSum* ksum,
                                                          const int2* krange, const int* korder,
                                                          const float* delta) {
   constexpr int KS = D / 16, MD = D / 32;
-  using B = BT<D>;
   using SQT = ST<D>;
   constexpr int qTile = SQT::bytes(32);            // one Q or dout tile (32 queries, swizzled)
   // Q, dout, then lse, delta, positions, segments (256 bytes each: a 64-lane
   // load writes its 32 values and 32 zeros).
   constexpr int pairBytes = 2 * qTile + 4 * 256;
   constexpr int stageBytes = 2 * pairBytes;
-  constexpr int combineBytes = 4 * MD * 16 * 64 * 4;
-  // The key tile's K and V rows (64 each, padded), after the stages: read as
-  // the B operands of S and dP every step instead of held in registers.
-  constexpr int kvOff = 3 * stageBytes;
-  constexpr int kvTile = B::bytes(64);
-  // Then P of the dK waves for the dV waves: two buffers of 4 slots (key
-  // half, pair parity) of 64 lanes x 32 bytes.
-  constexpr int pOff = kvOff + 2 * kvTile;
-  constexpr int pBufBytes = 4 * 64 * 32;
+  // After three stages, P and dS of the producers: two buffers of 4 slots
+  // (key half, pair parity) of 64 lanes x 64 bytes (P, then dS).
+  constexpr int pOff = 3 * stageBytes;
+  constexpr int pBufBytes = 4 * 64 * 64;
+  constexpr int combineBytes = 2 * 2 * MD * 16 * 64 * 4;
   constexpr int ldsBytes = pOff + 2 * pBufBytes > combineBytes ? pOff + 2 * pBufBytes : combineBytes;
   __shared__ __attribute__((aligned(16))) char smem_raw[ldsBytes];
   LdsByte* smem = (LdsByte*)smem_raw;
@@ -403,42 +400,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
   const int key = kt * kBK + 32 * kb + qn;
   const bool k_valid = key < P;
   const int key_ld = k_valid ? key : P - 1;
-  const int pos_k = a.positions[key_ld], seg_k = a.segments[key_ld];
-  const uint32_t wlim = a.window > 0 ? (uint32_t)a.window : 0x80000000u;
-  const float scale_log2 = a.scale * kLog2eB;
-
-  // Stage K and V of the key tile: row r of each padded tile holds key
-  // kt * 64 + r at KV head kh (rows past P and the pad chunks read zeros).
-  {
-    const int n_rows = min(kBK, P - kt * kBK);
-    const int rb = a.kv_heads * D * 2;
-    const long long e0 = ((long long)kt * kBK * a.kv_heads + kh) * D;
-    const int nrec = (n_rows - 1) * rb + 2 * D;
-    const i32x4 rk = raw_rsrc(static_cast<const uint16_t*>(a.k) + e0, nrec);
-    const i32x4 rv = raw_rsrc(static_cast<const uint16_t*>(a.v) + e0, nrec);
-    for (int i = wave; i < B::loads(64); i += 8) {
-      const int p = 64 * i + lane;
-      const int row = p / B::kChunks, ch = p - row * B::kChunks;
-      const int off = (ch == D / 8 || row >= n_rows) ? 0x40000000 : row * rb + ch * 16;
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + kvOff + 1024 * i);
-      lds_dma<16>(rk, dst, off);
-      lds_dma<16>(rv, dst + kvTile, off);
-    }
-  }
-  // This lane's B-operand reads: key 32 kb + qn, dimensions 16 ks + 8 hf ...
-  const int kv_rd = kvOff + (32 * kb + qn) * B::kStride + hf * 16;
 
   const int2 rng = make_int2(__builtin_amdgcn_readfirstlane(krange[kt].x), __builtin_amdgcn_readfirstlane(krange[kt].y));
   const int n_pairs = rng.y >= rng.x ? (rng.y - rng.x + 1) * G : 0;
   const int n_steps = (n_pairs + 1) / 2;
-  const TileSum ks_sum = ld_const(ksum, kt);
   const int row_bytes = a.heads * D * 2;
-  // A-operand reads of the Q and dout tiles: row qn, chunk 2 ks + hf stored
-  // at (2 ks + hf) ^ swz(qn) = 2 ks ^ (hf ^ swz(qn)).
-  const int q_row = qn * SQT::kStride;
-  const int q_xc = hf ^ SQT::swz(qn);
-  int t_offs[MD][2];
-  swz_tr_offs<D>(lane, t_offs);
+  // This lane's 64 bytes of P and dS in slot (kb, hp) of buffer pbuf.
+  auto p_slot = [&](int pbuf) { return pOff + pbuf * pBufBytes + ((2 * hp + kb) * 64 + lane) * 64; };
 
   // Stage the pair `pair` (query tile, head) into slot `slot` of buffer b:
   // Q and dout rows, lse and delta of the head, positions and segments.
@@ -470,47 +438,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
     }
   };
 
-  // ROLE 1 (dK waves): S, dP, P, dS and dK^T += Q^T dS for the pair of this
-  // step; P goes to LDS. ROLE 0 (dV waves): one step behind, dV^T += dO^T P
-  // with P read back and dO^T from the previous step's stage.
-  auto run = [&](auto role_c) {
-    constexpr int ROLE = decltype(role_c)::value;
-    f32x16 acc[MD];
+  // Producer: this lane's key as the B operand of S and dP (K^T and V^T
+  // columns, dimensions 16 ks + 8 hf ..).
+  auto produce = [&]() {
+    const int pos_k = a.positions[key_ld], seg_k = a.segments[key_ld];
+    const uint32_t wlim = a.window > 0 ? (uint32_t)a.window : 0x80000000u;
+    const float scale_log2 = a.scale * kLog2eB;
+    const TileSum ks_sum = ld_const(ksum, kt);
+    const uint16_t* kg = static_cast<const uint16_t*>(a.k) + ((long long)key_ld * a.kv_heads + kh) * D;
+    const uint16_t* vg = static_cast<const uint16_t*>(a.v) + ((long long)key_ld * a.kv_heads + kh) * D;
+    u32x4 kf[KS], vf[KS];
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[md][r] = 0.f;
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = load16(kg + ks * 16 + hf * 8);
+      vf[ks] = load16(vg + ks * 16 + hf * 8);
+    }
+    // A-operand reads of the Q and dout tiles: row qn, chunk 2 ks + hf
+    // stored at (2 ks + hf) ^ swz(qn) = 2 ks ^ (hf ^ swz(qn)).
+    const int q_row = qn * SQT::kStride;
+    const int q_xc = hf ^ SQT::swz(qn);
 
-    // acc += T^T X over the 32 queries of a pair: MFMA j (kk = j / MD, md =
-    // j % MD) takes its transposed operand (T^T, from the tile at tb) from a
-    // ring of four read three MFMAs ahead; X (P or dS, bf16) is in registers.
-    auto acc_mfma = [&](const LdsByte* tb, const u32x4 (&x)[2]) {
-      constexpr int NJ = 2 * MD;
-      bf16x8 rt[4];
-      auto tr_j = [&](auto jc) {
-        constexpr int j = decltype(jc)::value, kk = j / MD, md = j % MD;
-        rt[j & 3] = swz_tr_operand<D>(tb, t_offs, kk, md);
-      };
-      tr_j(std::integral_constant<int, 0>{});
-      tr_j(std::integral_constant<int, 1>{});
-      tr_j(std::integral_constant<int, 2>{});
-      static_for<NJ>([&](auto jc) {
-        constexpr int j = decltype(jc)::value, kk = j / MD, md = j % MD;
-        if constexpr (j + 3 < NJ) tr_j(std::integral_constant<int, j + 3>{});
-        acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rt[j & 3], __builtin_bit_cast(bf16x8, x[kk]), acc[md], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    };
-    // This lane's 32 bytes of P in slot (kb, hp) of P buffer pbuf.
-    auto p_slot = [&](int pbuf) { return pOff + pbuf * pBufBytes + ((2 * hp + kb) * 64 + lane) * 32; };
-
-    // Stages form a ring of three: step s reads stage s % 3 (the dV waves
-    // stage (s - 1) % 3), while the pairs of step s + 1 load into stage
-    // (s + 1) % 3, last read in step s - 1. P of step s goes to P buffer
-    // s % 2, read in step s + 1. A step's second slot past the last pair
-    // stages that last pair again (finite data; its products are masked to
-    // zero), so every step runs the same straight-line body and the
-    // accumulators stay in place.
     if (n_steps > 0) {
       load_pair(0, 0, 0);
       load_pair(min(1, n_pairs - 1), 1, 0);
@@ -519,155 +466,218 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
     }
     int b = 0;  // stage of this step
     for (int step = 0; step < n_steps; ++step) {
+      const int bn = b == 2 ? 0 : b + 1;
+      if (step + 1 < n_steps) {
+        load_pair(2 * step + 2, 0, bn);
+        load_pair(min(2 * step + 3, n_pairs - 1), 1, bn);
+      }
+      const int pair = 2 * step + hp;
+      const int qt = rng.x + min(pair, n_pairs - 1) / G;
+      const TileSum q_sum = ld_const(qp.qsum, qt);
+      // A pair that cannot meet the key tile (or lies past the last pair)
+      // contributes zeros.
+      const bool meet = pair < n_pairs && tiles_meet(q_sum, ks_sum, a.window);
+      const bool full = meet && tiles_full(q_sum, ks_sum, kt, P, a.window) && (qt + 1) * 32 <= P;
+      const LdsByte* pbase = smem + b * stageBytes + hp * pairBytes;
+      const LdsByte* qb = pbase;
+      const LdsByte* gb = pbase + qTile;
+      const LdsByte* misc = pbase + 2 * qTile;  // lse, delta, positions, segments
+      // S = Q K^T and dP = dO V^T; the Q and dout operands of a k-step are
+      // read from LDS two k-steps ahead of its MFMAs (a ring of three), and
+      // a scheduling fence keeps that order.
+      f32x16 s = {}, dp = {};
+      bf16x8 ra[3][2];
+      auto ld_ks = [&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        const int qo = q_row + (((2 * ks) ^ q_xc) << 4);
+        ra[ks % 3][0] = lds_ld<bf16x8>(qb + qo);
+        ra[ks % 3][1] = lds_ld<bf16x8>(gb + qo);
+      };
+      ld_ks(std::integral_constant<int, 0>{});
+      if constexpr (KS > 1) ld_ks(std::integral_constant<int, 1>{});
+      static_for<KS>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        if constexpr (ks + 2 < KS) ld_ks(std::integral_constant<int, ks + 2>{});
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][0], __builtin_bit_cast(bf16x8, kf[ks]), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][1], __builtin_bit_cast(bf16x8, vf[ks]), dp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // Register r of this lane holds query iq = 16 (r / 8) + 8 hf + r % 8
+      // of the tile and this lane's key; lse and delta of those queries
+      // come as four 16-byte reads each.
+      const int n_q = P - qt * 32;
+      float lse_r[16], dl_r[16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
+        const u32x4 lw = lds_ld<u32x4>(misc + iq0 * 4), dw = lds_ld<u32x4>(misc + 256 + iq0 * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lse_r[4 * c + e] = __uint_as_float(lw[e]);
+          dl_r[4 * c + e] = __uint_as_float(dw[e]);
+        }
+      }
+      // Positions and segments of the same queries, for a masked pair.
+      int qpos_r[16], qseg_r[16];
+      if (!full) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
+          const u32x4 pw = lds_ld<u32x4>(misc + 512 + iq0 * 4), sw = lds_ld<u32x4>(misc + 768 + iq0 * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            qpos_r[4 * c + e] = (int)pw[e];
+            qseg_r[4 * c + e] = (int)sw[e];
+          }
+        }
+      }
+      // P and dS in bf16, two 16-query halves each, to LDS.
+      u32x4 pp[2], pds[2];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float p2[2], d2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
+          const float l2 = lse_r[r + e] * kLog2eB;
+          bool ok = k_valid & meet;
+          if (!full)
+            ok = ok & (qseg_r[r + e] == seg_k) & ((uint32_t)qpos_r[r + e] - (uint32_t)pos_k < wlim) & (iq < n_q);
+          const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
+          p2[e] = p;
+          d2[e] = ok ? p * (dp[r + e] - dl_r[r + e]) : 0.f;
+        }
+        pp[r >> 3][(r & 7) >> 1] = pack_bf16x2(p2[0], p2[1]);
+        pds[r >> 3][(r & 7) >> 1] = pack_bf16x2(d2[0], d2[1]);
+      }
+      const int po = p_slot(step & 1);
+      lds_st(smem + po, pp[0]);
+      lds_st(smem + po + 16, pp[1]);
+      lds_st(smem + po + 32, pds[0]);
+      lds_st(smem + po + 48, pds[1]);
+      wait_all_loads();
+      wg_barrier();
+      b = bn;
+    }
+    wait_all_loads();
+    wg_barrier();
+    wg_barrier();  // the consumers' sums
+  };
+
+  // Consumer: one step behind its producer.
+  auto consume = [&]() {
+    f32x16 dk[MD], dv[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk[md][r] = 0.f;
+        dv[md][r] = 0.f;
+      }
+    int t_offs[MD][2];
+    swz_tr_offs<D>(lane, t_offs);
+    // dV^T += dO^T P and dK^T += Q^T dS for the pair staged at pbase, P and
+    // dS from P buffer pbuf: MFMA j (kk = j / 2 MD, md = (j / 2) % MD, dV
+    // for even j, dK for odd) takes its transposed operand from a ring of
+    // four read three MFMAs ahead.
+    auto accumulate = [&](const LdsByte* pbase, int pbuf) {
+      const LdsByte* qb = pbase;
+      const LdsByte* gb = pbase + qTile;
+      const int po = p_slot(pbuf);
+      const u32x4 pp[2] = {lds_ld<u32x4>(smem + po), lds_ld<u32x4>(smem + po + 16)};
+      const u32x4 pds[2] = {lds_ld<u32x4>(smem + po + 32), lds_ld<u32x4>(smem + po + 48)};
+      constexpr int NJ = 4 * MD;
+      bf16x8 rt[4];
+      auto tr_j = [&](auto jc) {
+        constexpr int j = decltype(jc)::value, kk = j / (2 * MD), md = (j / 2) % MD;
+        rt[j & 3] = swz_tr_operand<D>((j & 1) ? qb : gb, t_offs, kk, md);
+      };
+      tr_j(std::integral_constant<int, 0>{});
+      tr_j(std::integral_constant<int, 1>{});
+      tr_j(std::integral_constant<int, 2>{});
+      static_for<NJ>([&](auto jc) {
+        constexpr int j = decltype(jc)::value, kk = j / (2 * MD), md = (j / 2) % MD;
+        if constexpr (j + 3 < NJ) tr_j(std::integral_constant<int, j + 3>{});
+        if constexpr (j & 1)
+          dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rt[j & 3], __builtin_bit_cast(bf16x8, pds[kk]), dk[md], 0, 0, 0);
+        else
+          dv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rt[j & 3], __builtin_bit_cast(bf16x8, pp[kk]), dv[md], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+
+    // Stages form a ring of three: step s of the producers reads stage
+    // s % 3 and this wave stage (s - 1) % 3, while the pairs of step s + 1
+    // load into stage (s + 1) % 3, last read in step s - 1. P and dS of step
+    // s sit in P buffer s % 2. A step's second slot past the last pair
+    // stages that last pair again (its products are masked to zero), so
+    // every step runs the same straight-line body.
+    if (n_steps > 0) {
+      load_pair(0, 0, 0);
+      load_pair(min(1, n_pairs - 1), 1, 0);
+      wait_all_loads();
+      wg_barrier();
+    }
+    int b = 0;
+    for (int step = 0; step < n_steps; ++step) {
       const int bn = b == 2 ? 0 : b + 1, bp = b == 0 ? 2 : b - 1;
       if (step + 1 < n_steps) {
         load_pair(2 * step + 2, 0, bn);
         load_pair(min(2 * step + 3, n_pairs - 1), 1, bn);
       }
-      if constexpr (ROLE) {
-        const int pair = 2 * step + hp;
-        const int qt = rng.x + min(pair, n_pairs - 1) / G;
-        const TileSum q_sum = ld_const(qp.qsum, qt);
-        // A pair that cannot meet the key tile (or lies past the last pair)
-        // contributes zeros.
-        const bool meet = pair < n_pairs && tiles_meet(q_sum, ks_sum, a.window);
-        const bool full = meet && tiles_full(q_sum, ks_sum, kt, P, a.window) && (qt + 1) * 32 <= P;
-        const LdsByte* pbase = smem + b * stageBytes + hp * pairBytes;
-        const LdsByte* qb = pbase;
-        const LdsByte* gb = pbase + qTile;
-        const LdsByte* misc = pbase + 2 * qTile;  // lse, delta, positions, segments
-        // S = Q K^T and dP = dO V^T; the four operands of a k-step are read
-        // from LDS two k-steps ahead of its MFMAs (a ring of three sets), and
-        // a scheduling fence keeps that order, so LDS latency hides behind
-        // the MFMAs of the steps in between.
-        f32x16 s = {}, dp = {};
-        bf16x8 ra[3][4];
-        auto ld_ks = [&](auto kc) {
-          constexpr int ks = decltype(kc)::value;
-          bf16x8* o = ra[ks % 3];
-          const int qo = q_row + (((2 * ks) ^ q_xc) << 4);
-          o[0] = lds_ld<bf16x8>(qb + qo);
-          o[1] = lds_ld<bf16x8>(smem + kv_rd + ks * 32);
-          o[2] = lds_ld<bf16x8>(gb + qo);
-          o[3] = lds_ld<bf16x8>(smem + kv_rd + kvTile + ks * 32);
-        };
-        ld_ks(std::integral_constant<int, 0>{});
-        if constexpr (KS > 1) ld_ks(std::integral_constant<int, 1>{});
-        static_for<KS>([&](auto kc) {
-          constexpr int ks = decltype(kc)::value;
-          if constexpr (ks + 2 < KS) ld_ks(std::integral_constant<int, ks + 2>{});
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][0], ra[ks % 3][1], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks % 3][2], ra[ks % 3][3], dp, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        });
-        // Register r of this lane holds query iq = 16 (r / 8) + 8 hf + r % 8
-        // of the tile and this lane's key; lse and delta of those queries
-        // come as four 16-byte reads each.
-        const int n_q = P - qt * 32;
-        float lse_r[16], dl_r[16];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
-          const u32x4 lw = lds_ld<u32x4>(misc + iq0 * 4), dw = lds_ld<u32x4>(misc + 256 + iq0 * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            lse_r[4 * c + e] = __uint_as_float(lw[e]);
-            dl_r[4 * c + e] = __uint_as_float(dw[e]);
-          }
-        }
-        // Positions and segments of the same queries, for a masked pair.
-        int qpos_r[16], qseg_r[16];
-        if (!full) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
-            const u32x4 pw = lds_ld<u32x4>(misc + 512 + iq0 * 4), sw = lds_ld<u32x4>(misc + 768 + iq0 * 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              qpos_r[4 * c + e] = (int)pw[e];
-              qseg_r[4 * c + e] = (int)sw[e];
-            }
-          }
-        }
-        // P and dS in bf16, two 16-query halves each; P goes to LDS for the
-        // dV wave of the same keys and pairs.
-        u32x4 pp[2], pds[2];
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float p2[2], d2[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
-            const float l2 = lse_r[r + e] * kLog2eB;
-            bool ok = k_valid & meet;
-            if (!full)
-              ok = ok & (qseg_r[r + e] == seg_k) & ((uint32_t)qpos_r[r + e] - (uint32_t)pos_k < wlim) & (iq < n_q);
-            const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
-            p2[e] = p;
-            d2[e] = ok ? p * (dp[r + e] - dl_r[r + e]) : 0.f;
-          }
-          pp[r >> 3][(r & 7) >> 1] = pack_bf16x2(p2[0], p2[1]);
-          pds[r >> 3][(r & 7) >> 1] = pack_bf16x2(d2[0], d2[1]);
-        }
-        const int po = p_slot(step & 1);
-        lds_st(smem + po, pp[0]);
-        lds_st(smem + po + 16, pp[1]);
-        acc_mfma(qb, pds);
-      } else {
-        if (step > 0) {
-          const int po = p_slot((step - 1) & 1);
-          const u32x4 pp[2] = {lds_ld<u32x4>(smem + po), lds_ld<u32x4>(smem + po + 16)};
-          acc_mfma(smem + bp * stageBytes + hp * pairBytes + qTile, pp);
-        }
-      }
+      if (step > 0) accumulate(smem + bp * stageBytes + hp * pairBytes, (step - 1) & 1);
       wait_all_loads();
       wg_barrier();
       b = bn;
     }
-    // The dV waves' last pair (its stage is the last one read: nothing
-    // loads into it any more).
-    if constexpr (!ROLE) {
-      if (n_steps > 0) {
-        const int bp = b == 0 ? 2 : b - 1;
-        const int po = p_slot((n_steps - 1) & 1);
-        const u32x4 pp[2] = {lds_ld<u32x4>(smem + po), lds_ld<u32x4>(smem + po + 16)};
-        acc_mfma(smem + bp * stageBytes + hp * pairBytes + qTile, pp);
-      }
+    // The last pair (its stage is the last one read: nothing loads into it
+    // any more).
+    if (n_steps > 0) {
+      const int bp = b == 0 ? 2 : b - 1;
+      accumulate(smem + bp * stageBytes + hp * pairBytes, (n_steps - 1) & 1);
     }
     wait_all_loads();
     wg_barrier();
 
-    // The two parity wavefronts of a (key half, role) add their sums: the
-    // odd-pair one puts its sum in LDS, the even-pair one reads, adds and
-    // writes (dK scaled).
-    LdsByte* cb = smem + (2 * ROLE + kb) * (MD * 16 * 64 * 4);
+    // The two parity consumers of a key half add their sums: the odd-pair
+    // one puts its sums in LDS, the even-pair one reads, adds and writes.
+    LdsByte* cb = smem + kb * (2 * MD * 16 * 64 * 4);
     if (hp == 1) {
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) lds_st(cb + ((md * 16 + r) * 64 + lane) * 4, acc[md][r]);
+        for (int r = 0; r < 16; ++r) {
+          lds_st(cb + ((md * 16 + r) * 64 + lane) * 4, dk[md][r]);
+          lds_st(cb + (((MD + md) * 16 + r) * 64 + lane) * 4, dv[md][r]);
+        }
     }
     wg_barrier();
     if (hp == 0 && k_valid) {
-      const float f = ROLE ? a.scale : 1.f;
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[md][r] = (acc[md][r] + lds_ld<float>(cb + ((md * 16 + r) * 64 + lane) * 4)) * f;
-      uint16_t* og = static_cast<uint16_t*>(ROLE ? a.dk : a.dv) + ((long long)key * a.kv_heads + kh) * D;
+        for (int r = 0; r < 16; ++r) {
+          dk[md][r] += lds_ld<float>(cb + ((md * 16 + r) * 64 + lane) * 4);
+          dv[md][r] += lds_ld<float>(cb + (((MD + md) * 16 + r) * 64 + lane) * 4);
+        }
+      uint16_t* dkg = static_cast<uint16_t*>(a.dk) + ((long long)key * a.kv_heads + kh) * D;
+      uint16_t* dvg = static_cast<uint16_t*>(a.dv) + ((long long)key * a.kv_heads + kh) * D;
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          u32x2 w;
-          w[0] = pack_bf16x2(acc[md][4 * g], acc[md][4 * g + 1]);
-          w[1] = pack_bf16x2(acc[md][4 * g + 2], acc[md][4 * g + 3]);
-          *reinterpret_cast<u32x2*>(og + 32 * md + 8 * g + 4 * hf) = w;
+          u32x2 wk, wv;
+          wk[0] = pack_bf16x2(dk[md][4 * g] * a.scale, dk[md][4 * g + 1] * a.scale);
+          wk[1] = pack_bf16x2(dk[md][4 * g + 2] * a.scale, dk[md][4 * g + 3] * a.scale);
+          wv[0] = pack_bf16x2(dv[md][4 * g], dv[md][4 * g + 1]);
+          wv[1] = pack_bf16x2(dv[md][4 * g + 2], dv[md][4 * g + 3]);
+          *reinterpret_cast<u32x2*>(dkg + 32 * md + 8 * g + 4 * hf) = wk;
+          *reinterpret_cast<u32x2*>(dvg + 32 * md + 8 * g + 4 * hf) = wv;
         }
     }
   };
-  if (wave >= 4) run(std::integral_constant<int, 1>{});
-  else run(std::integral_constant<int, 0>{});
+  if (wave >= 4) produce();
+  else consume();
 }
 
 // ---------------------------------------------------------------------------
