@@ -379,7 +379,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
   constexpr int pairBytes = 2 * qTile + 4 * 256;
   constexpr int stageBytes = 2 * pairBytes;
   // After three stages, P and dS of the producers: two buffers of 4 slots
-  // (key half, pair parity) of 64 lanes x 64 bytes (P, then dS).
+  // (key half, pair parity) of 4 x 64 lanes x 16 bytes (P halves, then dS
+  // halves; piece c of lane l at 1024 c + 16 l, so each access covers the
+  // banks once).
   constexpr int pOff = 3 * stageBytes;
   constexpr int pBufBytes = 4 * 64 * 64;
   constexpr int combineBytes = 2 * 2 * MD * 16 * 64 * 4;
@@ -405,8 +407,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
   const int n_pairs = rng.y >= rng.x ? (rng.y - rng.x + 1) * G : 0;
   const int n_steps = (n_pairs + 1) / 2;
   const int row_bytes = a.heads * D * 2;
-  // This lane's 64 bytes of P and dS in slot (kb, hp) of buffer pbuf.
-  auto p_slot = [&](int pbuf) { return pOff + pbuf * pBufBytes + ((2 * hp + kb) * 64 + lane) * 64; };
+  // This lane's first piece of P and dS in slot (kb, hp) of buffer pbuf.
+  auto p_slot = [&](int pbuf) { return pOff + pbuf * pBufBytes + (2 * hp + kb) * 4096 + lane * 16; };
 
   // Stage the pair `pair` (query tile, head) into slot `slot` of buffer b:
   // Q and dout rows, lse and delta of the head, positions and segments.
@@ -552,9 +554,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
       }
       const int po = p_slot(step & 1);
       lds_st(smem + po, pp[0]);
-      lds_st(smem + po + 16, pp[1]);
-      lds_st(smem + po + 32, pds[0]);
-      lds_st(smem + po + 48, pds[1]);
+      lds_st(smem + po + 1024, pp[1]);
+      lds_st(smem + po + 2048, pds[0]);
+      lds_st(smem + po + 3072, pds[1]);
       wait_all_loads();
       wg_barrier();
       b = bn;
@@ -584,8 +586,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
       const LdsByte* qb = pbase;
       const LdsByte* gb = pbase + qTile;
       const int po = p_slot(pbuf);
-      const u32x4 pp[2] = {lds_ld<u32x4>(smem + po), lds_ld<u32x4>(smem + po + 16)};
-      const u32x4 pds[2] = {lds_ld<u32x4>(smem + po + 32), lds_ld<u32x4>(smem + po + 48)};
+      const u32x4 pp[2] = {lds_ld<u32x4>(smem + po), lds_ld<u32x4>(smem + po + 1024)};
+      const u32x4 pds[2] = {lds_ld<u32x4>(smem + po + 2048), lds_ld<u32x4>(smem + po + 3072)};
       constexpr int NJ = 4 * MD;
       bf16x8 rt[4];
       auto tr_j = [&](auto jc) {
