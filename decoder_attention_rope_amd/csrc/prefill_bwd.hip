@@ -301,31 +301,38 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
       }
       // Register r of this lane holds key j = 32 hb + 16 (r / 8) + 8 hf + r % 8.
       // Keys come in runs of four: their positions and segments are read
-      // 16 bytes at a time (a masked tile only).
+      // 16 bytes at a time (a masked tile only). One copy of this code for
+      // fully-allowed tiles and one for masked tiles, so the branch on
+      // `full` is taken once per half tile rather than once per element.
       u32x4 dsw[2];
+      auto ds_of = [&](auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-      for (int r4 = 0; r4 < 16; r4 += 4) {
-        const int j0 = 32 * hb + 16 * (r4 >> 3) + 8 * hf + (r4 & 7);
-        u32x4 kpw = {}, ksw = {};
-        if (!full) {
-          kpw = lds_ld<u32x4>(pb + j0 * 4);
-          ksw = lds_ld<u32x4>(pb + 256 + j0 * 4);
-        }
-#pragma unroll
-        for (int r = r4; r < r4 + 4; r += 2) {
-          float ds2[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int j = j0 + (r + e - r4);
-            bool ok = true;
-            if (!full)
-              ok = ((int)ksw[r + e - r4] == my_seg) & ((uint32_t)my_pos - kpw[r + e - r4] < wlim) & (j < n_j);
-            const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -lse2)) : 0.f;
-            ds2[e] = p * (dp[r + e] - dlt);
+        for (int r4 = 0; r4 < 16; r4 += 4) {
+          const int j0 = 32 * hb + 16 * (r4 >> 3) + 8 * hf + (r4 & 7);
+          u32x4 kpw = {}, ksw = {};
+          if constexpr (!FULL) {
+            kpw = lds_ld<u32x4>(pb + j0 * 4);
+            ksw = lds_ld<u32x4>(pb + 256 + j0 * 4);
           }
-          dsw[r >> 3][(r & 7) >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+#pragma unroll
+          for (int r = r4; r < r4 + 4; r += 2) {
+            float ds2[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int j = j0 + (r + e - r4);
+              bool ok = true;
+              if constexpr (!FULL)
+                ok = ((int)ksw[r + e - r4] == my_seg) & ((uint32_t)my_pos - kpw[r + e - r4] < wlim) & (j < n_j);
+              const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -lse2)) : 0.f;
+              ds2[e] = p * (dp[r + e] - dlt);
+            }
+            dsw[r >> 3][(r & 7) >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+          }
         }
-      }
+      };
+      if (full) ds_of(std::true_type{});
+      else ds_of(std::false_type{});
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -519,44 +526,51 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
           dl_r[4 * c + e] = __uint_as_float(dw[e]);
         }
       }
-      // Positions and segments of the same queries, for a masked pair.
-      int qpos_r[16], qseg_r[16];
-      if (!full) {
+      // P and dS in bf16, two 16-query halves each, to LDS. One copy of this
+      // code for fully-allowed pairs and one for masked pairs (their query
+      // positions and segments read 16 bytes at a time), so the branch on
+      // `full` is taken once per pair rather than once per element.
+      const int po = p_slot(step & 1);
+      auto p_ds = [&](auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
+        int qpos_r[16], qseg_r[16];
+        if constexpr (!FULL) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
-          const u32x4 pw = lds_ld<u32x4>(misc + 512 + iq0 * 4), sw = lds_ld<u32x4>(misc + 768 + iq0 * 4);
+          for (int c = 0; c < 4; ++c) {
+            const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
+            const u32x4 pw = lds_ld<u32x4>(misc + 512 + iq0 * 4), sw = lds_ld<u32x4>(misc + 768 + iq0 * 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            qpos_r[4 * c + e] = (int)pw[e];
-            qseg_r[4 * c + e] = (int)sw[e];
+            for (int e = 0; e < 4; ++e) {
+              qpos_r[4 * c + e] = (int)pw[e];
+              qseg_r[4 * c + e] = (int)sw[e];
+            }
           }
         }
-      }
-      // P and dS in bf16, two 16-query halves each, to LDS.
-      u32x4 pp[2], pds[2];
+        u32x4 pp[2], pds[2];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float p2[2], d2[2];
+        for (int r = 0; r < 16; r += 2) {
+          float p2[2], d2[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
-          const float l2 = lse_r[r + e] * kLog2eB;
-          bool ok = k_valid & meet;
-          if (!full)
-            ok = ok & (qseg_r[r + e] == seg_k) & ((uint32_t)qpos_r[r + e] - (uint32_t)pos_k < wlim) & (iq < n_q);
-          const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
-          p2[e] = p;
-          d2[e] = ok ? p * (dp[r + e] - dl_r[r + e]) : 0.f;
+          for (int e = 0; e < 2; ++e) {
+            const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
+            const float l2 = lse_r[r + e] * kLog2eB;
+            bool ok = k_valid & meet;
+            if constexpr (!FULL)
+              ok = ok & (qseg_r[r + e] == seg_k) & ((uint32_t)qpos_r[r + e] - (uint32_t)pos_k < wlim) & (iq < n_q);
+            const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
+            p2[e] = p;
+            d2[e] = ok ? p * (dp[r + e] - dl_r[r + e]) : 0.f;
+          }
+          pp[r >> 3][(r & 7) >> 1] = pack_bf16x2(p2[0], p2[1]);
+          pds[r >> 3][(r & 7) >> 1] = pack_bf16x2(d2[0], d2[1]);
         }
-        pp[r >> 3][(r & 7) >> 1] = pack_bf16x2(p2[0], p2[1]);
-        pds[r >> 3][(r & 7) >> 1] = pack_bf16x2(d2[0], d2[1]);
-      }
-      const int po = p_slot(step & 1);
-      lds_st(smem + po, pp[0]);
-      lds_st(smem + po + 1024, pp[1]);
-      lds_st(smem + po + 2048, pds[0]);
-      lds_st(smem + po + 3072, pds[1]);
+        lds_st(smem + po, pp[0]);
+        lds_st(smem + po + 1024, pp[1]);
+        lds_st(smem + po + 2048, pds[0]);
+        lds_st(smem + po + 3072, pds[1]);
+      };
+      if (full) p_ds(std::true_type{});
+      else p_ds(std::false_type{});
       wait_all_loads();
       wg_barrier();
       b = bn;
