@@ -559,7 +559,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
               ok = ok & (qseg_r[r + e] == seg_k) & ((uint32_t)qpos_r[r + e] - (uint32_t)pos_k < wlim) & (iq < n_q);
             const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
             p2[e] = p;
-            d2[e] = ok ? p * (dp[r + e] - dl_r[r + e]) : 0.f;
+            d2[e] = p * (dp[r + e] - dl_r[r + e]);  // p is 0 where masked; dP, delta finite
           }
           pp[r >> 3][(r & 7) >> 1] = pack_bf16x2(p2[0], p2[1]);
           pds[r >> 3][(r & 7) >> 1] = pack_bf16x2(d2[0], d2[1]);
