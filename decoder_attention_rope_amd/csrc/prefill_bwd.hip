@@ -130,7 +130,7 @@ __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x
 // ---------------------------------------------------------------------------
 // delta[i, h] = <dout[i, h, :], out[i, h, :]> in f32; D / 8 lanes per row.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, float* delta) {
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, float* delta, float* lse2) {
   const int cpr = a.head_dim / 8;  // 16-byte chunks per row (8 or 16)
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long total = (long long)a.p * a.heads * cpr;
@@ -145,7 +145,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, float* delta)
     }
   }
   for (int off = 1; off < cpr; off <<= 1) acc += __shfl_xor(acc, off, 64);
-  if (idx < total && (threadIdx.x & (cpr - 1)) == 0) delta[idx / cpr] = acc;
+  if (idx < total && (threadIdx.x & (cpr - 1)) == 0) {
+    delta[idx / cpr] = acc;
+    lse2[idx / cpr] = a.lse[idx / cpr] * kLog2eB;  // lse in base-2 units, for the dK/dV kernel
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, const TileSum* ksum,
                                                          const int2* krange, const int* korder,
-                                                         const float* delta) {
+                                                         const float* delta, const float* lse2) {
   constexpr int KS = D / 16, MD = D / 32;
   using SQT = ST<D>;
   constexpr int qTile = SQT::bytes(32);            // one Q or dout tile (32 queries, swizzled)
@@ -437,7 +440,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
     const int mw = wave - 4;
     const uint32_t mdst = __builtin_amdgcn_readfirstlane(base + 2 * qTile + 256 * (mw & 3));
     if (mw == 0 || mw == 1) {
-      const float* src = mw == 0 ? a.lse : delta;
+      const float* src = mw == 0 ? lse2 : delta;
       const i32x4 r = raw_rsrc(src + (long long)qt * 32 * a.heads + h, 4 * ((n_rows - 1) * a.heads + 1));
       lds_dma<4>(r, mdst, lane < 32 ? lane * a.heads * 4 : 0x40000000);
     } else if (mw == 2 || mw == 3) {
@@ -553,7 +556,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
-            const float l2 = lse_r[r + e] * kLog2eB;
+            const float l2 = lse_r[r + e];  // lse * log2(e), staged as such
             bool ok = k_valid & meet;
             if constexpr (!FULL)
               ok = ok & (qseg_r[r + e] == seg_k) & ((uint32_t)qpos_r[r + e] - (uint32_t)pos_k < wlim) & (iq < n_q);
@@ -703,12 +706,12 @@ size_t prefill_bwd_workspace_bytes(int p, int heads) {
   const size_t n_kt = (size_t)(p + kBK - 1) / kBK;
   const size_t n_q32 = (size_t)(p + 31) / 32;
   return prefill_plan_bytes(p) + align256(n_q32 * sizeof(TileSum)) + align256(n_kt * sizeof(int2)) +
-         2 * align256(n_kt * sizeof(int)) + align256((size_t)p * heads * sizeof(float));
+         2 * align256(n_kt * sizeof(int)) + 2 * align256((size_t)p * heads * sizeof(float));
 }
 
 template <int D>
 static hipError_t launch_bwd_main(const BwdArgs& a, const Plan& pl, const Plan& qp, const int2* krange,
-                                  const int* korder, const float* delta, hipStream_t stream) {
+                                  const int* korder, const float* delta, const float* lse2, hipStream_t stream) {
   const int n_groups = a.kv_heads * pl.head_groups;
   const dim3 gq(pl.n_qt * n_groups), blk(256);
   if (pl.gw == 4) bwd_dq_kernel<D, 4><<<gq, blk, 0, stream>>>(a, pl, delta);
@@ -716,7 +719,7 @@ static hipError_t launch_bwd_main(const BwdArgs& a, const Plan& pl, const Plan& 
   else bwd_dq_kernel<D, 1><<<gq, blk, 0, stream>>>(a, pl, delta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_dkdv_kernel<D><<<dim3(pl.n_kt * a.kv_heads), dim3(512), 0, stream>>>(a, qp, pl.ksum, krange, korder, delta);
+  bwd_dkdv_kernel<D><<<dim3(pl.n_kt * a.kv_heads), dim3(512), 0, stream>>>(a, qp, pl.ksum, krange, korder, delta, lse2);
   return hipGetLastError();
 }
 
@@ -756,6 +759,8 @@ hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t stream) {
   ws += align256((size_t)pl.n_kt * sizeof(int));
   kp.max_cost = (int)n_q32;
   float* delta = reinterpret_cast<float*>(ws);
+  ws += align256((size_t)a.p * a.heads * sizeof(float));
+  float* lse2 = reinterpret_cast<float*>(ws);
   e = prefill_summarize(pa, qp, stream);
   if (e != hipSuccess) return e;
   bwd_krange_kernel<<<dim3((pl.n_kt + 3) / 4), dim3(256), 0, stream>>>(a, qp, pl.ksum, krange, kp.cost, pl.n_kt);
@@ -764,11 +769,11 @@ hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t stream) {
   e = prefill_order(kp, stream);
   if (e != hipSuccess) return e;
   const long long chunks = (long long)a.p * a.heads * (a.head_dim / 8);
-  bwd_delta_kernel<<<dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream>>>(a, delta);
+  bwd_delta_kernel<<<dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream>>>(a, delta, lse2);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return a.head_dim == 64 ? launch_bwd_main<64>(a, pl, qp, krange, kp.order, delta, stream)
-                          : launch_bwd_main<128>(a, pl, qp, krange, kp.order, delta, stream);
+  return a.head_dim == 64 ? launch_bwd_main<64>(a, pl, qp, krange, kp.order, delta, lse2, stream)
+                          : launch_bwd_main<128>(a, pl, qp, krange, kp.order, delta, lse2, stream);
 }
 
 }  // namespace gqa
