@@ -69,6 +69,8 @@ CASES = [
     (6, 520, 16, 2, 64, 30, 300, 1),
     (7, 97, 2, 1, 128, 1, 40, 0),
     (8, 1000, 32, 8, 128, 64, 600, 0),
+    (9, 1, 4, 2, 128, 1, 1, 0),  # one token: one partial query tile and key tile
+    (10, 31, 8, 8, 64, 5, 31, 3),  # a single partial tile, window 3
 ]
 
 
