@@ -123,3 +123,52 @@ def test_graph_replay_matches_eager():
         got = results()
         for i, (a, b) in enumerate(zip(got, ref)):
             assert _same(a, b), f"replay {rep}: result {i} differs from the eager run"
+
+
+def test_graph_replay_training_pair_matches_eager():
+    print("[case] graph capture: packed forward with lse + backward", flush=True)
+    heads, kvh, d = 8, 2, 128
+    g = W.streams(778)
+    lengths, pos_h, seg_h = W.segment_layout(700, 20, 300, g["index"])
+    p = len(pos_h)
+    q = dev(host_values(W.normal(g["q"], (p, heads, d)), "bf16")[0])
+    k = dev(host_values(W.normal(g["k"], (p, kvh, d)), "bf16")[0])
+    v = dev(host_values(W.normal(g["v"], (p, kvh, d)), "bf16")[0])
+    gd = dev(host_values(W.normal(g["extra"], (p, heads, d)), "bf16")[0])
+    pos, seg = i32(pos_h), i32(seg_h)
+    bf = torch.bfloat16
+    out = torch.empty((p, heads, d), dtype=bf, device=DEV)
+    lse = torch.empty((p, heads), dtype=torch.float32, device=DEV)
+    dq = torch.empty((p, heads, d), dtype=bf, device=DEV)
+    dk = torch.empty((p, kvh, d), dtype=bf, device=DEV)
+    dv = torch.empty((p, kvh, d), dtype=bf, device=DEV)
+    wsf, nbf = workspace(gqa.gqa_prefill_packed_workspace(p, heads, kvh, d))
+    wsb, nbb = workspace(gqa.gqa_prefill_packed_backward_workspace(p, heads, kvh, d))
+
+    def work():
+        gqa.gqa_prefill_packed_lse(p, heads, kvh, d, gqa.GQA_BF16, 0.0, 64, q, k, v, pos, seg, out, lse,
+                                   wsf, nbf)
+        gqa.gqa_prefill_packed_backward(p, heads, kvh, d, gqa.GQA_BF16, 0.0, 64, q, k, v, out, gd, lse,
+                                        pos, seg, dq, dk, dv, wsb, nbb)
+
+    def results():
+        return [x.clone() for x in (out, lse, dq, dk, dv)]
+
+    work()
+    torch.cuda.synchronize()
+    ref = results()
+    assert all(torch.isfinite(x.float()).all() for x in ref)
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in (out, lse, dq, dk, dv):
+            x.fill_(float("nan"))
+        _ = torch.randn(4096, device=DEV).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(results(), ref)):
+            assert _same(a, b), f"replay {rep}: result {i} differs from the eager run"
