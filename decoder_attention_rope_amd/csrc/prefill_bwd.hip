@@ -14,7 +14,7 @@
 // Design: the forward stores lse (natural-log softmax denominators), so the
 // backward never renormalizes. Three kernels after the forward's prepared
 // walk:
-// * delta: one pass over out and dout.
+// * delta: one pass over out and dout (and lse, rewritten in base-2 units).
 // * dQ, one workgroup per query tile and group of query heads, as the
 //   forward: for each visited key tile, S^T = K Q^T and dP^T = V dO^T on the
 //   32x32x16 bf16 MFMA (K and V rows the A operands, q and dout in
@@ -22,15 +22,17 @@
 //   then dQ^T += K^T dS^T with K^T read from the same LDS tile by transposing
 //   8-byte reads (the key order inside a 32-key block is permuted as in the
 //   forward, so dS packs straight into the B operand).
-// * dK / dV, one workgroup per key tile and KV head: each wavefront owns 32
-//   keys (K^T and V^T as B operands in registers) and every other (query
-//   tile, head) pair; S = Q K^T and dP = dO V^T put a lane on one key, then
-//   dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed from
-//   LDS. The two wavefronts of a key half add their sums at the end.
+// * dK / dV, one workgroup per key tile and KV head, in producer / consumer
+//   wavefront pairs: a producer owns 32 keys (K^T and V^T as B operands in
+//   registers) and every other (query tile, head) pair; S = Q K^T and
+//   dP = dO V^T put a lane on one key, and it passes P and dS through LDS.
+//   Its consumer accumulates dV^T += dO^T P and dK^T += Q^T dS with dO^T
+//   and Q^T read transposed from LDS. The consumers of a key half add their
+//   sums at the end.
 // Query, dout, K and V tiles go from memory straight into LDS (row r of a
-// 32-row block holding entity kappa(r)), one tile ahead of the matrix work.
-// Tiles read only row-wise have rows padded to 2 D + 16 bytes; tiles that are
-// also read transposed have unpadded rows with XOR-swizzled 16-byte chunks.
+// 32-row block holding entity kappa(r)), ahead of the matrix work, in
+// unpadded rows with XOR-swizzled 16-byte chunks (they are read both
+// row-wise and transposed).
 #include "attn_tiles.h"
 #include "common.h"
 #include "internal.h"
@@ -39,29 +41,6 @@ namespace gqa {
 
 namespace {
 constexpr float kLog2eB = 1.4426950408889634f;
-
-// LDS tile of rows of D bf16 values, padded to 2 D + 16 bytes (the dK/dV
-// kernel's K and V tiles of 64 keys, read row-wise only).
-template <int D>
-struct BT {
-  static constexpr int kStride = 2 * D + 16;
-  static constexpr int kChunks = D / 8 + 1;  // 16-byte chunks per padded row
-  // 1-KiB direct loads covering `rows` padded rows (the last one may spill
-  // zeros up to the next KiB).
-  static constexpr int loads(int rows) { return (rows * kChunks + 63) / 64; }
-  static constexpr int bytes(int rows) { return 1024 * loads(rows); }
-};
-
-// Lane offset (bytes from the tile's first row) of slot p of a padded tile
-// whose row r holds row kappa(r) of a [*, row_bytes] tensor; pad slots and
-// tensor rows at or past `rows` fetch out of range.
-template <int D>
-__device__ __forceinline__ int padded_off(int p, int rows, int row_bytes) {
-  constexpr int kc = BT<D>::kChunks;
-  const int row = p / kc, ch = p - row * kc;
-  const int src = kappa(row);
-  return (ch == D / 8 || src >= rows) ? 0x40000000 : src * row_bytes + ch * 16;
-}
 
 // Swizzled LDS tile of rows of D bf16 values (the dK/dV kernel's Q and dout
 // tiles, the dQ kernel's K and V tiles): row stride 2 D bytes, 16-byte chunk
@@ -185,7 +164,6 @@ __global__ __launch_bounds__(256) void bwd_krange_kernel(BwdArgs a, Plan qp, con
 template <int D, int GW>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, const float* delta) {
   constexpr int SUB = 4 / GW, TQ = 32 * SUB, KS = D / 16, MD = D / 32;
-  using B = BT<D>;
   using SKT = ST<D>;
   constexpr int kTile = SKT::bytes(kBK);  // K and V tiles swizzled (K is also read transposed)
   constexpr int kOffV = 2 * kTile, kOffP = 4 * kTile;
