@@ -88,15 +88,23 @@ static double f32(double x) { return orc_round(x, ORC_DT_F32); }
 /* rsqrt(cast<f32>(H / Heads)) of `forward`, `packed` and `decode` [L], read
  * as the correctly rounded f32 value of 1/sqrt(D). */
 double orc_default_scale(int head_dim) {
+#if ORC_MUTATE == 15
+  return 1.0 / sqrt((double)head_dim);
+#else
   return f32(1.0 / sqrt(f32((double)head_dim)));
+#endif
 }
 
 /* ------------------------------------------------------------------------ */
-/* Rotary tables: rope.linnet `tables<S, D, T>(theta)` [L].                 */
-/*   inv_freq[i] = exp(-(f32(i) * 2.0 / f32(D)) * log(theta))   (f32 ops)    */
-/*   angles[s, i] = f32(s) * inv_freq[i]                          (f32 op)   */
-/*   full = concat(angles, angles) along the last axis: [S, D]               */
-/*   result = (cast<T>(cos(full)), cast<T>(sin(full)))                       */
+/* Rotary tables: [L], src/rope.linnet, `tables` (with THETA).               */
+/* The page builds, in f32, one inverse frequency per pair of head           */
+/* dimensions (theta raised to minus twice the pair index over D, written    */
+/* as an exponential of a product with log theta), multiplies each by the    */
+/* position to get the angle, repeats the angles for both halves of the     */
+/* head dimension and casts their cosine and sine to T.                      */
+/* The f32 steps, in order: i -> f32, times 2, divided by f32(D), negated,   */
+/* times f32(log(f32(theta))), exp; angle = f32(s) * inv_freq (one f32      */
+/* product); cos and sin of that angle in f32, then rounded to T.            */
 /* Reading: each f32 operation (including exp, log, cos, sin) returns the    */
 /* correctly rounded f32 result; the double-precision library value rounded */
 /* to f32 stands for it. `dtype` is T (ORC_DT_NONE keeps the f32 values).   */
@@ -104,6 +112,10 @@ double orc_default_scale(int head_dim) {
 /* ------------------------------------------------------------------------ */
 void orc_inv_freq(int D, double theta, double* inv_freq /* [D/2] */) {
   const double log_theta = f32(log(f32(theta)));
+#if ORC_MUTATE == 16
+  for (int i = 0; i < D / 2; ++i) inv_freq[i] = f32(exp(-(2.0 * i / D) * log(theta)));
+  return;
+#endif
   for (int i = 0; i < D / 2; ++i) {
     double a = f32(f32((double)i) * 2.0);
 #if ORC_MUTATE == 9

@@ -11,8 +11,13 @@ ideas / src/attention.linnet / src/rope.linnet; Nest cards llama-3.1-8b-
 instruct and gpt-oss-20b, blocks GroupedQueryAttention and SinkAttention):
   rounding      brute-force nearest-even search over bf16 bit patterns, and
                 torch's float32 -> bfloat16 conversion (a library routine)
-  inv_freq      the closed form theta^(-2i/D) of `tables`
-  tables        numpy cos/sin of the f32 angle, rounded by torch; s = 0 row
+  scale         the default scale rsqrt(f32(H / Heads)) as literal values
+                (1/sqrt(D) written out and rounded once to f32 by numpy)
+  inv_freq      the closed form theta^(-2i/D) of `tables`; bit for bit, the
+                page's f32 pipeline redone in numpy float32 arithmetic
+  tables        numpy cos/sin of the f32 angle, rounded by torch; s = 0 row;
+                bit for bit at the tiny Llama, Llama-3.1-8B and gpt-oss
+                table shapes, from numpy float32 angles
   rope          hand-worked rotations of basis vectors (the textbook 2-D
                 rotation on the pairs (i, i + D/2)); pair-norm preservation;
                 the relative-position property of rotary embeddings
@@ -59,6 +64,31 @@ def _close(a, b, atol, what):
     assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
     err = np.max(np.abs(a - b)) if a.size else 0.0
     assert err <= atol, f"{what}: max abs err {err:.3e} > {atol:.1e}"
+
+
+# The default softmax scale of `forward`, `packed` and `decode` (Linnet
+# "examples/01-llama" page, src/attention.linnet): rsqrt of the head dim cast
+# to f32. 1/sqrt(D) is written out in decimal (a power of two for D = 16 and
+# 64) and rounded once to f32 by numpy's cast; the attention pins use these
+# values, never the oracle's own.
+_SCALE = {
+    8: float(np.float32(0.35355339059327376220)),
+    16: 0.25,
+    64: 0.125,
+    128: float(np.float32(0.088388347648318440550)),
+}
+
+
+def _scale_ref(d):
+    return _SCALE[d]
+
+
+def pin_default_scale(o):
+    for d, ref in _SCALE.items():
+        got = o.default_scale(d)
+        assert got == ref, f"default scale D={d}: {got!r} vs {ref!r}"
+    assert o.default_scale(64) == 0.125
+    assert o.default_scale(128) == float(np.float32(1 / np.sqrt(128)))
 
 
 # ---------------------------------------------------------------------------
@@ -133,6 +163,45 @@ def pin_tables(o):
         assert mism < 1e-3, f"table entries differing from numpy+torch: {mism}"
 
 
+def _tables_f32_numpy(seq, d, theta):
+    """The `tables` pipeline (Linnet "examples/01-llama" page, src/rope.linnet)
+    in numpy float32 arithmetic: every product, quotient and negation is an
+    IEEE float32 operation; log, exp, cos and sin are the float64 library
+    values rounded once to float32 (the correctly rounded f32 result, as the
+    design reads the page's f32 ops). Returns inv_freq and the bf16 cos / sin
+    halves [seq, d/2] as float64."""
+    import math
+    f = np.float32
+    log_theta = f(math.log(float(f(theta))))
+    inv = np.empty(d // 2, dtype=np.float32)
+    for i in range(d // 2):
+        a = f(i) * f(2.0)
+        b = a / f(d)
+        e = (-b) * log_theta
+        inv[i] = f(math.exp(float(e)))
+    ang = np.arange(seq, dtype=np.float32)[:, None] * inv[None, :]
+    assert ang.dtype == np.float32
+    c = np.cos(ang.astype(np.float64)).astype(np.float32)
+    s = np.sin(ang.astype(np.float64)).astype(np.float32)
+    return inv.astype(np.float64), _bf16_vals(c), _bf16_vals(s)
+
+
+def pin_tables_f32_pipeline(o):
+    # The table shapes of the tiny Llama example (theta 1e4, D 64, 512 rows),
+    # the Llama-3.1-8B workloads (theta 5e5, D 128, 8192 rows) and gpt-oss
+    # (theta 5e5, D 64, 4352 rows): inv_freq and every bf16 entry bit for bit.
+    for seq, d, theta in ((512, 64, 10000.0), (8192, 128, 500000.0), (4352, 64, 500000.0)):
+        inv_ref, c_ref, s_ref = _tables_f32_numpy(seq, d, theta)
+        inv = o.inv_freq(d, theta)
+        assert np.array_equal(inv, inv_ref), \
+            f"inv_freq D={d} theta={theta}: {int(np.sum(inv != inv_ref))} values differ from the f32 pipeline"
+        c, s = o.rope_tables(seq, d, theta, "bf16")
+        half = d // 2
+        nc = int(np.sum(c[:, :half] != c_ref))
+        ns = int(np.sum(s[:, :half] != s_ref))
+        assert nc == 0 and ns == 0, f"tables {seq}x{d}: {nc} cos and {ns} sin entries differ"
+
+
 def pin_rope_hand(o):
     # D = 4: pairs (0, 2) and (1, 3); inv_freq = (1, theta^-1/2).
     d, theta = 4, 10000.0
@@ -199,7 +268,7 @@ def pin_mha_causal(o):
     q, k, v = (rng.standard_normal((1, s, h, d)) for _ in range(3))
     out = o.forward(q, k, v)[0]
     mask = np.tril(np.ones((s, s), dtype=bool))
-    ref = _sdpa(q[0], k[0], v[0], mask, o.default_scale(d), False)
+    ref = _sdpa(q[0], k[0], v[0], mask, _scale_ref(d), False)
     _close(out, ref, 1e-12, "MHA causal vs SDPA")
 
 
@@ -210,13 +279,13 @@ def pin_gqa(o):
     k, v = (rng.standard_normal((1, s, kvh, d)) for _ in range(2))
     out = o.forward(q, k, v)[0]
     mask = np.tril(np.ones((s, s), dtype=bool))
-    ref = _sdpa(q[0], k[0], v[0], mask, o.default_scale(d), True)
+    ref = _sdpa(q[0], k[0], v[0], mask, _scale_ref(d), True)
     _close(out, ref, 1e-12, "GQA vs SDPA(enable_gqa)")
     # the same by explicit broadcast_to + reshape of the KV heads
     kr = np.broadcast_to(k[0][:, :, None, :], (s, kvh, h // kvh, d)).reshape(s, h, d)
     vr = np.broadcast_to(v[0][:, :, None, :], (s, kvh, h // kvh, d)).reshape(s, h, d)
     ref2 = _sdpa(q[0], np.ascontiguousarray(kr), np.ascontiguousarray(vr), mask,
-                 o.default_scale(d), False)
+                 _scale_ref(d), False)
     _close(out, ref2, 1e-12, "GQA vs MHA on broadcast KV heads")
 
 
@@ -230,7 +299,7 @@ def pin_window(o):
         i = np.arange(s)[:, None]
         j = np.arange(s)[None, :]
         mask = (j <= i) & (i - j < w)
-        ref = _sdpa(q[0], k[0], v[0], mask, o.default_scale(d), True)
+        ref = _sdpa(q[0], k[0], v[0], mask, _scale_ref(d), True)
         _close(out, ref, 1e-12, f"window {w} vs SDPA band mask")
     # window 1 keeps only the query's own key: out = v exactly
     out = o.forward(q, k, v, window=1)[0]
@@ -245,7 +314,7 @@ def pin_sinks(o):
     q = rng.standard_normal((1, s, h, d))
     k, v = (rng.standard_normal((1, s, kvh, d)) for _ in range(2))
     sinks = rng.standard_normal(h)
-    scale = o.default_scale(d)
+    scale = _scale_ref(d)
     for w in (0, 6):
         out = o.forward(q, k, v, window=w, sinks=sinks)[0]
         g = h // kvh
@@ -321,7 +390,7 @@ def pin_packed_equals_segments(o):
     out = o.packed(q, k, v, pos, seg)
     st, n = starts[2], lengths[2]
     ref = _sdpa(q[st:st + n], k[st:st + n], v[st:st + n], np.tril(np.ones((n, n), bool)),
-                o.default_scale(d), True)
+                _scale_ref(d), True)
     _close(out[st:st + n], ref, 1e-12, "packed segment vs SDPA causal")
     # sampled queries give the same rows
     sel = np.array([0, 5, 20, 31], dtype=np.int32)
@@ -402,7 +471,7 @@ def pin_paged_equals_contiguous(o):
     t2[2, 1] = -1
     t2[3, 2] = num_pages + 5
     a = o.decode_paged(q, pk, pv, positions, t2)
-    scale = o.default_scale(d)
+    scale = _scale_ref(d)
     for r in range(rows):
         keep = np.arange(max_seq) <= positions[r]
         for pg in range(pages):
@@ -487,7 +556,7 @@ def pin_chunk_cached(o):
     rows = np.array([1, 0, 1, 2, 1, 0, 3, 2, -1, 0], dtype=np.int32)
     pos = np.array([5, 0, 6, 23, 7, 1, 4, 30, 2, -1], dtype=np.int32)
     n = rows.shape[0]
-    scale = o.default_scale(d)
+    scale = _scale_ref(d)
     for w, sk in ((0, None), (4, rng.standard_normal(h))):
         # q = 0: uniform weights, the mean of the attended values (closed form)
         out0 = o.prefill_cached(np.zeros((n, h, d)), rows, pos, ck, cv, window=w)
@@ -683,8 +752,10 @@ def pin_packed_backward(o):
 
 ALL_PINS = {
     "rounding": pin_rounding,
+    "default_scale": pin_default_scale,
     "inv_freq": pin_inv_freq,
     "tables": pin_tables,
+    "tables_f32_pipeline": pin_tables_f32_pipeline,
     "rope_hand": pin_rope_hand,
     "rope_norm_relative": pin_rope_norm_and_relative,
     "mha_causal": pin_mha_causal,

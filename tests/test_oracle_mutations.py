@@ -4,7 +4,8 @@ Each ORC_MUTATE value in oracle/gqa_oracle.c plants one plausible mistake
 (a wrong KV-head index, a dropped scale, a flipped RoPE sign, a strict `own`
 comparison, an off-by-one window, a scaled sink, a strict `seen`, a swapped
 page index, a wrong inv_freq denominator, truncating rounding, an ignored
-cache row, reversed in-page offsets, a transposed Linear weight). The oracle is
+cache row, reversed in-page offsets, a transposed Linear weight, a dropped
+backward term, an unrounded default scale, an fp64 inv_freq pipeline). The oracle is
 rebuilt with each one into a temporary directory; the pins must reject it.
 """
 import os
@@ -30,6 +31,8 @@ MUTATIONS = {
     12: "paged chunk reverses offsets inside a page",
     13: "linear reads the weight transposed",
     14: "attention backward drops the softmax row term delta",
+    15: "default scale left in fp64 (not rounded to f32)",
+    16: "inv_freq evaluated in plain fp64, rounded to f32 only at the end",
 }
 
 
