@@ -17,7 +17,13 @@ constexpr int kBK = 64;       // keys per tile
 constexpr int kPrepThreads = 1024;
 constexpr int kMaskWords = 6;  // 32-bit words per (query tile, group of 64 key tiles)
 constexpr int kRecInts = 16;   // ints per start record (64 bytes)
+constexpr int kRecVis = 12;    // visit-list entries copied into a start record
+constexpr int kVisMode = 24;   // visit-list entry: kt | mode << kVisMode
 constexpr float kNegInf = -__builtin_huge_valf();
+// Bytes by which a tile's buffer descriptor starts before the tile (see the
+// shared-M0 loads in the prefill kernel); the host keeps every packed
+// operand's range, p * row bytes + kShift, below 2^31.
+constexpr int kShift = 4096;
 
 // Per tile of tokens: [min, max] of segments and positions, and the smallest
 // position among the tokens of segment seg_min (pos_first) and of segment
@@ -36,10 +42,16 @@ struct Plan {
                    // 64-bit masks "visit", "every pair allowed" and "one
                    // segment" (see tiles_oneseg)
   int* rec;        // [n_qt][kRecInts] or null: per ordered slot i, the start
-                   // of its walk in one record -- query tile order[i], its
-                   // visited key-tile range, the index of the group of 64 key
-                   // tiles holding the first one (-1 if none) and that
-                   // group's kMaskWords mask words
+                   // of its walk in one record -- query tile order[i], the
+                   // numbers of fully allowed and of masked key tiles it
+                   // visits, and its first kRecVis visit-list entries
+  int* vis;        // [n_qt][n_kt] or null (packed keys): per query tile the
+                   // key tiles it visits, in walk order, as entries
+                   // kt | mode << kVisMode (mode 0: every pair allowed, 1: one
+                   // segment, positions decide, 2: the full predicate); the
+                   // fully allowed tiles first, then the others, each in
+                   // increasing kt
+  int* nfull;      // [n_qt] fully allowed tiles in each visit list
   int n_kt, n_qt, n_kg, tq, head_groups, gw;
   int max_cost;    // costs are clamped to [0, max_cost] for the ordering
 };
@@ -82,11 +94,14 @@ __device__ __forceinline__ bool tiles_full(const TileSum& q, const TileSum& k, i
          (window <= 0 || (long long)q.pos_max - (long long)k.pos_min < window);
 }
 
-// Both tiles lie in one and the same segment and key tile kt holds 64 real
-// keys: a pair is then allowed iff its positions (and the window) allow it,
-// so the per-element mask may skip the segment compare.
+// Both tiles lie in one and the same segment, key tile kt holds 64 real
+// keys and no position is negative: a pair is then allowed iff its
+// positions (and the window) allow it, so the per-element mask may skip the
+// segment compare, and two positions differ by less than 2^31, so one
+// unsigned compare of their difference tests order and window together.
 __device__ __forceinline__ bool tiles_oneseg(const TileSum& q, const TileSum& k, int kt, int p) {
-  return (kt + 1) * kBK <= p && q.seg_min == q.seg_max && k.seg_min == k.seg_max && k.seg_min == q.seg_min;
+  return (kt + 1) * kBK <= p && q.seg_min == q.seg_max && k.seg_min == k.seg_max && k.seg_min == q.seg_min &&
+         q.pos_min >= 0 && k.pos_min >= 0;
 }
 
 // Maximum of floats without the canonicalizing moves fmaxf needs (v_maximum3
@@ -162,10 +177,26 @@ __device__ __forceinline__ void lds_dma(i32x4 rsrc, uint32_t lds, int voffset) {
 }
 
 
+// Direct buffer-to-LDS load through the current M0: BYTES = 16 per lane from
+// base + voffset + OFF, written at LDS byte address M0 + OFF + 16 * lane (the
+// instruction offset moves both addresses). set_lds_m0 writes M0 (and the
+// wait state an LDS DMA needs after an M0 write); nothing else in the
+// kernels that use these touches M0.
+__device__ __forceinline__ void set_lds_m0(uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" :: "s"(lds) : "memory", "m0");
+}
+template <int OFF>
+__device__ __forceinline__ void lds_dma16_m0(i32x4 rsrc, int voffset) {
+  static_assert(OFF >= 0 && OFF < 4096, "instruction offset");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds" :: "v"(voffset), "s"(rsrc), "i"(OFF) : "memory");
+}
+
 // The prepared walk of a packed prefill (summaries, per query tile the key
 // tiles to visit and which of them need no mask, the costliest-first order),
-// built by three small kernels into the workspace; and its size.
-hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream);
+// built by three small kernels into the workspace; and its size. Query tiles
+// hold 32 tokens per wavefront of a head group: `waves` wavefronts per
+// workgroup (0: the forward kernel's own count).
+hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream, int waves = 0);
 // Summaries of pl's query tiles (pl.tq tokens) and, if pl.n_kt > 0, key tiles.
 hipError_t prefill_summarize(const PrefillArgs& a, const Plan& pl, hipStream_t stream);
 size_t prefill_plan_bytes(int p);

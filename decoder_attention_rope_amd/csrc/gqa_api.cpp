@@ -147,6 +147,8 @@ static int prefill_packed_impl(int32_t p, int32_t heads, int32_t kv_heads, int32
       segments == nullptr || out == nullptr)
     return GQA_ERR_INVALID_ARG;
   if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  // Each KV head's K (and V) is addressed through one 32-bit buffer range.
+  if ((long long)p * kv_heads * head_dim * 2 + 4096 >= (1LL << 31)) return GQA_ERR_UNSUPPORTED;
   if (p == 0) return GQA_OK;
   const size_t need = gqa::prefill_workspace_bytes(p, heads, kv_heads, head_dim);
   if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;

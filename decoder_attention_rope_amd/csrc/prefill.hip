@@ -112,7 +112,20 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(PrefillArgs a, Plan p
     }
     return;
   }
-  int first = pl.n_kt, last = -1, cnt = 0;
+  int first = pl.n_kt, last = -1, cnt = 0, nm = 0;
+  int* vis = pl.vis + (size_t)qt * pl.n_kt;
+  // The visit list holds the fully allowed tiles first: count them first.
+  int nf = 0;
+  for (int g = 0; g < pl.n_kg; ++g) {
+    const int kt = g * 64 + lane;
+    bool full = false;
+    if (kt < pl.n_kt) {
+      const TileSum k = pl.ksum[kt];
+      full = tiles_meet(q, k, a.window) && tiles_full(q, k, kt, a.p, a.window);
+    }
+    nf += __builtin_popcountll(__builtin_amdgcn_ballot_w64(full));
+  }
+  int rank_f = 0;
   for (int g = 0; g < pl.n_kg; ++g) {
     const int kt = g * 64 + lane;
     bool meet = false, full = false, one = false;
@@ -134,6 +147,15 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(PrefillArgs a, Plan p
       const unsigned long long w = lane < 2 ? vm : lane < 4 ? fm : om;
       pl.masks[((size_t)qt * pl.n_kg + g) * kMaskWords + lane] = (uint32_t)(w >> (32 * (lane & 1)));
     }
+    // Visit list in walk order: the fully allowed tiles, then the others,
+    // each in increasing kt (ranks by mbcnt over the ballots).
+    const unsigned long long mm = vm & ~fm;
+    const int rf = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(fm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)fm, 0u));
+    const int rm = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u));
+    if (full) vis[rank_f + rf] = kt;
+    else if (meet) vis[nf + nm + rm] = kt | ((one ? 1 : 2) << kVisMode);
+    rank_f += __builtin_popcountll(fm);
+    nm += __builtin_popcountll(mm);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -144,6 +166,7 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(PrefillArgs a, Plan p
   if (lane == 0) {
     pl.qrange[qt] = make_int2(first, last);
     pl.cost[qt] = cnt;
+    pl.nfull[qt] = nf;
   }
 }
 
@@ -196,16 +219,19 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_order_kernel(Plan pl) {
   __syncthreads();
   for (int i = tid; i < pl.n_qt; i += kPrepThreads) {
     const int qt = pl.order[i];
-    const int2 r = pl.qrange[qt];
-    const int g0 = (pl.n_kg > 0 && r.x <= r.y) ? r.x >> 6 : -1;
     int* rec = pl.rec + (size_t)i * kRecInts;
     rec[0] = qt;
-    rec[1] = r.x;
-    rec[2] = r.y;
-    rec[3] = g0;
-    for (int w = 0; w < kMaskWords; ++w)
-      rec[4 + w] = g0 >= 0 ? (int)pl.masks[((size_t)qt * pl.n_kg + g0) * kMaskWords + w] : 0;
-    for (int w = 4 + kMaskWords; w < kRecInts; ++w) rec[w] = 0;
+    if (pl.vis != nullptr) {
+      // Packed keys: the list's counts and its first entries in walk order.
+      const int nf = pl.nfull[qt], n = pl.cost[qt];
+      const int* vis = pl.vis + (size_t)qt * pl.n_kt;
+      rec[1] = nf;
+      rec[2] = n - nf;
+      rec[3] = 0;
+      for (int w = 0; w < kRecVis; ++w) rec[4 + w] = w < n ? vis[w] : 0;
+    } else {
+      for (int w = 1; w < kRecInts; ++w) rec[w] = 0;
+    }
   }
 }
 
@@ -250,14 +276,18 @@ __device__ __forceinline__ int vswz(int r) {
 // the tile loads run. Two 4-wave workgroups share a CU, so the two
 // wavefronts of a SIMD belong to different workgroups and never wait on each
 // other's barriers; with loads one tile ahead a workgroup's LDS (two K, two
-// V and three position buffers) lets two fit.
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillAhead = 1;
+// V and three position buffers) lets two fit. (Eight-wave workgroups alone
+// on a CU with loads two tiles ahead measure slower: the two wavefronts of a
+// SIMD then meet at every barrier.)
+template <int GW>
+constexpr int prefill_waves() { return 4; }
+template <int GW>
+constexpr int prefill_ahead() { return 1; }
 
 template <int D, int GW, int SRC>
-__global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill_kernel(PrefillArgs a, Plan pl) {
-  constexpr int NW = kPrefillWaves;
-  constexpr int AHEAD = kPrefillAhead;
+__global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) void prefill_kernel(PrefillArgs a, Plan pl) {
+  constexpr int NW = prefill_waves<GW>();
+  constexpr int AHEAD = prefill_ahead<GW>();
   constexpr int NKB = AHEAD + 1;  // K (and V) buffers
   constexpr int NPB = 4;          // position buffers (AHEAD + 2 used; a power of two)
   static_assert(AHEAD + 2 <= NPB, "position buffers");
@@ -295,10 +325,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   const int q_ld = q_valid ? q_tok : P - 1;  // lanes past P read a real row
   const int my_pos = a.positions[q_ld];
   const int my_seg = SRC == kSrcPacked || a.segments ? a.segments[q_ld] : 0;
-  // Packed keys: positions are token positions in [0, 2^31), so the
-  // difference of two fits in 32 bits and an unsigned compare tests
-  // pos_k <= pos_q together with the window.
+  // Packed keys. In one-segment tiles (mode 1) no position is negative, so
+  // two differ by less than 2^31 and one unsigned compare of the difference
+  // tests pos_k <= pos_q together with the window. The full predicate
+  // (mode 2) compares the positions as signed values, then the unsigned
+  // difference (exact once pos_k <= pos_q) against the window.
   const uint32_t wlim = a.window > 0 ? (uint32_t)a.window : 0x80000000u;
+  const uint32_t wlast = a.window > 0 ? (uint32_t)a.window - 1u : 0xffffffffu;
   // Cache keys: this query sees key slots [my_lo, my_hi] of cache row my_seg
   // (empty for a row outside the cache).
   const int my_hi = (my_seg >= 0 && my_seg < a.cache_rows) ? min(my_pos, a.cap - 1) : -1;
@@ -325,20 +358,22 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   float m_run = kNegInf;
   float l_run = 0.f;
 
-  int2 rng = make_int2(ld_const(rec, 1), ld_const(rec, 2));
-  rng.x = __builtin_amdgcn_readfirstlane(rng.x);
-  rng.y = __builtin_amdgcn_readfirstlane(rng.y);
-
   // Tile loads go straight from memory into LDS, AHEAD key tiles ahead of
   // the matrix work, spread over the workgroup's wavefronts: a K tile is
-  // L::kChunks 1-KiB loads (the last one by wave 0), a V tile D / 8, and for
+  // L::kChunks 1-KiB loads (wave w the KU consecutive ones from w KU, the
+  // last one wave 0), a V tile D / 8 (wave w the VU from w VU), and for
   // packed keys the positions (wave 1) and segments (wave 2) one 256-byte
-  // load each. Lane offsets (bytes from the tile's first row) are fixed per
-  // wavefront; padding lanes fetch out of range and write zeros.
+  // load each. A wavefront's K (V) loads share one M0, the instruction
+  // offset 1024 u moving both addresses; every buffer descriptor starts
+  // kShift bytes before its tile, so that lane offsets, less those
+  // instruction offsets, stay positive. Lane offsets (bytes from the tile's
+  // first row, plus kShift) are fixed per wavefront; padding lanes fetch out
+  // of range and write zeros.
   const int row_bytes = SRC == kSrcPacked ? a.kv_heads * D * 2 : D * 2;
   constexpr int KU = (L::kChunks - 1) / NW;  // K loads per wavefront, all waves
   constexpr int VU = (D / 8) / NW;           // V loads per wavefront
   static_assert(KU * NW == L::kChunks - 1 && VU * NW == D / 8, "loads cover the tiles");
+  static_assert(1024 * (KU > VU ? KU : VU) <= kShift, "instruction offsets");
   constexpr int kOob = 0x40000000;           // past every tile's range
   int k_voff[KU + 1], v_voff[VU];
   auto k_lane_off = [&](int i) {
@@ -347,13 +382,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     return ch == D / 8 ? kOob : kappa(row) * row_bytes + ch * 16;
   };
 #pragma unroll
-  for (int u = 0; u < KU; ++u) k_voff[u] = k_lane_off(wave + NW * u);
-  k_voff[KU] = k_lane_off(L::kChunks - 1);
+  for (int u = 0; u < KU; ++u) k_voff[u] = k_lane_off(wave * KU + u) + kShift - 1024 * u;
+  k_voff[KU] = k_lane_off(L::kChunks - 1) + kShift;
 #pragma unroll
   for (int u = 0; u < VU; ++u) {
-    const int p = 64 * (wave + NW * u) + lane;
+    const int p = 64 * (wave * VU + u) + lane;
     const int row = p / (D / 8), ch = p % (D / 8);
-    v_voff[u] = row * row_bytes + ((ch ^ vswz<D>(row)) << 4);
+    v_voff[u] = row * row_bytes + ((ch ^ vswz<D>(row)) << 4) + kShift - 1024 * u;
   }
   // Loads per wavefront per tile set, and the waits: a slot issues one K set
   // and one V set, and before its closing barrier waits for the sets the
@@ -381,22 +416,33 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   // one: packed keys of a single segment, the query tile's (mask by
   // positions only).
   struct TileRef {
-    int kt, r, page, rows, full, one;  // rows: cache slots of the tile anyone may see
+    int kt, r, page, rows, mode;  // rows: cache slots of the tile anyone may see;
+                                  // mode: 0 every pair allowed, 1 / 2 masked (see soft_slice)
   };
   // Buffer resource over one operand (K or V) of a key tile: 64 key slots of
-  // one cache plane, or 64 packed tokens at KV head kh.
+  // one cache plane, or 64 packed tokens at KV head kh; it starts kShift
+  // bytes before the tile. Packed keys: the range runs to the end of the
+  // operand (the host keeps p * row_bytes + kShift below 2^31), so rows past
+  // p read zeros; the per-tile work is two 64-bit adds and a subtraction.
+  const int tile_bytes = kBK * row_bytes;
+  const int nrec0 = P * row_bytes + kShift;
+  const unsigned long long kbase = reinterpret_cast<unsigned long long>(a.k) + 2ull * kh * D - kShift;
+  const unsigned long long vbase = reinterpret_cast<unsigned long long>(a.v) + 2ull * kh * D - kShift;
   auto tile_src = [&](TileRef t, const void* base) {
-    long long e0;
-    int n_rows;
     if constexpr (SRC != kSrcPacked) {
-      e0 = SRC == kSrcPaged ? ((long long)t.page * a.kv_heads + kh) * kBK * D
-                            : (((long long)t.r * a.kv_heads + kh) * a.cap + (long long)t.kt * kBK) * D;
-      n_rows = t.rows;
+      const long long e0 = SRC == kSrcPaged ? ((long long)t.page * a.kv_heads + kh) * kBK * D
+                                            : (((long long)t.r * a.kv_heads + kh) * a.cap + (long long)t.kt * kBK) * D;
+      return raw_rsrc(static_cast<const char*>(base) + 2 * e0 - kShift, (t.rows - 1) * row_bytes + 2 * D + kShift);
     } else {
-      e0 = (long long)t.kt * kBK * a.kv_heads * D + (long long)kh * D;
-      n_rows = min(kBK, P - t.kt * kBK);
+      const int off = t.kt * tile_bytes;
+      const unsigned long long b = (base == a.k ? kbase : vbase) + (unsigned)off;
+      i32x4 r;
+      r[0] = (int)(uint32_t)b;
+      r[1] = (int)(uint32_t)(b >> 32);  // device addresses are below 2^48: stride 0
+      r[2] = nrec0 - off;
+      r[3] = 0x00020000;
+      return r;
     }
-    return raw_rsrc(static_cast<const char*>(base) + 2 * e0, (n_rows - 1) * row_bytes + 2 * D);
   };
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   // Load u of a K set (tile t into K buffer kb and position buffer pb). The
@@ -405,34 +451,41 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   struct KSet {
     i32x4 rk, rx;
   };
-  const int* x_src = wave == 1 ? a.positions : a.segments;
+  const unsigned long long x_src = reinterpret_cast<unsigned long long>(wave == 1 ? a.positions : a.segments);
   const int x_lds = wave == 1 ? 0 : kBK * 4;
   auto k_set = [&](TileRef t) {
     KSet s;
     s.rk = tile_src(t, a.k);
     if constexpr (SRC == kSrcPacked) {
-      const int n_rows = min(kBK, P - t.kt * kBK);
-      s.rx = raw_rsrc(x_src + (long long)t.kt * kBK, 4 * n_rows);
+      const unsigned long long b = x_src + 4u * (unsigned)(t.kt * kBK);
+      s.rx[0] = (int)(uint32_t)b;
+      s.rx[1] = (int)(uint32_t)(b >> 32);
+      s.rx[2] = 4 * (P - t.kt * kBK);
+      s.rx[3] = 0x00020000;
     } else {
       s.rx = s.rk;
     }
     return s;
   };
-  auto k_load = [&](const KSet& s, int kb, int pb, auto uc) {
+  // xload: this tile's key positions and segments are needed (it is masked;
+  // a fully allowed tile never reads them).
+  auto k_load = [&](const KSet& s, int kb, int pb, bool xload, auto uc) {
     constexpr int u = decltype(uc)::value;
     if constexpr (u < KU) {
-      lds_dma<16>(s.rk, lds0 + L::kOff(kb) + 1024 * (wave + NW * u), k_voff[u]);
+      if constexpr (u == 0) set_lds_m0(lds0 + L::kOff(kb) + 1024 * KU * wave);
+      lds_dma16_m0<1024 * u>(s.rk, k_voff[u]);
     } else {
       if (wave == 0) {
         lds_dma<16>(s.rk, lds0 + L::kOff(kb) + 1024 * (L::kChunks - 1), k_voff[KU]);
-      } else if (SRC == kSrcPacked && wave < 3) {
+      } else if (SRC == kSrcPacked && wave < 3 && xload) {
         lds_dma<4>(s.rx, lds0 + L::posOff(pb) + x_lds, lane * 4);
       }
     }
   };
   auto v_load = [&](i32x4 rv, int vb, auto uc) {
     constexpr int u = decltype(uc)::value;
-    lds_dma<16>(rv, lds0 + L::vOff(vb) + 1024 * (wave + NW * u), v_voff[u]);
+    if constexpr (u == 0) set_lds_m0(lds0 + L::vOff(vb) + 1024 * VU * wave);
+    lds_dma16_m0<1024 * u>(rv, v_voff[u]);
   };
   // Wait until the tile loads of all but the last AHEAD - 1 slots have
   // landed (a slot issues KU + VU loads, one more on the waves with an extra
@@ -447,40 +500,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   // the compiler move memory accesses across it.
   auto barrier = [&]() { asm volatile("s_barrier" ::: "memory"); };
 
-  // Walk the visited key tiles with the prepared masks: scalar bit scans,
-  // one scalar load per group of 64 key tiles. Phase 0 visits the tiles in
-  // which every pair is allowed, phase 1 the others (the online softmax does
-  // not depend on the order of the key tiles), so each phase runs one
-  // specialized loop body.
-  // The masks of the first group come with the start record.
-  int vis_g = __builtin_amdgcn_readfirstlane(ld_const(rec, 3));
-  unsigned long long vis_m = (unsigned long long)(uint32_t)ld_const(rec, 4) | ((unsigned long long)(uint32_t)ld_const(rec, 5) << 32);
-  unsigned long long full_m = (unsigned long long)(uint32_t)ld_const(rec, 6) | ((unsigned long long)(uint32_t)ld_const(rec, 7) << 32);
-  unsigned long long one_m = (unsigned long long)(uint32_t)ld_const(rec, 8) | ((unsigned long long)(uint32_t)ld_const(rec, 9) << 32);
-  auto next_in = [&](int kt, int phase) {
-    while (kt <= rng.y) {
-      const int g = kt >> 6;
-      if (g != vis_g) {
-        const int* w = reinterpret_cast<const int*>(pl.masks) + ((long long)qt * pl.n_kg + g) * kMaskWords;
-        vis_m = (unsigned long long)(uint32_t)ld_const(w, 0) | ((unsigned long long)(uint32_t)ld_const(w, 1) << 32);
-        full_m = (unsigned long long)(uint32_t)ld_const(w, 2) | ((unsigned long long)(uint32_t)ld_const(w, 3) << 32);
-        one_m = (unsigned long long)(uint32_t)ld_const(w, 4) | ((unsigned long long)(uint32_t)ld_const(w, 5) << 32);
-        vis_g = g;
-      }
-      const unsigned long long m = (phase == 0 ? full_m : (vis_m & ~full_m)) >> (kt & 63);
-      if (m != 0) return __builtin_amdgcn_readfirstlane(kt + (int)__builtin_ctzll(m));  // in group vis_g
-      kt = (g + 1) << 6;
-    }
-    return rng.y + 1;
-  };
-  auto advance = [&](int kt, int& phase) {
-    int r = next_in(kt, phase);
-    if (r > rng.y && phase == 0) {
-      phase = 1;
-      r = next_in(rng.x, 1);
-    }
-    return r;
-  };
+  // Packed keys: walk the query tile's visit list (fully allowed tiles
+  // first; the online softmax does not depend on the order of the key
+  // tiles). The first kRecVis entries come with the start record.
+  const int v_n = __builtin_amdgcn_readfirstlane(ld_const(rec, 1)) + __builtin_amdgcn_readfirstlane(ld_const(rec, 2));
+  const int* visq = pl.vis + (long long)qt * pl.n_kt;
+  int v_i = 0;
 
   // Cache keys. Once per workgroup: the distinct cache rows of the query
   // tile's tokens, each with the smallest and largest position among them
@@ -566,7 +591,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   };
   bool c_started = false;
   auto cache_next = [&](int& phase) {
-    TileRef t{-1, 0, 0, 0, 0, 0};
+    TileRef t{-1, 0, 0, 0, 2};
     if (!c_started) {
       c_started = true;
       c_phase = c_single ? 0 : 1;
@@ -598,11 +623,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
         page = page_of(c_row, kt);
         if (page < 0 || page >= a.num_pages) continue;
       }
-      t = TileRef{kt, c_row, page, min(kBK, c_last - kt * kBK + 1), 0, 0};
+      t = TileRef{kt, c_row, page, min(kBK, c_last - kt * kBK + 1), 2};
       break;
     }
     phase = c_phase;
     t.kt = __builtin_amdgcn_readfirstlane(t.kt);
+    t.mode = __builtin_amdgcn_readfirstlane(phase == 0 ? 0 : 2);
     t.r = __builtin_amdgcn_readfirstlane(t.r);
     t.page = __builtin_amdgcn_readfirstlane(t.page);
     t.rows = __builtin_amdgcn_readfirstlane(t.rows);
@@ -637,7 +663,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   // Operand of slot step g: half-slot h = g / HS, step i = g % HS; even
   // steps are S^T MFMAs (K rows of half h of tile T), odd ones P.V MFMAs
   // (V^T of keys of half h of tile T - 1, two transposing reads).
-  auto operand = [&](const LdsByte* kb, const LdsByte* vb, auto gc) {
+  // kb: this lane's K row of the slot's K buffer; vb[md]: its V^T read
+  // address for block md of the slot's V buffer (per-slot VGPR bases, so
+  // every read below takes a small immediate offset).
+  auto operand = [&](const LdsByte* kb, const uint32_t* vb, auto gc) {
     constexpr int g = decltype(gc)::value;
     constexpr int h = g / HS, i = g % HS;
     if constexpr (i % 2 == 0) {
@@ -645,7 +674,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     } else {
       constexpr int j = i / 2, kk = j / MD, md = j % MD;
       typedef __attribute__((address_space(3))) bf16x4 LdsV4;
-      const LdsByte* p = vb + v_rd[md] + 16 * (2 * h + kk) * L::vStride;
+      const LdsByte* p = smem + vb[md] + 16 * (2 * h + kk) * L::vStride;
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsV4*)p);
       const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LdsV4*)(p + 4 * L::vStride));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -708,7 +737,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
               const int e = 4 * q4 + e4;
-              const bool ok = ((int)ksg[e4] == my_seg) & ((uint32_t)my_pos - kp[e4] < wlim) & (e < e_end);
+              const bool ok = ((int)ksg[e4] == my_seg) & ((int)kp[e4] <= my_pos) &
+                              ((uint32_t)my_pos - kp[e4] <= wlast) & (e < e_end);
               s[hb][8 * c + e] = ok ? s[hb][8 * c + e] : kNegInf;
             }
           }
@@ -782,22 +812,22 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
 
   // The key tiles in visiting order: phase 0 (every pair allowed) first,
   // then phase 1 (masked); the online softmax does not depend on the order.
-  auto valid = [&](TileRef t) { return SRC == kSrcPacked ? t.kt <= rng.y : t.kt >= 0; };
+  auto valid = [&](TileRef t) { return t.kt >= 0; };
   int wphase = 0;
-  int last_kt = -1;
   auto gen = [&]() {
-    TileRef t;
+    TileRef t{-1, 0, 0, 0, 2};
     if constexpr (SRC == kSrcPacked) {
-      const int kt = advance(last_kt < 0 ? rng.x : last_kt + 1, wphase);
-      t = TileRef{kt, 0, 0, 0, 0, 0};
-      if (kt <= rng.y) {
-        last_kt = kt;
-        t.one = (int)((one_m >> (kt & 63)) & 1ull);
+      if (v_i < v_n) {
+        const int* e = v_i < kRecVis ? rec + 4 : visq;
+        const int ent = __builtin_amdgcn_readfirstlane(ld_const(e, v_i));
+        t.kt = ent & ((1 << kVisMode) - 1);
+        t.mode = ent >> kVisMode;
+        ++v_i;
       }
     } else {
       t = cache_next(wphase);
+      t.mode = wphase == 0 ? 0 : 2;
     }
-    t.full = wphase == 0;
     return t;
   };
 
@@ -807,14 +837,21 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
   // (the previous one) exists (the softmax of its second half and its P.V
   // run). Unless `masked`, every pair of both tiles is allowed (a uniform
   // branch: one loop body serves both kinds of slot).
-  TileRef t_gen{-1, 0, 0, 0, 0, 0};
-  auto mode_of = [](TileRef t) { return t.full ? 0 : t.one ? 1 : 2; };
-  auto slot = [&](int mode, auto dosc, auto doprevc, TileRef t, TileRef tp, TileRef kn, TileRef vn, int T) {
+  TileRef t_gen{-1, 0, 0, 0, 2};
+  auto mode_of = [](TileRef t) { return t.mode; };
+  auto slot = [&](int mode_t, int mode_p, auto dosc, auto doprevc, TileRef t, TileRef tp, TileRef kn, TileRef vn, int T) {
     constexpr bool DO_S = decltype(dosc)::value;
     constexpr bool DO_PREV = decltype(doprevc)::value;
     const unsigned Tu = T;
-    const LdsByte* kb = smem + L::kOff(Tu % NKB) + k_rd;
-    const LdsByte* vb = smem + L::vOff((Tu + NKB - 1) % NKB);
+    uint32_t kb_off = L::kOff(Tu % NKB) + k_rd;
+    asm volatile("" : "+v"(kb_off));
+    const LdsByte* kb = smem + kb_off;
+    uint32_t vb[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      vb[md] = L::vOff((Tu + NKB - 1) % NKB) + v_rd[md];
+      asm volatile("" : "+v"(vb[md]));
+    }
     const LdsByte* pb_t = smem + L::posOff(Tu % NPB);
     const LdsByte* pb_p = smem + L::posOff((Tu + NPB - 1) % NPB);
     // Cache keys: this lane's visible slots relative to each tile; packed
@@ -842,7 +879,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
         if constexpr (decltype(has_mfma(gn{}))::value) ring[(g + 4) & 3] = operand(kb, vb, gn{});
       }
       if constexpr (DO_S && h == 0 && i < NLOAD) {
-        if constexpr (i <= KU) k_load(ks, (Tu + AHEAD) % NKB, (Tu + AHEAD) % NPB, std::integral_constant<int, i>{});
+        if constexpr (i <= KU) k_load(ks, (Tu + AHEAD) % NKB, (Tu + AHEAD) % NPB, AHEAD >= 2 || kn.mode != 0, std::integral_constant<int, i>{});
         else v_load(rv, (Tu + AHEAD - 1) % NKB, std::integral_constant<int, i - KU - 1>{});
       }
       if constexpr (DO_S && h == 1 && i == 0) t_gen = gen();
@@ -855,7 +892,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
           constexpr int c = decltype(cc)::value;
           if constexpr (2 + c * (HS - 2) / NSOFT == i)
             soft_slice(h == 0 ? pb_p : pb_t, h == 0 ? lo_p : lo_t, h == 0 ? hi_p : hi_t, h == 0 ? n_p : n_t,
-                       std::integral_constant<int, 1 - h>{}, cc, mode);
+                       std::integral_constant<int, 1 - h>{}, cc, h == 0 ? mode_p : mode_t);
         });
       }
       if constexpr (soft && i == HS - 1) rescale(alpha);
@@ -894,10 +931,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     // Prologue: K of the first AHEAD tiles and V of the first AHEAD - 1.
     {
       const KSet k0 = k_set(cur);
-      static_for<KU + 1>([&](auto uc) { k_load(k0, 0, 0, uc); });
+      static_for<KU + 1>([&](auto uc) { k_load(k0, 0, 0, AHEAD >= 2 || cur.mode != 0, uc); });
       if constexpr (AHEAD >= 2) {
         const KSet k1 = k_set(or_cur(n1, cur));
-        static_for<KU + 1>([&](auto uc) { k_load(k1, 1, 1, uc); });
+        static_for<KU + 1>([&](auto uc) { k_load(k1, 1, 1, true, uc); });
         const i32x4 r0 = tile_src(cur, a.v);
         static_for<VU>([&](auto uc) { v_load(r0, 0, uc); });
       }
@@ -905,20 +942,18 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
       wait_loads(extra_load);
       barrier();
     }
-    slot(mode_of(cur), T_{}, F_{}, cur, cur, kn_of(), vn_of(), 0);
+    slot(mode_of(cur), 0, T_{}, F_{}, cur, cur, kn_of(), vn_of(), 0);
     TileRef prev;
     shift(prev);
     int T = 1;
-    // Full tiles come first, so a slot whose tile is full has a full
-    // previous tile too; a slot's mask mode covers both of its tiles (a
-    // mode that masks more is always correct).
+    // Each half-slot masks by the mode of the tile whose softmax it runs.
     while (valid(cur)) {
-      slot(max(mode_of(cur), mode_of(prev)), T_{}, T_{}, cur, prev, kn_of(), vn_of(), T);
+      slot(mode_of(cur), mode_of(prev), T_{}, T_{}, cur, prev, kn_of(), vn_of(), T);
       shift(prev);
       ++T;
     }
     // Drain: the last tile's second half and its P.V.
-    slot(mode_of(prev), F_{}, T_{}, prev, prev, prev, prev, T);
+    slot(0, mode_of(prev), F_{}, T_{}, prev, prev, prev, prev, T);
   }
   // No tile load may still be writing this workgroup's LDS when it exits.
   __builtin_amdgcn_s_waitcnt(0xF70);
@@ -964,7 +999,8 @@ size_t prefill_plan_bytes(int p) {
   const size_t n_kg = (n_kt + 63) / 64;
   return align256(n_kt * sizeof(TileSum)) + align256(n_qt * sizeof(TileSum)) +
          align256(n_qt * sizeof(int2)) + 2 * align256(n_qt * sizeof(int)) +
-         align256(n_qt * n_kg * kMaskWords * sizeof(uint32_t)) + align256(n_qt * kRecInts * sizeof(int));
+         align256(n_qt * n_kg * kMaskWords * sizeof(uint32_t)) + align256(n_qt * kRecInts * sizeof(int)) +
+         align256(n_qt * sizeof(int)) + align256(n_qt * n_kt * sizeof(int));
 }
 
 size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim) {
@@ -977,17 +1013,18 @@ size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim) {
 template <int D, int GW>
 static void launch_main(const PrefillArgs& a, const Plan& pl, hipStream_t stream) {
   const int n_groups = a.kv_heads * pl.head_groups;
-  const dim3 grid(pl.n_qt * n_groups), block(64 * kPrefillWaves);
+  const dim3 grid(pl.n_qt * n_groups), block(64 * prefill_waves<GW>());
   if (a.src == kSrcContiguous) prefill_kernel<D, GW, kSrcContiguous><<<grid, block, 0, stream>>>(a, pl);
   else if (a.src == kSrcPaged) prefill_kernel<D, GW, kSrcPaged><<<grid, block, 0, stream>>>(a, pl);
   else prefill_kernel<D, GW, kSrcPacked><<<grid, block, 0, stream>>>(a, pl);
 }
 
-hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream) {
+hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream, int waves) {
   const int G = a.heads / a.kv_heads;
   pl.gw = group_width(G);
   pl.head_groups = G / pl.gw;
-  pl.tq = 32 * (kPrefillWaves / pl.gw);
+  if (waves <= 0) waves = pl.gw == 4 ? prefill_waves<4>() : pl.gw == 2 ? prefill_waves<2>() : prefill_waves<1>();
+  pl.tq = 32 * (waves / pl.gw);
   // Cache keys need no key-tile summaries or masks.
   pl.n_kt = a.src == kSrcPacked ? (a.p + kBK - 1) / kBK : 0;
   pl.n_qt = (a.p + pl.tq - 1) / pl.tq;
@@ -1007,6 +1044,12 @@ hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream) {
   const size_t n_kg_max = ((a.p + kBK - 1) / kBK + 63) / 64;
   pl.rec = reinterpret_cast<int*>(reinterpret_cast<char*>(pl.masks) +
                                   align256(n_qt_max * n_kg_max * kMaskWords * sizeof(uint32_t)));
+  pl.nfull = reinterpret_cast<int*>(reinterpret_cast<char*>(pl.rec) + align256(n_qt_max * kRecInts * sizeof(int)));
+  const size_t n_kt_max = (size_t)(a.p + kBK - 1) / kBK;
+  pl.vis = a.src == kSrcPacked
+               ? reinterpret_cast<int*>(reinterpret_cast<char*>(pl.nfull) + align256(n_qt_max * sizeof(int)))
+               : nullptr;
+  (void)n_kt_max;
 
   const int n_tiles = pl.n_kt + pl.n_qt;
   prefill_summarize_kernel<<<dim3((n_tiles + 3) / 4), dim3(256), 0, stream>>>(a, pl);

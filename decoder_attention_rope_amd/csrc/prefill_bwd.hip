@@ -713,7 +713,8 @@ hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t stream) {
   pa.ws = a.ws;
   pa.src = kSrcPacked;
   Plan pl;
-  hipError_t e = prefill_prepare(pa, pl, stream);
+  // The dQ kernel walks 4-wave query tiles (32 tokens of each head).
+  hipError_t e = prefill_prepare(pa, pl, stream, 4);
   if (e != hipSuccess) return e;
   char* ws = static_cast<char*>(a.ws) + prefill_plan_bytes(a.p);
   const size_t n_q32 = (size_t)(a.p + 31) / 32;

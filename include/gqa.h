@@ -79,10 +79,12 @@ extern "C" {
 #define GQA_PAGE_SIZE 64
 
 /*
- * gqa_rope_table -- the rotary tables of rope.linnet `tables<S, D, T>(theta)`.
- *   inv_freq[i] = exp(-(f32(i) * 2 / f32(D)) * log(theta)), i < D/2, in f32;
- *   angle[s, i] = f32(s) * inv_freq[i] (f32 product);
- *   table[0, s, i] = cast<T>(cos(angle)), table[1, s, i] = cast<T>(sin(angle)).
+ * gqa_rope_table -- the rotary tables of the Linnet "examples/01-llama" page,
+ * src/rope.linnet, `tables` (with THETA): per pair index i < D/2 an inverse
+ * frequency theta^(-2i/D), evaluated in f32 as i -> f32, times 2, divided by
+ * f32(D), negated, times f32(log(f32(theta))), exp; the angle at position s
+ * is the f32 product f32(s) * inv_freq[i]; table[0, s, i] holds its cosine
+ * and table[1, s, i] its sine, in f32 and then rounded to T.
  * Each f32 step is the correctly rounded f32 result (evaluated in fp64 on the
  * device and rounded), cos/sin rounded to f32 and then to T, nearest-even.
  * The page's [S, D] tables repeat every frequency in both halves of the head
@@ -166,9 +168,12 @@ int gqa_qkv_rope_write(int32_t n, int32_t hidden, int32_t heads, int32_t kv_head
  * window keeps it; grouped_attention then softmax-weights v.
  *   q [p, heads, D] and k, v [p, kv_heads, D] already rotated (see
  *   gqa_rope_write_kv); out [p, heads, D] of T.
- *   Built for T = bf16, D in {64, 128}; bf16 matrix cores, f32 softmax.
+ *   Built for T = bf16, D in {64, 128} and p * kv_heads * D * 2 + 4096 <
+ *   2^31 (else GQA_ERR_UNSUPPORTED); bf16 matrix cores, f32 softmax.
  *   workspace: device memory of at least gqa_prefill_packed_workspace(...)
- *   bytes (tile summaries and the schedule), 256-byte aligned.
+ *   bytes (tile summaries, the per-query-tile visit lists -- about
+ *   ceil(p / 32) * ceil(p / 64) * 4 bytes -- and the schedule), 256-byte
+ *   aligned.
  */
 int gqa_prefill_packed(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
                        int32_t dtype, float scale, int32_t window, const void* sinks,
