@@ -520,7 +520,9 @@ __global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) 
   __shared__ int sTokLo[SRC == kSrcPacked ? 1 : TQ];
   __shared__ int sTokHi[SRC == kSrcPacked ? 1 : TQ];
   __shared__ unsigned long long sLead[2];
+  __shared__ int sBad;
   unsigned long long lead0 = 0, lead1 = 0;
+  bool any_bad = false;
   if constexpr (SRC != kSrcPacked) {
     const int t = qt * TQ + tid;
     const bool tok = tid < TQ && t < P;
@@ -531,7 +533,11 @@ __global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) 
       sTokRow[tid] = row_ok ? trow : -1;
       sTokLo[tid] = tpos;
     }
+    if (tid == 0) sBad = 0;
     __syncthreads();
+    // A token whose row is outside the cache has no keys: its tile may not
+    // take the unmasked single-row path.
+    if (tok && !row_ok) sBad = 1;
     bool lead = row_ok;
     int lo = tpos, hi = tpos;
     if (row_ok) {
@@ -553,9 +559,10 @@ __global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) 
     __syncthreads();
     lead0 = sLead[0];
     lead1 = TQ > 64 ? sLead[1] : 0ull;
+    any_bad = sBad != 0;
   }
   const int n_lead = __builtin_popcountll(lead0) + __builtin_popcountll(lead1);
-  const bool c_single = n_lead == 1;
+  const bool c_single = n_lead == 1 && !any_bad;
   // Walk state: current leader token u, its row, key-tile range, last slot.
   int c_phase = 0, c_u = -1, c_row = 0, c_klo = 0, c_khi = -1, c_last = -1, c_kt = 0;
   int c_flo = 0, c_fhi = -1;

@@ -185,7 +185,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
   const bool q_valid = q_tok < P;
   const int q_ld = q_valid ? q_tok : P - 1;
   const int my_pos = a.positions[q_ld], my_seg = a.segments[q_ld];
-  const uint32_t wlim = a.window > 0 ? (uint32_t)a.window : 0x80000000u;
+  // The `own` predicate on signed positions, then the window on the
+  // unsigned difference (exact once pos_k <= pos_q).
+  const uint32_t wlast = a.window > 0 ? (uint32_t)a.window - 1u : 0xffffffffu;
   const float scale_log2 = a.scale * kLog2eB;
   const float lse2 = a.lse[(long long)q_ld * a.heads + h] * kLog2eB;
   const float dlt = delta[(long long)q_ld * a.heads + h];
@@ -304,7 +306,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
               const int j = j0 + (r + e - r4);
               bool ok = true;
               if constexpr (!FULL)
-                ok = ((int)ksw[r + e - r4] == my_seg) & ((uint32_t)my_pos - kpw[r + e - r4] < wlim) & (j < n_j);
+                ok = ((int)ksw[r + e - r4] == my_seg) & ((int)kpw[r + e - r4] <= my_pos) &
+                     ((uint32_t)my_pos - kpw[r + e - r4] <= wlast) & (j < n_j);
               const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -lse2)) : 0.f;
               ds2[e] = p * (dp[r + e] - dlt);
             }
@@ -432,7 +435,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
   // columns, dimensions 16 ks + 8 hf ..).
   auto produce = [&]() {
     const int pos_k = a.positions[key_ld], seg_k = a.segments[key_ld];
-    const uint32_t wlim = a.window > 0 ? (uint32_t)a.window : 0x80000000u;
+    const uint32_t wlast = a.window > 0 ? (uint32_t)a.window - 1u : 0xffffffffu;
     const float scale_log2 = a.scale * kLog2eB;
     const TileSum ks_sum = ld_const(ksum, kt);
     const uint16_t* kg = static_cast<const uint16_t*>(a.k) + ((long long)key_ld * a.kv_heads + kh) * D;
@@ -537,7 +540,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
             const float l2 = lse_r[r + e];  // lse * log2(e), staged as such
             bool ok = k_valid & meet;
             if constexpr (!FULL)
-              ok = ok & (qseg_r[r + e] == seg_k) & ((uint32_t)qpos_r[r + e] - (uint32_t)pos_k < wlim) & (iq < n_q);
+              ok = ok & (qseg_r[r + e] == seg_k) & (pos_k <= qpos_r[r + e]) &
+                   ((uint32_t)qpos_r[r + e] - (uint32_t)pos_k <= wlast) & (iq < n_q);
             const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
             p2[e] = p;
             d2[e] = p * (dp[r + e] - dl_r[r + e]);  // p is 0 where masked; dP, delta finite

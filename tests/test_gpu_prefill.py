@@ -77,6 +77,35 @@ def test_prefill_arbitrary_order_and_ids():
         assert_close(f64(out), ref, "bf16", f"prefill shuffled/duplicates W={window}")
 
 
+def extreme_position_layout(g):
+    """Packed segments whose positions span the int32 range: one at the top
+    (up to 2^31 - 1), one negative, one mixing the extremes with duplicates
+    and a plain one; differences of two positions reach 2^32 - 1."""
+    imax, imin = np.iinfo(np.int32).max, np.iinfo(np.int32).min
+    top = np.arange(imax - 149, imax + 1, dtype=np.int64)
+    neg = np.arange(-200, -80, dtype=np.int64)
+    mix = g["index"].choice(np.array([imin, imin + 1, imin + 5, -3, -1, 0, 2, imax - 4, imax - 1, imax],
+                                     dtype=np.int64), 90)
+    plain = np.arange(0, 64, dtype=np.int64)
+    pos = np.concatenate([top, neg, mix, plain]).astype(np.int32)
+    seg = np.concatenate([np.full(len(a), i) for i, a in enumerate((top, neg, mix, plain))]).astype(np.int32)
+    return pos, seg
+
+
+def test_prefill_extreme_positions():
+    """The literal `own` mask and window for positions anywhere in int32."""
+    heads, kvh, d = 32, 8, 128
+    g = W.streams(4343)
+    pos, seg = extreme_position_layout(g)
+    print(f"[case] prefill extreme positions P={len(pos)}", flush=True)
+    dv, hv, (sk, sk64), _ = make_inputs(4343, len(pos), heads, kvh, d)
+    o = oracle.default()
+    for window, sinks in ((0, None), (37, sk), (np.iinfo(np.int32).max, None)):
+        out = run_prefill(*dv, pos, seg, heads, kvh, d, window, sinks)
+        ref = o.packed(*hv, pos, seg, window=window, sinks=None if sinks is None else sk64)
+        assert_close(f64(out), ref, "bf16", f"prefill extreme positions W={window}")
+
+
 def test_prefill_descending_ids_offset_positions():
     """Key tiles that straddle segment boundaries with segment ids in
     descending order (a tile's smallest id sits in its later tokens) and

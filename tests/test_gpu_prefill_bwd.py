@@ -25,9 +25,13 @@ GRAD_TOL = 2e-2
 LSE_TOL = 1e-4
 
 
-def run_pair(seed, p, heads, kvh, d, lo, hi, window):
+def run_pair(seed, p, heads, kvh, d, lo, hi, window, layout=None):
     g = W.streams(seed)
-    lengths, pos, seg = W.segment_layout(p, lo, hi, g["index"])
+    if layout is None:
+        lengths, pos, seg = W.segment_layout(p, lo, hi, g["index"])
+    else:
+        pos, seg = layout
+        p = len(pos)
     q_t, q64 = host_values(W.normal(g["q"], (p, heads, d)), "bf16")
     k_t, k64 = host_values(W.normal(g["k"], (p, kvh, d)), "bf16")
     v_t, v64 = host_values(W.normal(g["v"], (p, kvh, d)), "bf16")
@@ -113,3 +117,22 @@ def test_backward_llama8b_packed_sampled():
     sl = slice(a, a + 600)
     dq_r, _, _ = o.packed_backward(q[sl], k[sl], v[sl], g[sl], pos[sl], seg[sl])
     check_grad(dq[sl], dq_r, f"dq first 600 of segment {li}")
+
+
+def test_backward_extreme_positions():
+    """dq, dk, dv under the literal `own` mask with positions anywhere in
+    int32 (differences up to 2^32 - 1), with and without a window."""
+    from tests.test_gpu_prefill import extreme_position_layout
+    heads, kvh, d = 8, 2, 128
+    layout = extreme_position_layout(W.streams(4344))
+    o = oracle.default()
+    for window in (0, 37):
+        print(f"[case] backward extreme positions W={window}", flush=True)
+        (out, lse, dq, dk, dv), (q, k, v, g), pos, seg = run_pair(4344, 0, heads, kvh, d, 0, 0, window,
+                                                                  layout=layout)
+        lse_ref = o.packed_lse(q, k, pos, seg, None, window)
+        assert np.max(np.abs(lse - lse_ref)) <= LSE_TOL
+        rq, rk, rv = o.packed_backward(q, k, v, g, pos, seg, None, window)
+        check_grad(dq, rq, "dq")
+        check_grad(dk, rk, "dk")
+        check_grad(dv, rv, "dv")

@@ -145,6 +145,36 @@ def test_prefill_cached_interleaved_and_invalid():
     assert_close(f64(out), ref, "bf16", "prefill_cached paged, invalid pages")
 
 
+def test_prefill_cached_single_row_tile_with_invalid_rows():
+    """A query tile whose valid tokens all read one cache row, plus tokens
+    whose row is -1 or past the cache: those get no keys and output 0 (the
+    tile must not take the unmasked single-row path), the others match the
+    oracle. Contiguous cache and paged pool."""
+    heads, kvh, d = 32, 8, 128
+    g = W.streams(2150)
+    batch, max_seq, n = 2, 600, 40
+    rows = np.ones(n, dtype=np.int32)
+    pos = np.arange(500, 500 + n, dtype=np.int32)
+    rows[5] = -1
+    rows[12] = batch + 3
+    ck, cv, ck64, cv64 = contiguous_cache(g, batch, kvh, max_seq, d, [max_seq - 1] * batch)
+    q_t, q64 = host_values(W.normal(g["q"], (n, heads, d)), "bf16")
+    o = oracle.default()
+    for window in (0, 300):
+        ref = o.prefill_cached(q64, rows, pos, ck64, cv64, window=window)
+        assert np.all(ref[5] == 0) and np.all(ref[12] == 0)
+        out = f64(run_cached(dev(q_t), rows, pos, gqa.GQA_CACHE_CONTIGUOUS, ck, cv, heads, kvh, d,
+                             batch, max_seq, window=window))
+        assert np.all(out[5] == 0) and np.all(out[12] == 0), "a token with no row got keys"
+        assert_close(out, ref, "bf16", f"prefill_cached one-row tile with invalid rows W={window}")
+    pk, pv, pk64, pv64, table = paged_from_contiguous(g, ck64, cv64)
+    ref = o.prefill_paged(q64, rows, pos, np.nan_to_num(pk64), np.nan_to_num(pv64), table)
+    out = f64(run_cached(dev(q_t), rows, pos, gqa.GQA_CACHE_PAGED_TABLE, pk, pv, heads, kvh, d,
+                         pk.shape[0], 64, table=table))
+    assert np.all(out[5] == 0) and np.all(out[12] == 0), "a token with no table row got keys"
+    assert_close(out, ref, "bf16", "prefill_cached paged one-row tile with invalid rows")
+
+
 def test_prefill_cached_rows_null_and_empty():
     heads, kvh, d = 8, 8, 64
     g = W.streams(2200)

@@ -34,11 +34,10 @@ def test_rope_table(d, max_pos, theta, dtype):
     got_c, got_s = f64(tab[0]), f64(tab[1])
     ref_c, ref_s = c[:, :d // 2], s[:, :d // 2]
     mism = int(np.sum(got_c != ref_c) + np.sum(got_s != ref_s))
-    # Both sides are the correctly rounded f32 value cast to T; a mismatch
-    # can only come from a last-bit difference of a library cos/sin/exp/log.
-    ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -23
-    assert np.max(np.abs(got_c - ref_c)) <= ulp and np.max(np.abs(got_s - ref_s)) <= ulp
-    assert mism <= max(1, got_c.size // 100000), f"{mism} table entries differ"
+    print(f"[parity] rope_table D={d} S={max_pos}: {mism} of {2 * got_c.size} entries differ", flush=True)
+    # Both sides round the f32 steps of the page's pipeline the same way and
+    # cast the f32 cos / sin to T: every entry must be identical.
+    assert mism == 0, f"{mism} table entries differ from the oracle"
     assert np.all(got_c[0] == 1.0) and np.all(got_s[0] == 0.0)
 
 
