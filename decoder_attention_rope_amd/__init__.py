@@ -15,6 +15,8 @@ import os
 __all__ = [
     "GQAError", "lib", "library_path",
     "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_WORKSPACE", "GQA_ERR_HIP",
+    "GQA_ERR_INDEX", "GQA_OP_PREFILL_PACKED", "GQA_OP_PREFILL_CACHED", "GQA_OP_PREFILL_BACKWARD",
+    "GQA_OP_DECODE_ROWS", "GQA_OP_DECODE_PAGED", "GQA_OP_STEP_PACKED", "GQA_OP_STEP_PAGED",
     "GQA_BF16", "GQA_F32", "GQA_CACHE_NONE", "GQA_CACHE_CONTIGUOUS", "GQA_CACHE_PAGED_TABLE",
     "GQA_CACHE_PAGED_SLOTS", "GQA_PAGE_SIZE",
     "gqa_rope_table", "gqa_rope_write_kv", "gqa_prefill_packed", "gqa_prefill_packed_workspace",
@@ -23,11 +25,15 @@ __all__ = [
     "gqa_qkv_rope_write", "gqa_prefill_packed_lse", "gqa_prefill_packed_backward",
     "gqa_prefill_packed_backward_workspace",
     "gqa_decode_rows", "gqa_decode_rows_workspace", "gqa_decode_paged",
-    "gqa_decode_paged_workspace", "gqa_status_string", "gqa_set_dry_run", "gqa_abi_version",
+    "gqa_decode_paged_workspace", "gqa_status_string", "gqa_status_str", "gqa_workspace_bytes",
+    "gqa_set_dry_run", "gqa_set_checked", "gqa_abi_version",
     "dtype_code",
 ]
 
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = 0, 1, 2, 3, 4
+GQA_ERR_INDEX = 5
+(GQA_OP_PREFILL_PACKED, GQA_OP_PREFILL_CACHED, GQA_OP_PREFILL_BACKWARD, GQA_OP_DECODE_ROWS,
+ GQA_OP_DECODE_PAGED, GQA_OP_STEP_PACKED, GQA_OP_STEP_PAGED) = range(7)
 GQA_BF16, GQA_F32 = 0, 1
 GQA_CACHE_NONE, GQA_CACHE_CONTIGUOUS, GQA_CACHE_PAGED_TABLE, GQA_CACHE_PAGED_SLOTS = 0, 1, 2, 3
 GQA_PAGE_SIZE = 64
@@ -89,7 +95,10 @@ _decode_paged = _sig("gqa_decode_paged", ctypes.c_int,
                       _vp, _vp, _vp, _vp, _sz, _vp])
 _decode_paged_ws = _sig("gqa_decode_paged_workspace", _sz, [_i32, _i32, _i32, _i32, _i32])
 _status_string = _sig("gqa_status_string", ctypes.c_char_p, [_i32])
+_status_str = _sig("gqa_status_str", ctypes.c_char_p, [_i32])
+_workspace_bytes = _sig("gqa_workspace_bytes", _sz, [_i32] * 7)
 _set_dry_run = _sig("gqa_set_dry_run", _i32, [_i32])
+_set_checked = _sig("gqa_set_checked", _i32, [_i32])
 _abi_version = _sig("gqa_abi_version", _i32, [])
 
 
@@ -138,8 +147,22 @@ def gqa_status_string(status):
     return _status_string(int(status)).decode()
 
 
+def gqa_status_str(status):
+    return _status_str(int(status)).decode()
+
+
+def gqa_workspace_bytes(op, heads, kv_heads, head_dim, n_tokens, n_rows, max_len):
+    return _workspace_bytes(op, heads, kv_heads, head_dim, n_tokens, n_rows, max_len)
+
+
 def gqa_set_dry_run(on):
+    """Dry run for calls made from the calling thread; returns the previous setting."""
     return _set_dry_run(1 if on else 0)
+
+
+def gqa_set_checked(on):
+    """Checked mode for calls made from the calling thread; returns the previous setting."""
+    return _set_checked(1 if on else 0)
 
 
 def gqa_abi_version():

@@ -5,15 +5,90 @@
 // synchronizes.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
+#include <cstdlib>
 
 #include "gqa.h"
 #include "internal.h"
 
 namespace {
 
-std::atomic<int32_t> g_dry_run{0};
+// Per calling thread: one thread's dry run or checked mode never changes
+// another thread's calls. Checked mode starts on when GQA_CHECK is set to
+// anything but "0" in the environment.
+thread_local int32_t g_dry_run = 0;
+int32_t env_checked() {
+  const char* e = std::getenv("GQA_CHECK");
+  return (e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0')) ? 1 : 0;
+}
+thread_local int32_t g_checked = env_checked();
+
+// Checked mode: run the index checks; GQA_ERR_INDEX if any value is out of
+// its range (nothing else is enqueued then).
+int run_checks(const gqa::IndexCheck* c, int n, void* stream) {
+  int bad = 0;
+  const hipError_t e = gqa::index_check(c, n, static_cast<hipStream_t>(stream), &bad);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  return bad != 0 ? GQA_ERR_INDEX : GQA_OK;
+}
+
+int clamp_i32(long long x) { return x > 0x7fffffffLL ? 0x7fffffff : (int)x; }
+
+// What each call's index arguments must satisfy in checked mode.
+gqa::IndexCheck check_rope_write(int n, const int32_t* positions, const void* rope_table,
+                                 int rope_max_pos, int cache_kind, int dim0, int seq,
+                                 const int32_t* rows, const int32_t* slots, const int32_t* table,
+                                 int table_rows, int table_pages) {
+  gqa::IndexCheck c{};
+  c.n = n;
+  c.positions = positions;
+  if (rope_table != nullptr) c.rope_hi = rope_max_pos;
+  if (cache_kind == GQA_CACHE_CONTIGUOUS) {
+    c.rows = rows;
+    c.rows_hi = dim0;
+    c.pos_hi = seq;
+  } else if (cache_kind == GQA_CACHE_PAGED_TABLE) {
+    c.rows = rows;
+    c.rows_hi = table_rows;
+    c.pos_hi = clamp_i32((long long)table_pages * GQA_PAGE_SIZE);
+    c.table = table;
+    c.table_rows = table_rows;
+    c.table_pages = table_pages;
+    c.num_pages = dim0;
+    c.table_mode = 1;
+  } else if (cache_kind == GQA_CACHE_PAGED_SLOTS) {
+    c.slots = slots;
+    c.slots_hi = clamp_i32((long long)dim0 * GQA_PAGE_SIZE);
+  }
+  return c;
+}
+
+gqa::IndexCheck check_decode_rows(int batch, int max_seq, const int32_t* positions) {
+  gqa::IndexCheck c{};
+  c.n = batch;
+  c.positions = positions;
+  c.pos_hi = max_seq;
+  return c;
+}
+
+gqa::IndexCheck check_paged_keys(int n, const int32_t* rows, bool row_is_token,
+                                 const int32_t* positions, const int32_t* table, int table_rows,
+                                 int table_pages, int num_pages, int window) {
+  gqa::IndexCheck c{};
+  c.n = n;
+  c.rows = rows;
+  c.row_is_token = row_is_token ? 1 : 0;
+  c.rows_hi = table_rows;
+  c.positions = positions;
+  c.pos_hi = clamp_i32((long long)table_pages * GQA_PAGE_SIZE);
+  c.table = table;
+  c.table_rows = table_rows;
+  c.table_pages = table_pages;
+  c.num_pages = num_pages;
+  c.table_mode = 2;
+  c.window = window;
+  return c;
+}
 constexpr float kLog2e = 1.4426950408889634f;
 
 bool supported_dim(int32_t d) { return d == 64 || d == 128; }
@@ -42,7 +117,17 @@ extern "C" {
 
 int32_t gqa_abi_version(void) { return 1; }
 
-int32_t gqa_set_dry_run(int32_t on) { return g_dry_run.exchange(on ? 1 : 0); }
+int32_t gqa_set_dry_run(int32_t on) {
+  const int32_t prev = g_dry_run;
+  g_dry_run = on ? 1 : 0;
+  return prev;
+}
+
+int32_t gqa_set_checked(int32_t on) {
+  const int32_t prev = g_checked;
+  g_checked = on ? 1 : 0;
+  return prev;
+}
 
 const char* gqa_status_string(int32_t status) {
   switch (status) {
@@ -56,10 +141,14 @@ const char* gqa_status_string(int32_t status) {
       return "workspace missing or too small";
     case GQA_ERR_HIP:
       return "HIP runtime error";
+    case GQA_ERR_INDEX:
+      return "index argument out of range (checked mode)";
     default:
       return "unknown status";
   }
 }
+
+const char* gqa_status_str(int32_t status) { return gqa_status_string(status); }
 
 int gqa_rope_table(int32_t head_dim, int32_t max_pos, float theta, int32_t dtype, void* table,
                    void* stream) {
@@ -68,7 +157,7 @@ int gqa_rope_table(int32_t head_dim, int32_t max_pos, float theta, int32_t dtype
   if (!(theta > 0.0f) || !std::isfinite(theta)) return GQA_ERR_INVALID_ARG;
   if (table == nullptr) return GQA_ERR_INVALID_ARG;
   if (!supported_dim(head_dim)) return GQA_ERR_UNSUPPORTED;
-  if (g_dry_run.load()) return GQA_OK;
+  if (g_dry_run) return GQA_OK;
   return hip_status(gqa::launch_rope_table(head_dim, max_pos, theta, dtype, table,
                                            static_cast<hipStream_t>(stream)));
 }
@@ -102,7 +191,14 @@ int gqa_rope_write_kv(int32_t n, int32_t heads, int32_t kv_heads, int32_t head_d
   } else if (rope_table == nullptr || (q == nullptr && k == nullptr)) {
     return GQA_ERR_INVALID_ARG;  // nothing to do is a caller error
   }
-  if (n == 0 || g_dry_run.load()) return GQA_OK;
+  if (n == 0 || g_dry_run) return GQA_OK;
+  if (g_checked) {
+    const gqa::IndexCheck c = check_rope_write(n, positions, rope_table, rope_max_pos, cache_kind,
+                                               cache_dim0, cache_seq, rows, slots, table,
+                                               table_rows, table_pages);
+    st = run_checks(&c, 1, stream);
+    if (st != GQA_OK) return st;
+  }
   gqa::RopeWriteArgs a;
   a.n = n;
   a.heads = heads;
@@ -182,7 +278,7 @@ int gqa_prefill_packed(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_
                        void* workspace, size_t workspace_bytes, void* stream) {
   return prefill_packed_impl(p, heads, kv_heads, head_dim, dtype, scale, window, sinks, q, k, v,
                              positions, segments, out, workspace, workspace_bytes, stream,
-                             !g_dry_run.load());
+                             !g_dry_run);
 }
 
 int gqa_prefill_packed_lse(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
@@ -194,7 +290,7 @@ int gqa_prefill_packed_lse(int32_t p, int32_t heads, int32_t kv_heads, int32_t h
   const int st = prefill_packed_impl(p, heads, kv_heads, head_dim, dtype, scale, window, nullptr, q, k,
                                      v, positions, segments, out, workspace, workspace_bytes, stream,
                                      false);
-  if (st != GQA_OK || p == 0 || g_dry_run.load()) return st;
+  if (st != GQA_OK || p == 0 || g_dry_run) return st;
   gqa::PrefillArgs a{};
   a.p = p;
   a.heads = heads;
@@ -243,7 +339,7 @@ int gqa_prefill_packed_backward(int32_t p, int32_t heads, int32_t kv_heads, int3
   const size_t need = gqa::prefill_bwd_workspace_bytes(p, heads);
   if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GQA_ERR_WORKSPACE;
-  if (g_dry_run.load()) return GQA_OK;
+  if (g_dry_run) return GQA_OK;
   gqa::BwdArgs a{};
   a.p = p;
   a.heads = heads;
@@ -280,7 +376,7 @@ static int prefill_cached_impl(int32_t n, int32_t heads, int32_t kv_heads, int32
                                int32_t cache_dim0, int32_t cache_seq, const int32_t* table,
                                int32_t table_rows, int32_t table_pages, void* out,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               bool launch) {
+                               bool launch, bool check) {
   if (n < 0 || window < 0) return GQA_ERR_INVALID_ARG;
   int st = check_heads(heads, kv_heads, head_dim, dtype);
   if (st != GQA_OK) return st;
@@ -303,6 +399,21 @@ static int prefill_cached_impl(int32_t n, int32_t heads, int32_t kv_heads, int32
   if (workspace == nullptr || workspace_bytes < need) return GQA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return GQA_ERR_WORKSPACE;
   if (!launch) return GQA_OK;
+  if (check) {
+    gqa::IndexCheck c{};
+    if (cache_kind == GQA_CACHE_CONTIGUOUS) {
+      c.n = n;
+      c.rows = rows;
+      c.rows_hi = cache_dim0;
+      c.positions = positions;
+      c.pos_hi = cache_seq;
+    } else {
+      c = check_paged_keys(n, rows, false, positions, table, table_rows, table_pages, cache_dim0,
+                           window);
+    }
+    st = run_checks(&c, 1, stream);
+    if (st != GQA_OK) return st;
+  }
   gqa::PrefillArgs a{};
   a.p = n;
   a.heads = heads;
@@ -345,7 +456,7 @@ int gqa_prefill_cached(int32_t n, int32_t heads, int32_t kv_heads, int32_t head_
   return prefill_cached_impl(n, heads, kv_heads, head_dim, dtype, scale, window, sinks, q, rows,
                              positions, cache_kind, cache_k, cache_v, cache_dim0, cache_seq, table,
                              table_rows, table_pages, out, workspace, workspace_bytes, stream,
-                             !g_dry_run.load());
+                             !g_dry_run, g_checked != 0);
 }
 
 static size_t decode_ws(int rows, int heads, int kv_heads, int head_dim, int dtype, int paged,
@@ -386,7 +497,7 @@ static int decode_rows_impl(int32_t batch, int32_t heads, int32_t kv_heads, int3
                     int32_t dtype, float scale, int32_t window, const void* sinks,
                     const void* q, const void* cache_k, const void* cache_v, int32_t max_seq,
                     const int32_t* positions, void* out, void* workspace,
-                    size_t workspace_bytes, void* stream, bool launch) {
+                    size_t workspace_bytes, void* stream, bool launch, bool check) {
   if (batch < 0 || window < 0 || max_seq <= 0) return GQA_ERR_INVALID_ARG;
   int st = check_heads(heads, kv_heads, head_dim, dtype);
   if (st != GQA_OK) return st;
@@ -395,6 +506,11 @@ static int decode_rows_impl(int32_t batch, int32_t heads, int32_t kv_heads, int3
       out == nullptr)
     return GQA_ERR_INVALID_ARG;
   if (batch == 0) return GQA_OK;
+  if (launch && check) {
+    const gqa::IndexCheck c = check_decode_rows(batch, max_seq, positions);
+    st = run_checks(&c, 1, stream);
+    if (st != GQA_OK) return st;
+  }
   gqa::DecodeArgs a{};
   a.rows = batch;
   a.heads = heads;
@@ -424,14 +540,15 @@ int gqa_decode_rows(int32_t batch, int32_t heads, int32_t kv_heads, int32_t head
                     size_t workspace_bytes, void* stream) {
   return decode_rows_impl(batch, heads, kv_heads, head_dim, dtype, scale, window, sinks, q, cache_k,
                           cache_v, max_seq, positions, out, workspace, workspace_bytes, stream,
-                          !g_dry_run.load());
+                          !g_dry_run, g_checked != 0);
 }
 
 static int decode_paged_impl(int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
                      int32_t head_dim, int32_t dtype, float scale, int32_t window,
                      const void* sinks, const void* q, const void* pool_k, const void* pool_v,
                      int32_t num_pages, const int32_t* positions, const int32_t* table,
-                     void* out, void* workspace, size_t workspace_bytes, void* stream, bool launch) {
+                     void* out, void* workspace, size_t workspace_bytes, void* stream, bool launch,
+                     bool check) {
   if (rows < 0 || pages <= 0 || num_pages <= 0 || window < 0) return GQA_ERR_INVALID_ARG;
   if ((long long)pages * GQA_PAGE_SIZE > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
   int st = check_heads(heads, kv_heads, head_dim, dtype);
@@ -441,6 +558,12 @@ static int decode_paged_impl(int32_t rows, int32_t pages, int32_t heads, int32_t
       table == nullptr || out == nullptr)
     return GQA_ERR_INVALID_ARG;
   if (rows == 0) return GQA_OK;
+  if (launch && check) {
+    const gqa::IndexCheck c =
+        check_paged_keys(rows, nullptr, true, positions, table, rows, pages, num_pages, window);
+    st = run_checks(&c, 1, stream);
+    if (st != GQA_OK) return st;
+  }
   gqa::DecodeArgs a{};
   a.rows = rows;
   a.heads = heads;
@@ -470,7 +593,7 @@ int gqa_decode_paged(int32_t rows, int32_t pages, int32_t heads, int32_t kv_head
                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
   return decode_paged_impl(rows, pages, heads, kv_heads, head_dim, dtype, scale, window, sinks, q,
                            pool_k, pool_v, num_pages, positions, table, out, workspace,
-                           workspace_bytes, stream, !g_dry_run.load());
+                           workspace_bytes, stream, !g_dry_run, g_checked != 0);
 }
 
 
@@ -509,7 +632,7 @@ int gqa_step_packed(int32_t batch, int32_t p, int32_t heads, int32_t kv_heads, i
   const size_t pre_ws = p > 0 ? align_up_256(gqa_prefill_packed_workspace(p, heads, kv_heads, head_dim)) : 0;
   char* ws = static_cast<char*>(workspace);
   // Validate both parts before enqueuing either (dry-run validation first).
-  const bool launch = !g_dry_run.load();
+  const bool launch = !g_dry_run;
   int s1 = p > 0 ? prefill_packed_impl(p, heads, kv_heads, head_dim, dtype, scale, window, sinks,
                                       static_cast<const char*>(q) + batch * row, k, v, positions,
                                       segments, static_cast<char*>(out) + batch * row, ws,
@@ -518,15 +641,21 @@ int gqa_step_packed(int32_t batch, int32_t p, int32_t heads, int32_t kv_heads, i
   int s2 = batch > 0 ? decode_rows_impl(batch, heads, kv_heads, head_dim, dtype, scale, window,
                                         sinks, q, cache_k, cache_v, max_seq, step_positions, out,
                                         ws == nullptr ? nullptr : ws + pre_ws,
-                                        workspace_bytes - pre_ws, stream, false)
+                                        workspace_bytes - pre_ws, stream, false, false)
                      : GQA_OK;
   if (s1 != GQA_OK) return s1;
   if (s2 != GQA_OK) return s2;
   if (!launch) return GQA_OK;
+  if (g_checked && batch > 0) {
+    // The packed part's positions and segments take any value.
+    const gqa::IndexCheck c = check_decode_rows(batch, max_seq, step_positions);
+    st = run_checks(&c, 1, stream);
+    if (st != GQA_OK) return st;
+  }
   if (batch > 0) {
     s2 = decode_rows_impl(batch, heads, kv_heads, head_dim, dtype, scale, window, sinks, q, cache_k,
                           cache_v, max_seq, step_positions, out, ws + pre_ws,
-                          workspace_bytes - pre_ws, stream, true);
+                          workspace_bytes - pre_ws, stream, true, false);
     if (s2 != GQA_OK) return s2;
   }
   if (p > 0)
@@ -561,34 +690,46 @@ int gqa_step_paged(int32_t p, int32_t rows, int32_t pages, int32_t heads, int32_
   const size_t row = (size_t)heads * head_dim * 2;
   const size_t pre_ws = p > 0 ? align_up_256(gqa_prefill_cached_workspace(p, heads, kv_heads, head_dim)) : 0;
   char* ws = static_cast<char*>(workspace);
-  const bool launch = !g_dry_run.load();
+  const bool launch = !g_dry_run;
   int s1 = p > 0 ? prefill_cached_impl(p, heads, kv_heads, head_dim, dtype, scale, window, sinks, q,
                                        token_rows, positions, GQA_CACHE_PAGED_TABLE, pool_k, pool_v,
                                        num_pages, GQA_PAGE_SIZE, table, rows, pages, out, ws,
-                                       pre_ws, stream, false)
+                                       pre_ws, stream, false, false)
                  : GQA_OK;
   int s2 = rows > 0 ? decode_paged_impl(rows, pages, heads, kv_heads, head_dim, dtype, scale, window,
                                         sinks, static_cast<const char*>(q) + p * row, pool_k,
                                         pool_v, num_pages, step_positions, table,
                                         static_cast<char*>(out) + p * row,
                                         ws == nullptr ? nullptr : ws + pre_ws,
-                                        workspace_bytes - pre_ws, stream, false)
+                                        workspace_bytes - pre_ws, stream, false, false)
                     : GQA_OK;
   if (s1 != GQA_OK) return s1;
   if (s2 != GQA_OK) return s2;
   if (!launch) return GQA_OK;
+  if (g_checked) {
+    gqa::IndexCheck c[2];
+    int nc = 0;
+    if (p > 0)
+      c[nc++] = check_paged_keys(p, token_rows, false, positions, table, rows, pages, num_pages,
+                                 window);
+    if (rows > 0)
+      c[nc++] = check_paged_keys(rows, nullptr, true, step_positions, table, rows, pages, num_pages,
+                                 window);
+    st = run_checks(c, nc, stream);
+    if (st != GQA_OK) return st;
+  }
   if (rows > 0) {
     s2 = decode_paged_impl(rows, pages, heads, kv_heads, head_dim, dtype, scale, window, sinks,
                            static_cast<const char*>(q) + p * row, pool_k, pool_v, num_pages,
                            step_positions, table, static_cast<char*>(out) + p * row, ws + pre_ws,
-                           workspace_bytes - pre_ws, stream, true);
+                           workspace_bytes - pre_ws, stream, true, false);
     if (s2 != GQA_OK) return s2;
   }
   if (p > 0)
     return prefill_cached_impl(p, heads, kv_heads, head_dim, dtype, scale, window, sinks, q,
                                token_rows, positions, GQA_CACHE_PAGED_TABLE, pool_k, pool_v,
                                num_pages, GQA_PAGE_SIZE, table, rows, pages, out, ws, pre_ws,
-                               stream, true);
+                               stream, true, false);
   return GQA_OK;
 }
 
@@ -623,7 +764,14 @@ int gqa_qkv_rope_write(int32_t n, int32_t hidden, int32_t heads, int32_t kv_head
   if (hidden % 64 != 0 || ((long long)(heads + 2 * kv_heads) * head_dim) % 128 != 0)
     return GQA_ERR_UNSUPPORTED;
   if (((long long)n + 128) * hidden * 2 > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
-  if (n == 0 || g_dry_run.load()) return GQA_OK;
+  if (n == 0 || g_dry_run) return GQA_OK;
+  if (g_checked) {
+    const gqa::IndexCheck c = check_rope_write(n, positions, rope_table, rope_max_pos, cache_kind,
+                                               cache_dim0, cache_seq, rows, slots, table,
+                                               table_rows, table_pages);
+    st = run_checks(&c, 1, stream);
+    if (st != GQA_OK) return st;
+  }
   gqa::QkvArgs a{};
   a.n = n;
   a.hidden = hidden;
@@ -660,4 +808,27 @@ int gqa_qkv_rope_write(int32_t n, int32_t hidden, int32_t heads, int32_t kv_head
   a.wr.table_pages = table_pages;
   return hip_status(gqa::launch_qkv(a, static_cast<hipStream_t>(stream)));
 }
+
+size_t gqa_workspace_bytes(int32_t op, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                           int32_t n_tokens, int32_t n_rows, int32_t max_len) {
+  switch (op) {
+    case GQA_OP_PREFILL_PACKED:
+      return gqa_prefill_packed_workspace(n_tokens, heads, kv_heads, head_dim);
+    case GQA_OP_PREFILL_CACHED:
+      return gqa_prefill_cached_workspace(n_tokens, heads, kv_heads, head_dim);
+    case GQA_OP_PREFILL_BACKWARD:
+      return gqa_prefill_packed_backward_workspace(n_tokens, heads, kv_heads, head_dim);
+    case GQA_OP_DECODE_ROWS:
+      return gqa_decode_rows_workspace(n_rows, heads, kv_heads, head_dim, max_len);
+    case GQA_OP_DECODE_PAGED:
+      return gqa_decode_paged_workspace(n_rows, max_len, heads, kv_heads, head_dim);
+    case GQA_OP_STEP_PACKED:
+      return gqa_step_packed_workspace(n_rows, n_tokens, heads, kv_heads, head_dim, max_len);
+    case GQA_OP_STEP_PAGED:
+      return gqa_step_paged_workspace(n_tokens, n_rows, max_len, heads, kv_heads, head_dim);
+    default:
+      return 0;
+  }
+}
+
 }  // extern "C"

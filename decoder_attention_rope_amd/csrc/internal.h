@@ -138,4 +138,24 @@ struct BwdArgs {
 size_t prefill_bwd_workspace_bytes(int p, int heads);
 hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t stream);
 
+// Checked mode: one validation pass over n tokens' index arguments. A field
+// left null / 0 is not checked.
+struct IndexCheck {
+  int n;
+  const int32_t* rows;       // rows[t] in [0, rows_hi) (null: row 0, or t if row_is_token)
+  int rows_hi;
+  int row_is_token;
+  const int32_t* positions;  // positions[t] in [0, pos_hi) (cache) and [0, rope_hi) (rotary table)
+  int pos_hi, rope_hi;
+  const int32_t* slots;      // slots[t] in [0, slots_hi)
+  int slots_hi;
+  const int32_t* table;      // [table_rows, table_pages] page ids in [0, num_pages)
+  int table_rows, table_pages, num_pages;
+  int table_mode;            // 1: the page of positions[t]; 2: the pages of its key range
+  int window;
+};
+// Runs the checks on `stream`, waits for them, and returns the number of
+// values found outside their range in *violations.
+hipError_t index_check(const IndexCheck* checks, int n_checks, hipStream_t stream, int* violations);
+
 }  // namespace gqa

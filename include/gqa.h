@@ -42,11 +42,21 @@
  *   Index values held in device memory (positions, rows, slots, table
  *   entries, segments) are not checked on the host; the kernels give every
  *   value a defined, memory-safe meaning, stated per entry point below.
+ * - Checked mode (gqa_set_checked(1), or GQA_CHECK set to anything but "0"
+ *   in the environment when a thread starts): before enqueuing its kernels,
+ *   a call validates its index arguments on the device -- cache rows,
+ *   positions (against the cache capacity and the rotary table), slots, and
+ *   the page-table entries of the pages it reads or writes -- and returns
+ *   GQA_ERR_INDEX, enqueuing nothing else, if any is out of range. The check
+ *   waits for `stream` (checked mode synchronizes; it is for debugging) and
+ *   calls in checked mode on one device take turns. Packed prefill (and its
+ *   training pair) have no index constraints: any positions and segment ids
+ *   are meaningful.
  * - Determinism: identical inputs give bitwise identical outputs (no float
  *   atomics; the split schedule depends only on the shapes).
  * - Thread safety: calls may be made from any host thread.
- * - Dry run: after gqa_set_dry_run(1), calls validate and return without any
- *   HIP call (for hosts without a GPU).
+ * - Dry run: after gqa_set_dry_run(1), calls made by the same host thread
+ *   validate and return without any HIP call (for hosts without a GPU).
  */
 #ifndef GQA_H_
 #define GQA_H_
@@ -64,6 +74,7 @@ extern "C" {
 #define GQA_ERR_UNSUPPORTED 2 /* valid, but this dtype / head dim / op is not built */
 #define GQA_ERR_WORKSPACE 3   /* workspace missing or smaller than required */
 #define GQA_ERR_HIP 4         /* a HIP runtime call or kernel launch failed */
+#define GQA_ERR_INDEX 5       /* checked mode: an index argument is out of range */
 
 /* Element types. */
 #define GQA_BF16 0
@@ -350,11 +361,36 @@ int gqa_step_paged(int32_t p, int32_t rows, int32_t pages, int32_t heads, int32_
 size_t gqa_step_paged_workspace(int32_t p, int32_t rows, int32_t pages, int32_t heads,
                                 int32_t kv_heads, int32_t head_dim);
 
-/* Human-readable name of a status code (static storage). */
+/* Human-readable name of a status code (static storage); gqa_status_str is
+ * the same function. */
 const char* gqa_status_string(int32_t status);
+const char* gqa_status_str(int32_t status);
 
-/* Dry-run switch (process-wide); returns the previous setting. */
+/*
+ * gqa_workspace_bytes -- the workspace query of an operation, one entry for
+ * all of them (the per-operation *_workspace functions above give the same
+ * numbers). n_tokens: p (packed / backward / step prefill tokens) or n
+ * (cached prefill); n_rows: decode rows (batch); max_len: max_seq
+ * (contiguous decode, step_packed) or pages per table row (paged decode,
+ * step_paged). Arguments an operation does not use are ignored; an unknown
+ * op returns 0.
+ */
+#define GQA_OP_PREFILL_PACKED 0
+#define GQA_OP_PREFILL_CACHED 1
+#define GQA_OP_PREFILL_BACKWARD 2
+#define GQA_OP_DECODE_ROWS 3
+#define GQA_OP_DECODE_PAGED 4
+#define GQA_OP_STEP_PACKED 5
+#define GQA_OP_STEP_PAGED 6
+size_t gqa_workspace_bytes(int32_t op, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                           int32_t n_tokens, int32_t n_rows, int32_t max_len);
+
+/* Dry-run switch of the calling host thread; returns the previous setting. */
 int32_t gqa_set_dry_run(int32_t on);
+
+/* Checked-mode switch of the calling host thread (see the conventions
+ * above); returns the previous setting. */
+int32_t gqa_set_checked(int32_t on);
 
 /* ABI version of this header. */
 int32_t gqa_abi_version(void);

@@ -263,3 +263,64 @@ def test_training_entries_argument_checks(g):
     bwd(unsup, dtype=1)
     bwd(ws_err, wsb=16)
     bwd(ws_err, ws=257)
+
+
+def test_workspace_bytes_matches_per_op_queries(g):
+    for heads, kvh, d in ((32, 8, 128), (64, 8, 64), (12, 12, 64)):
+        for n, rows, max_len in ((1, 1, 1), (333, 5, 64), (16384, 64, 128), (4096, 32, 1024)):
+            assert g.gqa_workspace_bytes(g.GQA_OP_PREFILL_PACKED, heads, kvh, d, n, rows, max_len) == \
+                g.gqa_prefill_packed_workspace(n, heads, kvh, d)
+            assert g.gqa_workspace_bytes(g.GQA_OP_PREFILL_CACHED, heads, kvh, d, n, rows, max_len) == \
+                g.gqa_prefill_cached_workspace(n, heads, kvh, d)
+            assert g.gqa_workspace_bytes(g.GQA_OP_PREFILL_BACKWARD, heads, kvh, d, n, rows, max_len) == \
+                g.gqa_prefill_packed_backward_workspace(n, heads, kvh, d)
+            assert g.gqa_workspace_bytes(g.GQA_OP_DECODE_ROWS, heads, kvh, d, n, rows, max_len) == \
+                g.gqa_decode_rows_workspace(rows, heads, kvh, d, max_len)
+            assert g.gqa_workspace_bytes(g.GQA_OP_DECODE_PAGED, heads, kvh, d, n, rows, max_len) == \
+                g.gqa_decode_paged_workspace(rows, max_len, heads, kvh, d)
+            assert g.gqa_workspace_bytes(g.GQA_OP_STEP_PACKED, heads, kvh, d, n, rows, max_len) == \
+                g.gqa_step_packed_workspace(rows, n, heads, kvh, d, max_len)
+            assert g.gqa_workspace_bytes(g.GQA_OP_STEP_PAGED, heads, kvh, d, n, rows, max_len) == \
+                g.gqa_step_paged_workspace(n, rows, max_len, heads, kvh, d)
+    assert g.gqa_workspace_bytes(99, 32, 8, 128, 100, 1, 1) == 0
+
+
+def test_status_names(g):
+    for st in range(7):
+        assert g.gqa_status_str(st) == g.gqa_status_string(st)
+    assert "index" in g.gqa_status_str(g.GQA_ERR_INDEX)
+    assert g.gqa_status_str(99) == "unknown status"
+
+
+def test_dry_run_and_checked_mode_are_per_thread(g):
+    """One thread's switches never reach another thread's calls."""
+    import threading
+    seen = {}
+
+    def other():
+        seen["dry"] = g.gqa_set_dry_run(0)      # this thread's own setting: off
+        seen["checked"] = g.gqa_set_checked(1)  # on here only
+        seen["checked_back"] = g.gqa_set_checked(0)
+
+    prev_checked = g.gqa_set_checked(0)
+    assert g.gqa_set_dry_run(1) == 1            # the fixture turned it on for this thread
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen == {"dry": 0, "checked": 0, "checked_back": 1}
+    assert g.gqa_set_checked(prev_checked) == 0  # unchanged by the other thread
+
+
+def test_checked_mode_from_environment():
+    """GQA_CHECK in the environment turns checked mode on for every thread."""
+    import subprocess
+    import sys
+    code = ("import decoder_attention_rope_amd as g, threading; r = [g.gqa_set_checked(0)]; "
+            "t = threading.Thread(target=lambda: r.append(g.gqa_set_checked(0))); t.start(); t.join(); "
+            "print(r)")
+    for val, want in (("1", "[1, 1]"), ("0", "[0, 0]")):
+        env = dict(os.environ, GQA_CHECK=val)
+        out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                             text=True, timeout=120)
+        assert out.returncode == 0, out.stderr
+        assert out.stdout.strip() == want, out.stdout
