@@ -25,13 +25,15 @@ __all__ = [
     "gqa_qkv_rope_write", "gqa_prefill_packed_lse", "gqa_prefill_packed_backward",
     "gqa_prefill_packed_backward_workspace",
     "gqa_decode_rows", "gqa_decode_rows_workspace", "gqa_decode_paged",
-    "gqa_decode_paged_workspace", "gqa_status_string", "gqa_status_str", "gqa_workspace_bytes",
+    "gqa_decode_paged_workspace", "gqa_decode_paged_noalloc", "GQA_DECODE_SCRATCH_BYTES",
+    "gqa_status_string", "gqa_status_str", "gqa_workspace_bytes",
     "gqa_set_dry_run", "gqa_set_checked", "gqa_abi_version",
     "dtype_code",
 ]
 
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = 0, 1, 2, 3, 4
 GQA_ERR_INDEX = 5
+GQA_DECODE_SCRATCH_BYTES = 16 << 20
 (GQA_OP_PREFILL_PACKED, GQA_OP_PREFILL_CACHED, GQA_OP_PREFILL_BACKWARD, GQA_OP_DECODE_ROWS,
  GQA_OP_DECODE_PAGED, GQA_OP_STEP_PACKED, GQA_OP_STEP_PAGED) = range(7)
 GQA_BF16, GQA_F32 = 0, 1
@@ -94,6 +96,9 @@ _decode_paged = _sig("gqa_decode_paged", ctypes.c_int,
                      [_i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _i32,
                       _vp, _vp, _vp, _vp, _sz, _vp])
 _decode_paged_ws = _sig("gqa_decode_paged_workspace", _sz, [_i32, _i32, _i32, _i32, _i32])
+_decode_paged_noalloc = _sig("gqa_decode_paged_noalloc", ctypes.c_int,
+                             [_i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp,
+                              _i32, _vp, _vp, _vp, _vp])
 _status_string = _sig("gqa_status_string", ctypes.c_char_p, [_i32])
 _status_str = _sig("gqa_status_str", ctypes.c_char_p, [_i32])
 _workspace_bytes = _sig("gqa_workspace_bytes", _sz, [_i32] * 7)
@@ -297,3 +302,11 @@ def gqa_decode_paged(rows, pages, heads, kv_heads, head_dim, dtype, scale, windo
                          _ptr(positions), _ptr(table), _ptr(out), _ptr(workspace),
                          workspace_bytes, _stream(stream)),
            "gqa_decode_paged")
+
+
+def gqa_decode_paged_noalloc(rows, pages, heads, kv_heads, head_dim, dtype, scale, window, sinks,
+                             q, pool_k, pool_v, num_pages, positions, table, out, stream=None):
+    _check(_decode_paged_noalloc(rows, pages, heads, kv_heads, head_dim, dtype, scale, window,
+                                 _ptr(sinks), _ptr(q), _ptr(pool_k), _ptr(pool_v), num_pages,
+                                 _ptr(positions), _ptr(table), _ptr(out), _stream(stream)),
+           "gqa_decode_paged_noalloc")

@@ -19,6 +19,8 @@
 // butterfly shuffles, and the split's scores live in LDS between the QK and
 // PV phases (one exp per score). It serves f32, contiguous caches and every
 // head-group size.
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 
@@ -313,6 +315,49 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   decode_merge_kernel<T, D><<<dim3(a.kv_heads, a.rows), 256, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+// Bytes of split partials the launch below will write for `a` (0 when the
+// matrix-core path covers each row with one split and writes the output
+// itself).
+size_t decode_partials_bytes(const DecodeArgs& a) {
+  int nsplit;
+  if (decode_mfma_supported(a)) {
+    const int sl = decode_mfma_split_len(a.rows, a.kv_heads, a.cap);
+    nsplit = (a.cap + sl - 1) / sl;
+    if (nsplit == 1) return 0;
+  } else {
+    decode_plan(a.rows, a.heads, a.kv_heads, a.head_dim, a.dtype, a.paged, a.cap, nullptr, &nsplit,
+                nullptr);
+  }
+  return (size_t)a.rows * a.heads * nsplit * (a.head_dim + 2) * sizeof(float);
+}
+
+// Scratch of the entry point that allocates nothing: the split partials live
+// in this module array (each GPU the library runs on holds its own copy for
+// the life of the process). In host code the name `scratch` is only a
+// stand-in: its device address, per device, comes from hipGetSymbolAddress
+// on the first call made with that device current, and only that address is
+// handed to kernels. Calls that overlap on one GPU share it and race.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = static_cast<float*>(p);
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {

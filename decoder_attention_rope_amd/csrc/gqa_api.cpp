@@ -548,7 +548,7 @@ static int decode_paged_impl(int32_t rows, int32_t pages, int32_t heads, int32_t
                      const void* sinks, const void* q, const void* pool_k, const void* pool_v,
                      int32_t num_pages, const int32_t* positions, const int32_t* table,
                      void* out, void* workspace, size_t workspace_bytes, void* stream, bool launch,
-                     bool check) {
+                     bool check, bool noalloc = false) {
   if (rows < 0 || pages <= 0 || num_pages <= 0 || window < 0) return GQA_ERR_INVALID_ARG;
   if ((long long)pages * GQA_PAGE_SIZE > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
   int st = check_heads(heads, kv_heads, head_dim, dtype);
@@ -583,6 +583,15 @@ static int decode_paged_impl(int32_t rows, int32_t pages, int32_t heads, int32_t
   a.pages = pages;
   a.num_pages = num_pages;
   a.out = out;
+  if (noalloc) {
+    // The split partials go to the library's own device array.
+    if (gqa::decode_partials_bytes(a) > gqa::kDecodeScratchBytes) return GQA_ERR_WORKSPACE;
+    if (!launch) return GQA_OK;
+    float* ptr = nullptr;
+    if (gqa::decode_scratch(&ptr) != hipSuccess) return GQA_ERR_HIP;
+    a.ws = ptr;
+    return hip_status(gqa::launch_decode(a, static_cast<hipStream_t>(stream)));
+  }
   return decode_common(a, workspace_bytes, workspace, static_cast<hipStream_t>(stream), launch);
 }
 
@@ -594,6 +603,16 @@ int gqa_decode_paged(int32_t rows, int32_t pages, int32_t heads, int32_t kv_head
   return decode_paged_impl(rows, pages, heads, kv_heads, head_dim, dtype, scale, window, sinks, q,
                            pool_k, pool_v, num_pages, positions, table, out, workspace,
                            workspace_bytes, stream, !g_dry_run, g_checked != 0);
+}
+
+int gqa_decode_paged_noalloc(int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
+                             int32_t head_dim, int32_t dtype, float scale, int32_t window,
+                             const void* sinks, const void* q, const void* pool_k,
+                             const void* pool_v, int32_t num_pages, const int32_t* positions,
+                             const int32_t* table, void* out, void* stream) {
+  return decode_paged_impl(rows, pages, heads, kv_heads, head_dim, dtype, scale, window, sinks, q,
+                           pool_k, pool_v, num_pages, positions, table, out, nullptr, 0, stream,
+                           !g_dry_run, false, true);
 }
 
 

@@ -108,6 +108,13 @@ hipError_t launch_rope_write(const RopeWriteArgs& a, hipStream_t stream);
 void decode_plan(int rows, int heads, int kv_heads, int head_dim, int dtype, int paged, int cap,
                  int* split_len, int* nsplit, size_t* ws_bytes);
 hipError_t launch_decode(DecodeArgs a, hipStream_t stream);
+// The entry point that allocates nothing: its split partials live in a
+// module array of kDecodeScratchBytes per GPU; decode_scratch returns that
+// array's device address on the current device, decode_partials_bytes what
+// a launch needs of it.
+constexpr size_t kDecodeScratchBytes = 16u << 20;
+size_t decode_partials_bytes(const DecodeArgs& a);
+hipError_t decode_scratch(float** ptr);
 bool decode_mfma_supported(const DecodeArgs& a);
 int decode_mfma_split_len(int rows, int kv_heads, int cap);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);

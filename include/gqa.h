@@ -311,6 +311,28 @@ size_t gqa_decode_paged_workspace(int32_t rows, int32_t pages, int32_t heads,
                                   int32_t kv_heads, int32_t head_dim);
 
 /*
+ * gqa_decode_paged_noalloc -- gqa_decode_paged for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments (no workspace) and the
+ * same results, bit for bit, as gqa_decode_paged. The split partials live
+ * in a device array the library holds, GQA_DECODE_SCRATCH_BYTES per GPU,
+ * until the process ends; the call allocates and frees nothing. A call whose
+ * partials would exceed that array returns GQA_ERR_WORKSPACE before touching
+ * the device (bf16 with Heads / KvHeads <= 16 needs at most rows * heads *
+ * ceil(pages * 64 / 1024) * (D + 2) * 4 bytes, often none). Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialized by the caller. The array needs
+ * no clearing: a call reads only partials it wrote itself. Checked mode does
+ * not apply to this entry.
+ */
+#define GQA_DECODE_SCRATCH_BYTES (16u << 20)
+int gqa_decode_paged_noalloc(int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
+                             int32_t head_dim, int32_t dtype, float scale, int32_t window,
+                             const void* sinks, const void* q, const void* pool_k,
+                             const void* pool_v, int32_t num_pages, const int32_t* positions,
+                             const int32_t* table, void* out, void* stream);
+
+/*
  * gqa_step_packed -- `step_packed<P>` of GroupedQueryAttention (llama-
  * 3.1-8b-instruct card) and SinkAttention (gpt-oss-20b card, with the
  * window): one call over `batch` decode tokens and `p` packed prefill
