@@ -137,8 +137,12 @@ def test_prefill_llama8b_packed_full_sampled():
     out = run_prefill(*dv, pos, seg, wl.heads, wl.kv_heads, wl.head_dim)
     starts = np.concatenate([[0], np.cumsum(lengths)[:-1]])
     ends = np.cumsum(lengths) - 1
+    # Every query of each 32-token query tile that a segment boundary cuts
+    # (their key tiles mix two segments), every 16th query, the segment ends
+    # and a random sample.
+    straddle = [np.arange(32 * (b // 32), min(p, 32 * (b // 32) + 32)) for b in starts[1:] if b % 32]
     sel = np.unique(np.concatenate([starts, ends, W.sample_indices(p, 200, g2["extra"]),
-                                    [p - 1]])).astype(np.int32)
+                                    np.arange(0, p, 16), [p - 1]] + straddle)).astype(np.int32)
     ref = oracle.default().packed(*hv, pos, seg, sel=sel)
     assert_close(f64(out)[sel], ref, "bf16", f"llama8b packed prefill, {len(sel)} sampled queries")
 

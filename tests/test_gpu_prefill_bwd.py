@@ -117,6 +117,19 @@ def test_backward_llama8b_packed_sampled():
     sl = slice(a, a + 600)
     dq_r, _, _ = o.packed_backward(q[sl], k[sl], v[sl], g[sl], pos[sl], seg[sl])
     check_grad(dq[sl], dq_r, f"dq first 600 of segment {li}")
+    # The longest segment whole, for KV head 0 and the query heads that read
+    # it (heads 0 .. G - 1): every key's dk and dv and every query's dq of
+    # that group. (KV heads are independent, so the slice is exact.)
+    sl = slice(int(starts[li]), int(ends[li]))
+    gq = h // kvh
+    dq_r, dk_r, dv_r = o.packed_backward(q[sl][:, :gq], k[sl][:, :1], v[sl][:, :1], g[sl][:, :gq],
+                                         pos[sl], seg[sl])
+    print(f"[parity] backward longest segment ({int(lens[li])} tokens), KV head 0: max |err| "
+          f"dk {np.max(np.abs(dk[sl][:, :1] - dk_r)):.3e} (max |ref| {np.max(np.abs(dk_r)):.3g}), "
+          f"dv {np.max(np.abs(dv[sl][:, :1] - dv_r)):.3e} (max |ref| {np.max(np.abs(dv_r)):.3g})", flush=True)
+    check_grad(dk[sl][:, :1], dk_r, f"dk segment {li}, KV head 0")
+    check_grad(dv[sl][:, :1], dv_r, f"dv segment {li}, KV head 0")
+    check_grad(dq[sl][:, :gq], dq_r, f"dq segment {li}, heads 0..{gq - 1}")
 
 
 def test_backward_extreme_positions():
