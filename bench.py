@@ -44,7 +44,7 @@ def parse_args():
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the absolute numbers of the three other workload configurations")
     ap.add_argument("--cpu-sample-rows", type=int, default=64)
-    ap.add_argument("--cpu-sample-queries", type=int, default=16384)
+    ap.add_argument("--cpu-sample-queries", type=int, default=8192)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch's copy kernel), for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -262,6 +262,158 @@ def other_configs(gqa, W, torch, np, stream, reps):
     return out
 
 
+def oracle_other_configs(o, np, W, only=None):
+    """The oracle on the other workload configurations, timed on this host:
+    the tiny Llama example (prefill of 128 tokens, then its 16 decode steps),
+    GPT-2 f32 decode_rows (all 32 rows) and the gpt-oss layer pair (the
+    windowed layer's prefill whole, the full layer's on a sample of queries,
+    and a sample of each layer's decode steps). Inputs are seeded draws of the
+    same shapes, index layouts and positions as the GPU runs; each entry
+    gives the oracle's seconds and its rate on the algorithmic work it did."""
+    res = {}
+    if only is None or "tiny_llama" in only:
+        wl = W.TINY_LLAMA
+        H, KVH, D, S, NS, MS = wl.heads, wl.kv_heads, wl.head_dim, wl.extra["prefill"], \
+            wl.extra["decode_steps"], wl.extra["max_seq"]
+        g = W.streams(1)
+        n = S + NS
+        q = W.normal(g["q"], (n, H, D)).astype(np.float64)
+        k = W.normal(g["k"], (n, KVH, D)).astype(np.float64)
+        v = W.normal(g["v"], (n, KVH, D)).astype(np.float64)
+        pos = np.arange(n, dtype=np.int32)
+        t0 = time.perf_counter()
+        c, sn = o.rope_tables(MS, D, wl.theta, "bf16")
+        qr = o.rope(q, pos, c, sn, "bf16")
+        kr = o.rope(k, pos, c, sn, "bf16")
+        o.packed(qr[:S], kr[:S], v[:S], pos[:S], np.zeros(S, np.int32))
+        t_p = time.perf_counter() - t0
+        cache = np.full((1, KVH, MS, D), np.nan)
+        ck, cv, _ = o.write_contiguous(kr, v, pos, cache, cache.copy())
+        t0 = time.perf_counter()
+        for i in range(S, n):
+            o.decode_rows(qr[i:i + 1], ck, cv, pos[i:i + 1])
+        t_d = time.perf_counter() - t0
+        fl = 4 * D * H * S * (S + 1) // 2
+        db = sum((p_ + 1) * KVH * D * 2 * 2 for p_ in range(S, n))
+        res["tiny_llama"] = {"seconds": t_p + t_d, "prefill_seconds": t_p, "prefill_flops": fl,
+                             "prefill_gflops": fl / t_p / 1e9, "decode_seconds_16_steps": t_d,
+                             "decode_gbs": db / t_d / 1e9,
+                             "sample": "whole: tables + rope + prefill S=128, 16 decode steps"}
+    if only is None or "gpt2_decode_rows_f32" in only:
+        wl = W.GPT2_DECODE_ROWS
+        H, KVH, D, B, MS = wl.heads, wl.kv_heads, wl.head_dim, wl.extra["batch"], wl.extra["max_seq"]
+        g = W.streams(2)
+        dpos = W.uniform_positions(B, 0, MS - 1, g["extra"])
+        ck = W.normal(g["pool_k"], (B, KVH, MS, D)).astype(np.float64)
+        cv = W.normal(g["pool_v"], (B, KVH, MS, D)).astype(np.float64)
+        q = W.normal(g["q"], (B, H, D)).astype(np.float64)
+        t0 = time.perf_counter()
+        o.decode_rows(q, ck, cv, dpos)
+        t2 = time.perf_counter() - t0
+        b2 = int(np.sum(dpos.astype(np.int64) + 1)) * KVH * D * 4 * 2 + 2 * B * H * D * 4
+        res["gpt2_decode_rows_f32"] = {"seconds": t2, "algorithmic_bytes": b2, "gbs": b2 / t2 / 1e9,
+                                       "sample": "whole: all 32 rows"}
+    if only is None or "gpt_oss" in only:
+        wl = W.GPT_OSS_SINK
+        H, KVH, D, S, NS, MS = wl.heads, wl.kv_heads, wl.head_dim, wl.extra["prefill"], \
+            wl.extra["decode_steps"], wl.extra["max_seq"]
+        n = S + NS
+        g = W.streams(5)
+        q = W.normal(g["q"], (n, H, D)).astype(np.float64)
+        k = W.normal(g["k"], (n, KVH, D)).astype(np.float64)
+        v = W.normal(g["v"], (n, KVH, D)).astype(np.float64)
+        sinks = W.normal(g["sinks"], (H,)).astype(np.float64)
+        pos = np.arange(n, dtype=np.int32)
+        seg = np.zeros(S, np.int32)
+        cache = np.full((1, KVH, MS, D), np.nan)
+        ck, cv, _ = o.write_contiguous(k, v, pos, cache, cache.copy())
+        layers = {}
+        secs = 0.0
+        for win in wl.extra["windows"]:
+            sel = None if win > 0 else np.arange(0, S, 8, dtype=np.int32)
+            qs = np.arange(S) if sel is None else sel
+            t0 = time.perf_counter()
+            o.packed(q[:S], k[:S], v[:S], pos[:S], seg, window=win, sinks=sinks, sel=sel)
+            t_p = time.perf_counter() - t0
+            pairs = int(sum(min(int(i) + 1, win) if win > 0 else int(i) + 1 for i in qs))
+            steps = np.arange(S, n, 8)
+            t0 = time.perf_counter()
+            for i in steps:
+                o.decode_rows(q[i:i + 1], ck, cv, pos[i:i + 1], window=win, sinks=sinks)
+            t_d = time.perf_counter() - t0
+            kv = sum(min(int(p_) + 1, win) if win > 0 else int(p_) + 1 for p_ in steps)
+            layers[f"window{win}"] = {
+                "prefill_seconds": t_p, "prefill_gflops": 4 * D * H * pairs / t_p / 1e9,
+                "prefill_sample": "all 4096 queries" if sel is None else f"{len(sel)} of {S} queries",
+                "decode_seconds": t_d, "decode_gbs": kv * KVH * D * 2 * 2 / t_d / 1e9,
+                "decode_sample": f"{len(steps)} of {NS} steps"}
+            secs += t_p + t_d
+        res["gpt_oss"] = {"seconds": secs, "layers": layers}
+    return res
+
+
+def gpu_clocks():
+    """Current gfx (per XCD) and memory clocks in MHz from amd-smi (None if
+    amd-smi is not there)."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        if r.returncode != 0:
+            return None
+        data = json.loads(r.stdout)
+        clk = data["gpu_data"][0]["clock"] if isinstance(data, dict) else data[0]["clock"]
+
+        def mhz(entry):
+            c = entry.get("clk") if isinstance(entry, dict) else None
+            return c.get("value") if isinstance(c, dict) else None
+        return {"gfx_mhz": [mhz(v) for k, v in sorted(clk.items()) if k.startswith("gfx")],
+                "mem_mhz": [mhz(v) for k, v in sorted(clk.items()) if k.startswith("mem")],
+                "gfx_max_mhz": next((v["max_clk"]["value"] for k, v in clk.items()
+                                     if k.startswith("gfx") and isinstance(v.get("max_clk"), dict)),
+                                    None)}
+    except Exception:
+        return None
+
+
+def clocks_under_load(fn, seconds=1.5):
+    """GPU clocks sampled while fn runs back to back for about `seconds`."""
+    import threading
+    box = {}
+    t = threading.Thread(target=lambda: (time.sleep(seconds / 2), box.update(c=gpu_clocks())))
+    t.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end or t.is_alive():
+        fn()
+    t.join()
+    return box.get("c")
+
+
+def host_info(torch, clocks_before, clocks_prefill):
+    """Versions, the host CPU and the GPU clocks around the run."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    rocm = None
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    return {"cpu_count": os.cpu_count(), "cpu_model": model,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "rocm": rocm, "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+            "gpu": torch.cuda.get_device_name(0),
+            "seeds": {"decode": SEED_DECODE, "prefill": SEED_PREFILL, "chunked": SEED_CHUNKED,
+                      "qkv": SEED_QKV},
+            "gpu_clocks_idle_before": clocks_before,
+            "gpu_clocks_during_prefill": clocks_prefill}
+
+
 def copy_calibration():
     """A plain copy of known size: 1 GiB read + 1 GiB written per launch."""
     import torch
@@ -318,6 +470,7 @@ def main():
     bf16 = torch.bfloat16
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
+    clocks_before = gpu_clocks()
 
     # ---------------- decode workload (Llama-3.1-8B paged) ----------------
     wd = W.LLAMA8B_PAGED
@@ -420,6 +573,12 @@ def main():
     per_op_pct = {n: [float(np.percentile([ev[i].elapsed_time(ev[i + 1]) * 1e3 for ev in evs], p_))
                       for p_ in (10, 50, 90)] for i, n in enumerate(names)}
     step_ms = float(np.mean([ev[0].elapsed_time(ev[5]) for ev in evs]))
+
+    def prefill_only():
+        gqa.gqa_prefill_packed(P, H, KVH, D, gqa.GQA_BF16, 0.0, 0, None, pq, pk, pv, p_pos, p_seg,
+                               p_out, p_ws, pws_n)
+        torch.cuda.synchronize()
+    clocks_prefill = clocks_under_load(prefill_only)
 
     # ---------------- next row: chunked prefill over a paged prefix ----------------
     # Timed on its own after the step (it is not part of the step): 16 rows of
@@ -611,29 +770,57 @@ def main():
     if snap is not None:
         import oracle
         o = oracle.default()
-        # Decode of all sampled rows, repeated until ~4 s of CPU work.
+        threads = o.num_threads()
+        # Llama-3.1-8B paged decode: all sampled rows, repeated to ~2 s.
         reps, cpu_dec_s = 0, 0.0
-        while reps == 0 or cpu_dec_s < 4.0:
+        while reps == 0 or cpu_dec_s < 2.0:
             t = time.perf_counter()
             o.decode_paged(snap["q"], snap["pk"], snap["pv"], dpos[snap["rows"]], snap["table"])
             cpu_dec_s += time.perf_counter() - t
             reps += 1
-        s_bytes = reps * (int(np.sum(lengths[snap["rows"]])) * KVH * D * 2 * 2 +
-                          2 * len(snap["rows"]) * H * D * 2)
+        s_keys = int(np.sum(lengths[snap["rows"]]))
+        s_bytes = s_keys * KVH * D * 2 * 2 + 2 * len(snap["rows"]) * H * D * 2
+        # Llama-3.1-8B packed prefill: a sample of the queries.
         t = time.perf_counter()
         o.packed(snap["pq"], snap["pk_"], snap["pv_"], ppos, pseg, sel=snap["sel"])
         cpu_pre_s = time.perf_counter() - t
         s_pairs = int(np.sum(ppos[snap["sel"]].astype(np.int64) + 1))
         s_flops = 4 * D * H * s_pairs
-        cpu = {"value": s_bytes / cpu_dec_s / 1e9, "unit": "GB/s", "cores": o.num_threads(),
+        per_config = {
+            "llama8b_paged_decode": {
+                "seconds": cpu_dec_s / reps, "algorithmic_bytes": s_bytes,
+                "gbs": s_bytes * reps / cpu_dec_s / 1e9,
+                "sample": f"{len(snap['rows'])} of {rows} rows ({s_keys} keys), {reps} passes"},
+            "llama8b_packed_prefill": {
+                "seconds": cpu_pre_s, "algorithmic_flops": s_flops,
+                "gflops": s_flops / cpu_pre_s / 1e9,
+                "sample": f"{len(snap['sel'])} of {P} queries ({s_pairs} attended pairs per head)"},
+        }
+        per_config.update(oracle_other_configs(o, np, W))
+        # Single-threaded: the tiny Llama example, GPT-2 decode_rows and one
+        # pass of the paged decode.
+        o.set_num_threads(1)
+        single = {}
+        t = time.perf_counter()
+        o.decode_paged(snap["q"], snap["pk"], snap["pv"], dpos[snap["rows"]], snap["table"])
+        t1 = time.perf_counter() - t
+        single["llama8b_paged_decode"] = {"seconds": t1, "gbs": s_bytes / t1 / 1e9}
+        single.update(oracle_other_configs(o, np, W, only=("tiny_llama", "gpt2_decode_rows_f32")))
+        o.set_num_threads(threads)
+        total = cpu_dec_s + cpu_pre_s + sum(v.get("seconds", 0.0) for v in per_config.values()
+                                            if isinstance(v, dict) and "layers" not in v) + \
+            sum(v["seconds"] for v in single.values())
+        cpu = {"value": s_bytes * reps / cpu_dec_s / 1e9, "unit": "GB/s", "cores": threads,
                "kind": "oracle",
                "sample": (f"decode_paged on {len(snap['rows'])} of {rows} rows "
-                          f"({int(np.sum(lengths[snap['rows']]))} keys) x {reps} passes, "
+                          f"({s_keys} keys) x {reps} passes, "
                           f"{cpu_dec_s:.2f} s; "
                           f"packed prefill on {len(snap['sel'])} of {P} queries "
-                          f"({s_pairs} attended pairs/head, {cpu_pre_s:.2f} s)"),
+                          f"({s_pairs} attended pairs/head, {cpu_pre_s:.2f} s); the other "
+                          "configurations in per_config, single-threaded times in single_thread"),
                "prefill_tflops": s_flops / cpu_pre_s / 1e12,
-               "seconds": cpu_dec_s + cpu_pre_s}
+               "per_config": per_config, "single_thread": single,
+               "seconds": total}
 
     result = {
         "metric": METRIC,
@@ -668,6 +855,7 @@ def main():
         "other_configs": others,
         "wall_s_timed": wall,
         "cpu_baseline": cpu,
+        "host": host_info(torch, clocks_before, clocks_prefill),
     }
     print(json.dumps(result), flush=True)
     return 0

@@ -40,7 +40,10 @@ GQA_BF16, GQA_F32 = 0, 1
 GQA_CACHE_NONE, GQA_CACHE_CONTIGUOUS, GQA_CACHE_PAGED_TABLE, GQA_CACHE_PAGED_SLOTS = 0, 1, 2, 3
 GQA_PAGE_SIZE = 64
 
-library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
+# The in-tree build, or another build of the same sources named by
+# GQA_LIBRARY (the host-sanitizer test loads one that way).
+library_path = os.environ.get("GQA_LIBRARY") or \
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
 if not os.path.exists(library_path):
     raise ImportError(
         f"{library_path} is missing: build the HIP library first "

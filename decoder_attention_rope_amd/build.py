@@ -36,9 +36,18 @@ SOURCE_FLAGS = {
 }
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON_FLAGS + SOURCE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+# Host-code sanitizers (AddressSanitizer + UndefinedBehaviorSanitizer) for the
+# host-sanitizer test build; device code is built as usual. Each flag sits
+# behind -Xarch_host, so it reaches the host compilation only.
+HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-Xarch_host", "-fno-sanitize-recover=all",
+                       "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src, verbose, build_dir=None, extra=()):
+    obj = os.path.join(build_dir or BUILD_DIR, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + COMMON_FLAGS + SOURCE_FLAGS.get(src, []) + list(extra) + \
+        ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,19 +61,26 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False, jobs=None):
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose=False, jobs=None, out=None, host_sanitize=False):
+    """Build the library to `out` (default: the in-tree libgqa.so). With
+    host_sanitize the host code is instrumented (objects in their own
+    directory next to `out`; the process that loads it preloads clang's
+    AddressSanitizer runtime)."""
+    lib = out or LIB
+    build_dir = BUILD_DIR if out is None else os.path.join(os.path.dirname(out), "_build_san")
+    os.makedirs(build_dir, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     jobs = jobs or min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
+    extra = HOST_SANITIZE_FLAGS if host_sanitize else []
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -33,8 +33,9 @@ def _dt(x):
 
 
 def load(path=None):
-    """Load (building if needed) the oracle library at `path`."""
-    path = path or _build.DEFAULT_LIB
+    """Load (building if needed) the oracle library at `path` (default: the
+    in-tree build, or ORACLE_LIBRARY from the environment)."""
+    path = path or os.environ.get("ORACLE_LIBRARY") or _build.DEFAULT_LIB
     if path in _LIBS:
         return _LIBS[path]
     if not os.path.exists(path):
@@ -69,6 +70,8 @@ def load(path=None):
     lib.orc_packed_backward.argtypes = [c_int, c_int, c_int, c_int, _D, _D, _D, _D, _I, _I, c_dbl,
                                         c_int, _D, _D, _D]
     lib.orc_num_threads.restype = c_int
+    lib.orc_set_num_threads.restype = None
+    lib.orc_set_num_threads.argtypes = [c_int]
     lib.orc_mutation.restype = c_int
     _LIBS[path] = lib
     return lib
@@ -113,6 +116,10 @@ class Oracle:
 
     def num_threads(self):
         return self.lib.orc_num_threads()
+
+    def set_num_threads(self, n):
+        """Threads of the following calls (timing only; results do not depend on it)."""
+        self.lib.orc_set_num_threads(int(n))
 
     def mutation(self):
         return self.lib.orc_mutation()

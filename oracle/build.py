@@ -14,10 +14,19 @@ SRC = os.path.join(HERE, "gqa_oracle.c")
 DEFAULT_LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(out=DEFAULT_LIB, mutation=0, verbose=False):
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the oracle (host
+# code only; the caller preloads gcc's libasan and libubsan).
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def build(out=DEFAULT_LIB, mutation=0, verbose=False, sanitize=None):
+    if sanitize is None:
+        sanitize = os.environ.get("ORACLE_SANITIZE", "") not in ("", "0")
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
            "-shared", "-fPIC", "-std=c11", "-Wall", "-Wno-unused-function",
-           "-DORC_MUTATE=%d" % int(mutation), SRC, "-o", out + ".tmp", "-lm"]
+           "-DORC_MUTATE=%d" % int(mutation)] + (SANITIZE_FLAGS if sanitize else []) + \
+          [SRC, "-o", out + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -733,4 +733,14 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Threads for the calls that follow (timing only; results do not depend on
+ * it: every parallel loop writes disjoint outputs). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int orc_mutation(void) { return ORC_MUTATE; }

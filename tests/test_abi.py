@@ -46,7 +46,7 @@ def test_exports_every_declared_symbol(g):
     names = declared_functions()
     assert {"gqa_rope_write_kv", "gqa_prefill_packed", "gqa_decode_paged",
             "gqa_decode_rows"} <= set(names)
-    cdll = ctypes.CDLL(LIB)
+    cdll = ctypes.CDLL(g.library_path)
     missing = [n for n in names if not hasattr(cdll, n)]
     assert not missing, f"declared but not exported: {missing}"
     assert g.gqa_abi_version() == 1
