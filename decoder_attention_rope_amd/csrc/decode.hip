@@ -13,12 +13,30 @@
 // denominator. Splitting by ranges reaches exactly the softmax over the union
 // (up to rounding order).
 //
-// This generic kernel runs on the vector ALUs: a token's row of D elements is
-// spread over D*sizeof(T)/16 lanes that each load one 16-byte chunk (so a
-// wavefront reads whole rows, coalesced), dot products are finished with
-// butterfly shuffles, and the split's scores live in LDS between the QK and
-// PV phases (one exp per score). It serves f32, contiguous caches and every
-// head-group size.
+// This generic kernel runs on the vector ALUs and serves f32, and bf16 with
+// more query heads per KV head than the matrix-core kernel takes. It makes
+// one pass over the keys with an online softmax in registers:
+// * A workgroup of NW wavefronts owns one (row, KV head, head chunk, split of
+//   keys); its wavefronts take chunks of CK keys round-robin. A key row of D
+//   elements is spread over LPT = D * sizeof(T) / 16 lanes that each load one
+//   16-byte chunk, so every load instruction of a wavefront reads 64 / LPT
+//   whole, consecutive rows (1 KB).
+// * A chunk's K and V loads (UNR per lane each, nontemporal) are all issued
+//   before any is used, unconditionally: addresses are clamped into the
+//   split's key range and keys outside it are masked afterwards.
+// * Dot products are finished with DPP butterflies inside each 16-lane row,
+//   so all LPT lanes of a key hold the same score bit for bit; each lane then
+//   keeps the running max, sum and weighted V of its key slot for its EPL
+//   dimensions. Slots and wavefronts are combined once, at the end.
+// * With a single split per (row, head chunk) the workgroup also normalizes,
+//   adds the sink and writes the output; otherwise it writes a partial for
+//   the merge kernel below.
+// * Rows are split only when there are too few (row, head chunk) units to
+//   fill the chip. With enough units and at most 64 rows, every unit is one
+//   workgroup of up to 16 wavefronts and the workgroups map to rows in order
+//   of decreasing key count (ranked on the device from the positions):
+//   workgroups start in blockIdx order, so the longest rows start first and
+//   the short ones fill the gaps, with no merge pass.
 #include <mutex>
 
 #include "common.h"
@@ -28,50 +46,100 @@ namespace gqa {
 
 namespace {
 constexpr int kSplitLen = 256;
-constexpr int kBlock = 256;
 constexpr float kNegInf = -__builtin_huge_valf();
 }  // namespace
 
-template <typename T, int D, bool PAGED>
-__device__ __forceinline__ const T* row_ptr(const DecodeArgs& a, const void* base, int r, int kh,
-                                            int t) {
-  if (PAGED) {
-    const int page = a.table[(long long)r * a.pages + t / kPageSize];
-    if (page < 0 || page >= a.num_pages) return nullptr;
-    return static_cast<const T*>(base) +
-           (((long long)page * a.kv_heads + kh) * kPageSize + t % kPageSize) * D;
-  }
-  return static_cast<const T*>(base) + (((long long)r * a.kv_heads + kh) * a.cap + t) * D;
+// Sum over the LPT lanes of each key slot (LPT = 8, 16 or 32), left in every
+// one of them. Inside a 16-lane row the butterfly runs on DPP (quad swaps,
+// then the half-row and row mirrors); the step across rows is a shuffle.
+// Every lane adds the same two values in either order, so all lanes of a
+// slot end with identical bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_get(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+template <int LPT>
+__device__ __forceinline__ float slot_sum(float v) {
+  v += dpp_get<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_get<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_get<0x141>(v);  // row_half_mirror
+  if (LPT >= 16) v += dpp_get<0x140>(v);  // row_mirror
+  if (LPT >= 32) v += __shfl_xor(v, 16, 64);
+  return v;
 }
 
-template <typename T, int D, int GC, bool PAGED>
-__global__ __launch_bounds__(kBlock) void decode_split_kernel(DecodeArgs a) {
-  constexpr int EPL = Elem<T>::kPer16B;  // elements per lane per token
-  constexpr int LPT = D / EPL;           // lanes per token
-  constexpr int TPP = kBlock / LPT;      // tokens per pass of the block
-  __shared__ float sc[GC][kSplitLen];
-  __shared__ float red[4][GC][D];
-  __shared__ float stat[GC][2];
+#ifndef GQA_DECODE_VEC_TARGET_WGS
+#define GQA_DECODE_VEC_TARGET_WGS 1024
+#endif
+#ifndef GQA_DECODE_VEC_LOADS
+#define GQA_DECODE_VEC_LOADS 8
+#endif
+#ifndef GQA_DECODE_VEC_SORT_UNITS
+#define GQA_DECODE_VEC_SORT_UNITS 256
+#endif
+constexpr int kVecLoads = GQA_DECODE_VEC_LOADS;  // K (and V) loads per lane per chunk, at most
+constexpr int kVecWaves = 8;         // wavefronts per workgroup with split rows
+constexpr int kVecWavesSorted = 16;  // ... with one workgroup per row and head chunk
+constexpr int kSortMaxRows = 64;     // rows one wavefront can rank
+
+// Row of rank k when rows (at most 64) are ordered by the number of keys they
+// attend, longest first (ties by row index). Every wavefront of the caller
+// computes it on its own: lane l holds row l's key count and counts the rows
+// ahead of it.
+__device__ __forceinline__ int row_of_rank(const DecodeArgs& a, int k) {
+  const int lane = threadIdx.x & 63;
+  int n = -1;  // lanes past the last row never match
+  if (lane < a.rows) {
+    int lo, hi;
+    decode_key_range(a.positions[lane], a.cap, a.window, lo, hi);
+    n = hi >= lo ? hi - lo + 1 : 0;
+  }
+  int rank = 0;
+  for (int j = 0; j < a.rows; ++j) {
+    const int nj = __builtin_amdgcn_readlane(n, j);
+    rank += (nj > n) | ((nj == n) & (j < lane));
+  }
+  const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < a.rows && rank == k);
+  return (int)__builtin_ctzll(hit);
+}
+
+template <typename T, int D, int GC, bool PAGED, int NW, bool SORTED>
+__global__ __launch_bounds__(64 * NW) void decode_vec_kernel(DecodeArgs a) {
+  constexpr int EPL = Elem<T>::kPer16B;       // elements per lane per key row
+  constexpr int LPT = D / EPL;                // lanes per key row
+  constexpr int TPW = 64 / LPT;               // key rows per load instruction
+  constexpr int UNR = TPW * kVecLoads <= kPageSize ? kVecLoads : kPageSize / TPW;
+  constexpr int CK = TPW * UNR;               // keys per chunk (inside one page)
+  constexpr int RS = D + 2;
+  __shared__ float red[NW][GC][RS];
 
   const int split = blockIdx.x;
-  const int r = blockIdx.z;
+  // Sorted dispatch (one split): workgroups are launched in blockIdx order,
+  // so the longest rows start first and shorter ones fill in behind them.
+  const int r = SORTED ? __builtin_amdgcn_readfirstlane(row_of_rank(a, blockIdx.z)) : blockIdx.z;
   const int G = a.heads / a.kv_heads;
   const int nchunks = G / GC;
   const int kh = blockIdx.y / nchunks;
   const int h0 = kh * G + (blockIdx.y % nchunks) * GC;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sub = lane % LPT;  // 16-byte column of the key row
+  const int tk = lane / LPT;   // key slot within a load instruction
 
   int lo, hi;
   decode_key_range(a.positions[r], a.cap, a.window, lo, hi);
   const int t0 = max(lo, split * a.split_len);
   const int t1 = min(hi + 1, (split + 1) * a.split_len);
-  if (t0 >= t1) return;  // the merge never reads a split outside [lo, hi]
-  const int n = t1 - t0;
-
-  const int sub = tid % LPT;
-  const int tk = tid / LPT;
+  if (t0 >= t1) {
+    // No keys in this split. The merge never reads a split outside [lo, hi];
+    // with a single split this workgroup owns the output, which is 0.
+    if (a.nsplit == 1) {
+      T* out = static_cast<T*>(a.out) + ((long long)r * a.heads + h0) * D;
+      for (int x = tid; x < GC * D; x += 64 * NW) Elem<T>::store1(out + x, 0.f);
+    }
+    return;
+  }
 
   float qr[GC][EPL];
 #pragma unroll
@@ -79,200 +147,245 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(DecodeArgs a) {
     const T* qp = static_cast<const T*>(a.q) + ((long long)r * a.heads + h0 + h) * D + sub * EPL;
     Elem<T>::to_f32(load16(qp), qr[h]);
   }
-
-  // Phase 1: scaled scores (log2 domain) of every key of the split. The
-  // loads of UNR passes are issued before any of them is used, so that many
-  // memory round trips overlap.
-  constexpr int UNR = 8;
-  for (int base = 0; base < n; base += TPP * UNR) {
-    u32x4 raw[UNR];
-    bool valid[UNR];
+  float m_run[GC], l_run[GC], acc[GC][EPL];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int i = base + u * TPP + tk;
-      const T* kp = i < n ? row_ptr<T, D, PAGED>(a, a.k, r, kh, t0 + i) : nullptr;
-      valid[u] = kp != nullptr;
-      raw[u] = valid[u] ? load16(kp + sub * EPL) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int i = base + u * TPP + tk;
-      float dot[GC];
-#pragma unroll
-      for (int h = 0; h < GC; ++h) dot[h] = 0.f;
-      if (valid[u]) {
-        float x[EPL];
-        Elem<T>::to_f32(raw[u], x);
-#pragma unroll
-        for (int h = 0; h < GC; ++h)
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) dot[h] += qr[h][e] * x[e];
-      }
-#pragma unroll
-      for (int off = LPT / 2; off >= 1; off >>= 1)
-#pragma unroll
-        for (int h = 0; h < GC; ++h) dot[h] += __shfl_xor(dot[h], off, 64);
-      if (sub == 0 && i < n) {
-#pragma unroll
-        for (int h = 0; h < GC; ++h) sc[h][i] = valid[u] ? dot[h] * a.scale_log2 : kNegInf;
-      }
-    }
-  }
-  __syncthreads();
-
-  // Phase 2: per-head max, exponentials and their sum.
-  for (int h = wave; h < GC; h += 4) {
-    float m = kNegInf;
-    for (int i = lane; i < n; i += 64) m = fmaxf(m, sc[h][i]);
-    m = wave_max(m);
-    float l = 0.f;
-    for (int i = lane; i < n; i += 64) {
-      const float p = (m == kNegInf) ? 0.f : exp2f(sc[h][i] - m);
-      sc[h][i] = p;
-      l += p;
-    }
-    l = wave_sum(l);
-    if (lane == 0) {
-      stat[h][0] = m;
-      stat[h][1] = l;
-    }
-  }
-  __syncthreads();
-
-  // Phase 3: probability-weighted values.
-  float acc[GC][EPL];
-#pragma unroll
-  for (int h = 0; h < GC; ++h)
+  for (int h = 0; h < GC; ++h) {
+    m_run[h] = kNegInf;
+    l_run[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  for (int base = 0; base < n; base += TPP * UNR) {
-    u32x4 raw[UNR];
-    bool valid[UNR];
+  }
+
+  const T* kbase = static_cast<const T*>(a.k);
+  const T* vbase = static_cast<const T*>(a.v);
+  const int c_begin = t0 / CK;
+  const int c_end = (t1 + CK - 1) / CK;
+  for (int c = c_begin + wave; c < c_end; c += NW) {
+    const int tb = c * CK;
+    long long row0;  // element offset of key tb
+    if (PAGED) {
+      const int page = a.table[(long long)r * a.pages + tb / kPageSize];
+      if (page < 0 || page >= a.num_pages) continue;  // no keys from this page
+      row0 = (((long long)page * a.kv_heads + kh) * kPageSize + tb % kPageSize) * D;
+    } else {
+      row0 = (((long long)r * a.kv_heads + kh) * a.cap + tb) * D;
+    }
+    // Key u * TPW + tk of the chunk; keys outside [t0, t1) read a clamped
+    // in-range row and are masked below.
+    u32x4 kx[UNR], vx[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int i = base + u * TPP + tk;
-      // Keys of invalid pages were never scored.
-      const T* vp = i < n ? row_ptr<T, D, PAGED>(a, a.v, r, kh, t0 + i) : nullptr;
-      valid[u] = vp != nullptr;
-      raw[u] = valid[u] ? load16(vp + sub * EPL) : u32x4{0, 0, 0, 0};
+      const int t = min(max(tb + u * TPW + tk, t0), t1 - 1);
+      kx[u] = load16_stream(kbase + row0 + (long long)(t - tb) * D + sub * EPL);
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      if (valid[u]) {
-        const int i = base + u * TPP + tk;
+      const int t = min(max(tb + u * TPW + tk, t0), t1 - 1);
+      vx[u] = load16_stream(vbase + row0 + (long long)(t - tb) * D + sub * EPL);
+    }
+    // Keep all 2 * UNR loads in flight together: without this fence the
+    // scheduler sinks each load to just before its first use, which leaves
+    // only a few in flight per wavefront.
+    __builtin_amdgcn_sched_barrier(0);
+    const bool full = tb >= t0 && tb + CK <= t1;
+#pragma unroll
+    for (int h = 0; h < GC; ++h) {
+      float s[UNR];
+      float cmax = kNegInf;
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
         float x[EPL];
-        Elem<T>::to_f32(raw[u], x);
+        Elem<T>::to_f32(kx[u], x);
+        float d = 0.f;
 #pragma unroll
-        for (int h = 0; h < GC; ++h) {
-          const float p = sc[h][i];
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] += p * x[e];
+        for (int e = 0; e < EPL; ++e) d = __builtin_fmaf(qr[h][e], x[e], d);
+        d = slot_sum<LPT>(d) * a.scale_log2;
+        if (!full) {
+          const int t = tb + u * TPW + tk;
+          d = ((t >= t0) & (t < t1)) ? d : kNegInf;
         }
+        s[u] = d;
+        cmax = fmaxf(cmax, d);
+      }
+      const float m_new = fmaxf(m_run[h], cmax);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[h] - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const float p = fast_exp2(s[u] - m_use);
+        psum += p;
+        float x[EPL];
+        Elem<T>::to_f32(vx[u], x);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = __builtin_fmaf(p, x[e], acc[h][e]);
+      }
+      l_run[h] = l_run[h] * alpha + psum;
+      m_run[h] = m_new;
+    }
+  }
+
+  // Combine the TPW key slots of the wavefront (lanes sub + LPT * tk).
+#pragma unroll
+  for (int h = 0; h < GC; ++h) {
+    float M = m_run[h];
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float f = (m_run[h] == kNegInf) ? 0.f : fast_exp2(m_run[h] - M);
+    float l = l_run[h] * f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] *= f;
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+      l += __shfl_xor(l, off, 64);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
+    }
+    if (tk == 0) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red[wave][h][2 + sub * EPL + e] = acc[h][e];
+      if (sub == 0) {
+        red[wave][h][0] = M;
+        red[wave][h][1] = l;
       }
     }
   }
-#pragma unroll
-  for (int off = LPT; off < 64; off <<= 1)
-#pragma unroll
-    for (int h = 0; h < GC; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
-  if (lane < LPT) {
-#pragma unroll
-    for (int h = 0; h < GC; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) red[wave][h][sub * EPL + e] = acc[h][e];
-  }
   __syncthreads();
 
-  for (int x = tid; x < GC * D; x += kBlock) {
+  // Combine the wavefronts: one thread per (head, dimension).
+  for (int x = tid; x < GC * D; x += 64 * NW) {
     const int h = x / D;
     const int d = x % D;
-    float* part = a.ws + (((long long)r * a.heads + h0 + h) * a.nsplit + split) * (D + 2);
-    part[2 + d] = red[0][h][d] + red[1][h][d] + red[2][h][d] + red[3][h][d];
-    if (d == 0) {
-      part[0] = stat[h][0];
-      part[1] = stat[h][1];
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, red[w][h][0]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = red[w][h][0];
+      const float sc = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+      num += sc * red[w][h][2 + d];
+      den += sc * red[w][h][1];
+    }
+    if (a.nsplit == 1) {
+      // The only split: normalize here; the sink joins the denominator.
+      if (a.sinks != nullptr) {
+        const float s2 = Elem<T>::load1(static_cast<const T*>(a.sinks) + h0 + h) * kLog2e;
+        const float Ms = fmaxf(M, s2);
+        const float f = (M == kNegInf) ? 0.f : fast_exp2(M - Ms);
+        num *= f;
+        den = den * f + fast_exp2(s2 - Ms);
+      }
+      Elem<T>::store1(static_cast<T*>(a.out) + ((long long)r * a.heads + h0 + h) * D + d,
+                      den > 0.f ? num / den : 0.f);
+    } else {
+      float* part = a.ws + (((long long)r * a.heads + h0 + h) * a.nsplit + split) * RS;
+      part[2 + d] = num;
+      if (d == 0) {
+        part[0] = M;
+        part[1] = den;
+      }
     }
   }
 }
 
-// Combine the split partials of one (row, KV head): the G query heads' split
-// weights exp2(m_s - M) go to LDS, then every (head, dimension) output is one
-// coalesced pass over the splits. The sink logit joins the denominator here.
-constexpr int kMergeMaxW = 4096;
+// Combine the split partials of one (row, query head) in one wavefront: lane
+// l owns dimensions l (and l + 64 for D = 128). Splits are visited in groups
+// of kMergeGroup whose partials are all loaded at once -- before the row's
+// key range is known, so those loads do not wait for the position -- and
+// splits outside the range (never written by this call) are then dropped by
+// selection. Each group is folded into a running (max, denominator,
+// numerator) with rescaling. The sink logit starts the running state: max =
+// sink, denominator 2^0 = 1.
+constexpr int kMergeGroup = 8;
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  __shared__ float w[kMergeMaxW];
-  __shared__ float inv_l[64];
-  const int kh = blockIdx.x;
-  const int r = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int G = a.heads / a.kv_heads;
-  const int h0 = kh * G;
+  constexpr int DPL = D / 64;  // dimensions per lane
+  constexpr int NG = kMergeGroup;
+  const int lane = threadIdx.x & 63;
+  const int rh = blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, query head)
+  if (rh >= a.rows * a.heads) return;
+  const int r = rh / a.heads;
+  const int h = rh % a.heads;
+  const float* part = a.ws + (long long)rh * a.nsplit * (D + 2);
+  float ms[NG], ls[NG], xs[NG][DPL];
+  auto load_group = [&](int s0) {
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const float* p = part + (long long)min(s0 + i, a.nsplit - 1) * (D + 2);
+      ms[i] = p[0];
+      ls[i] = p[1];
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) xs[i][j] = p[2 + lane + 64 * j];
+    }
+  };
+  // The first group, the position and the sink are all in flight together.
+  load_group(0);
+  const int pos = a.positions[r];
+  const float sink = a.sinks != nullptr ? Elem<T>::load1(static_cast<const T*>(a.sinks) + h) : 0.f;
+  __builtin_amdgcn_sched_barrier(0);
   int lo, hi;
-  decode_key_range(a.positions[r], a.cap, a.window, lo, hi);
-  int s_first = 0, ns = 0;
-  if (hi >= lo) {
-    s_first = lo / a.split_len;
-    ns = hi / a.split_len - s_first + 1;
+  decode_key_range(pos, a.cap, a.window, lo, hi);
+  // Splits [s_lo, s_hi] hold the row's keys (none when hi < lo).
+  const int s_lo = hi >= lo ? lo / a.split_len : 1;
+  const int s_hi = hi >= lo ? hi / a.split_len : 0;
+  float M = kNegInf, den = 0.f, num[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) num[j] = 0.f;
+  if (a.sinks != nullptr) {
+    M = sink * kLog2e;
+    den = 1.f;
   }
-  const bool has_sink = a.sinks != nullptr;
-  auto part = [&](int h, int s) {
-    return a.ws + (((long long)r * a.heads + h0 + h) * a.nsplit + s_first + s) * (D + 2);
-  };
-  auto sink2 = [&](int h) {
-    return has_sink ? Elem<T>::load1(static_cast<const T*>(a.sinks) + h0 + h) * kLog2e : kNegInf;
-  };
-  T* out = static_cast<T*>(a.out) + ((long long)r * a.heads + h0) * D;
-  if (G * ns > kMergeMaxW || G > 64) {
-    // Serial fallback for very long caches: one thread per output.
-    for (int x = tid; x < G * D; x += blockDim.x) {
-      const int h = x / D, d = x % D;
-      float M = sink2(h);
-      for (int s = 0; s < ns; ++s) M = fmaxf(M, part(h, s)[0]);
-      float num = 0.f, den = (has_sink && M != kNegInf) ? fast_exp2(sink2(h) - M) : 0.f;
-      for (int s = 0; s < ns; ++s) {
-        const float ms = part(h, s)[0];
-        if (ms == kNegInf) continue;
-        const float ws = fast_exp2(ms - M);
-        num += ws * part(h, s)[2 + d];
-        den += ws * part(h, s)[1];
+  for (int s0 = 0;;) {
+    bool ok[NG];
+    float gmax = M;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      ok[i] = s0 + i >= s_lo && s0 + i <= s_hi && ms[i] != kNegInf;
+      gmax = ok[i] ? fmaxf(gmax, ms[i]) : gmax;
+    }
+    if (gmax != kNegInf) {
+      const float f = (M == kNegInf) ? 0.f : fast_exp2(M - gmax);
+      den *= f;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) num[j] *= f;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const float w = fast_exp2(ms[i] - gmax);
+        den = ok[i] ? __builtin_fmaf(w, ls[i], den) : den;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) num[j] = ok[i] ? __builtin_fmaf(w, xs[i][j], num[j]) : num[j];
       }
-      Elem<T>::store1(out + (long long)h * D + d, den > 0.f ? num / den : 0.f);
+      M = gmax;
     }
-    return;
+    s0 += NG;
+    if (s0 >= a.nsplit) break;
+    load_group(s0);
   }
-  for (int x = tid; x < G * ns; x += blockDim.x) w[x] = part(x / ns, x % ns)[0];
-  __syncthreads();
-  if (tid < G) {
-    float M = sink2(tid);
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, w[tid * ns + s]);
-    float L = (has_sink && M != kNegInf) ? fast_exp2(sink2(tid) - M) : 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = w[tid * ns + s];
-      const float ws = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
-      w[tid * ns + s] = ws;
-      L += ws * part(tid, s)[1];
-    }
-    inv_l[tid] = L > 0.f ? 1.f / L : 0.f;
-  }
-  __syncthreads();
-  for (int x = tid; x < G * D; x += blockDim.x) {
-    const int h = x / D, d = x % D;
-    float acc = 0.f;
-    const float* ws = w + h * ns;
-    for (int s = 0; s < ns; ++s) {
-      const float wt = ws[s];
-      if (wt != 0.f) acc += wt * part(h, s)[2 + d];
-    }
-    Elem<T>::store1(out + (long long)h * D + d, acc * inv_l[h]);
-  }
+  T* out = static_cast<T*>(a.out) + (long long)rh * D;
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) Elem<T>::store1(out + lane + 64 * j, den > 0.f ? num[j] / den : 0.f);
 }
 
-// Vector-ALU split plan; its 256-key splits are the shortest of both paths,
-// so its workspace bound covers the matrix-core path too.
+static hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
+  const int waves = a.rows * a.heads;
+  dim3 grid((waves + 3) / 4);
+  if (a.dtype == kDtypeBf16) {
+    if (a.head_dim == 64) decode_merge_kernel<uint16_t, 64><<<grid, 256, 0, stream>>>(a);
+    else decode_merge_kernel<uint16_t, 128><<<grid, 256, 0, stream>>>(a);
+  } else {
+    if (a.head_dim == 64) decode_merge_kernel<float, 64><<<grid, 256, 0, stream>>>(a);
+    else decode_merge_kernel<float, 128><<<grid, 256, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+// Workspace bound of both decode paths: neither splits a row into pieces
+// shorter than kSplitLen keys, so at most ceil(cap / kSplitLen) partials of
+// D + 2 floats per (row, query head) are ever written.
 void decode_plan(int rows, int heads, int kv_heads, int head_dim, int dtype, int paged, int cap,
                  int* split_len, int* nsplit, size_t* ws_bytes) {
   (void)kv_heads;
@@ -285,22 +398,64 @@ void decode_plan(int rows, int heads, int kv_heads, int head_dim, int dtype, int
   if (ws_bytes) *ws_bytes = (size_t)rows * heads * ns * (head_dim + 2) * sizeof(float);
 }
 
-template <typename T, int D, bool PAGED>
-static hipError_t launch_split_t(const DecodeArgs& a, int gc, hipStream_t stream) {
+// Query heads per workgroup of the vector kernel: as many as divide G, up to
+// 8 for f32 and 4 for bf16 (whose K and V rows take twice the registers per
+// 16-byte load once widened).
+static int decode_vec_heads(const DecodeArgs& a) {
+  const int G = a.heads / a.kv_heads;
+  const int most = a.dtype == kDtypeBf16 ? 4 : 8;
+  int gc = 1;
+  while (gc * 2 <= most && G % (gc * 2) == 0) gc *= 2;
+  return gc;
+}
+
+// Split length of the vector kernel: the whole cache (sorted dispatch) when
+// at most 64 rows give at least GQA_DECODE_VEC_SORT_UNITS (row, head chunk)
+// units; otherwise the longest length (a multiple of the page size) that
+// still gives about GQA_DECODE_VEC_TARGET_WGS workgroups, never under
+// kSplitLen keys.
+static int decode_vec_split_len(const DecodeArgs& a) {
+  const long long units = (long long)a.rows * a.heads / decode_vec_heads(a);
+  if (a.rows <= kSortMaxRows && units >= GQA_DECODE_VEC_SORT_UNITS)
+    return (a.cap + kPageSize - 1) / kPageSize * kPageSize;  // one split, sorted dispatch
+  long long nsplit = (GQA_DECODE_VEC_TARGET_WGS + units - 1) / units;
+  const long long max_split = (a.cap + kSplitLen - 1) / kSplitLen;
+  if (nsplit > max_split) nsplit = max_split;
+  if (nsplit < 1) nsplit = 1;
+  long long len = (a.cap + nsplit - 1) / nsplit;
+  len = (len + kPageSize - 1) / kPageSize * kPageSize;
+  return (int)(len > 0 ? len : kPageSize);
+}
+
+// Wavefronts per workgroup: 8 with split rows; with sorted dispatch 16 where
+// the head chunk's state fits 128 registers (f32 up to 2 heads, bf16 1).
+template <typename T, int GC, bool SORTED>
+constexpr int vec_waves() {
+  return SORTED && GC * Elem<T>::kPer16B <= 8 ? kVecWavesSorted : kVecWaves;
+}
+
+template <typename T, int D, int GC, bool PAGED, bool SORTED>
+static void launch_vec_gc(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
+  constexpr int NW = vec_waves<T, GC, SORTED>();
+  decode_vec_kernel<T, D, GC, PAGED, NW, SORTED><<<grid, dim3(64 * NW), 0, stream>>>(a);
+}
+
+template <typename T, int D, bool PAGED, bool SORTED>
+static hipError_t launch_vec_t(const DecodeArgs& a, int gc, hipStream_t stream) {
   const int G = a.heads / a.kv_heads;
   dim3 grid(a.nsplit, a.kv_heads * (G / gc), a.rows);
   switch (gc) {
     case 8:
-      decode_split_kernel<T, D, 8, PAGED><<<grid, kBlock, 0, stream>>>(a);
+      if constexpr (sizeof(T) == 4) launch_vec_gc<T, D, 8, PAGED, SORTED>(a, grid, stream);
       break;
     case 4:
-      decode_split_kernel<T, D, 4, PAGED><<<grid, kBlock, 0, stream>>>(a);
+      launch_vec_gc<T, D, 4, PAGED, SORTED>(a, grid, stream);
       break;
     case 2:
-      decode_split_kernel<T, D, 2, PAGED><<<grid, kBlock, 0, stream>>>(a);
+      launch_vec_gc<T, D, 2, PAGED, SORTED>(a, grid, stream);
       break;
     default:
-      decode_split_kernel<T, D, 1, PAGED><<<grid, kBlock, 0, stream>>>(a);
+      launch_vec_gc<T, D, 1, PAGED, SORTED>(a, grid, stream);
       break;
   }
   return hipGetLastError();
@@ -308,28 +463,25 @@ static hipError_t launch_split_t(const DecodeArgs& a, int gc, hipStream_t stream
 
 template <typename T, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  const int G = a.heads / a.kv_heads;
-  const int gc = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  hipError_t e = a.paged ? launch_split_t<T, D, true>(a, gc, stream)
-                         : launch_split_t<T, D, false>(a, gc, stream);
-  if (e != hipSuccess) return e;
-  decode_merge_kernel<T, D><<<dim3(a.kv_heads, a.rows), 256, 0, stream>>>(a);
-  return hipGetLastError();
+  const int gc = decode_vec_heads(a);
+  hipError_t e;
+  if (a.nsplit == 1 && a.rows <= kSortMaxRows)
+    e = a.paged ? launch_vec_t<T, D, true, true>(a, gc, stream)
+                : launch_vec_t<T, D, false, true>(a, gc, stream);
+  else
+    e = a.paged ? launch_vec_t<T, D, true, false>(a, gc, stream)
+                : launch_vec_t<T, D, false, false>(a, gc, stream);
+  if (e != hipSuccess || a.nsplit == 1) return e;  // one split: the output is written
+  return launch_merge(a, stream);
 }
 
-// Bytes of split partials the launch below will write for `a` (0 when the
-// matrix-core path covers each row with one split and writes the output
-// itself).
+// Bytes of split partials the launch below will write for `a` (0 when each
+// row is covered by one split and the kernel writes the output itself).
 size_t decode_partials_bytes(const DecodeArgs& a) {
-  int nsplit;
-  if (decode_mfma_supported(a)) {
-    const int sl = decode_mfma_split_len(a.rows, a.kv_heads, a.cap);
-    nsplit = (a.cap + sl - 1) / sl;
-    if (nsplit == 1) return 0;
-  } else {
-    decode_plan(a.rows, a.heads, a.kv_heads, a.head_dim, a.dtype, a.paged, a.cap, nullptr, &nsplit,
-                nullptr);
-  }
+  const int sl = decode_mfma_supported(a) ? decode_mfma_split_len(a.rows, a.kv_heads, a.cap)
+                                          : decode_vec_split_len(a);
+  const int nsplit = (a.cap + sl - 1) / sl;
+  if (nsplit == 1) return 0;
   return (size_t)a.rows * a.heads * nsplit * (a.head_dim + 2) * sizeof(float);
 }
 
@@ -368,14 +520,10 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
     hipError_t e = launch_decode_mfma(a, stream);
     if (e != hipSuccess) return e;
     if (a.nsplit == 1) return hipSuccess;  // the split kernel wrote the output
-    if (a.head_dim == 64)
-      decode_merge_kernel<uint16_t, 64><<<dim3(a.kv_heads, a.rows), 256, 0, stream>>>(a);
-    else
-      decode_merge_kernel<uint16_t, 128><<<dim3(a.kv_heads, a.rows), 256, 0, stream>>>(a);
-    return hipGetLastError();
+    return launch_merge(a, stream);
   }
-  decode_plan(a.rows, a.heads, a.kv_heads, a.head_dim, a.dtype, a.paged, a.cap, &a.split_len,
-              &a.nsplit, nullptr);
+  a.split_len = decode_vec_split_len(a);
+  a.nsplit = (a.cap + a.split_len - 1) / a.split_len;
   if (a.dtype == kDtypeBf16) {
     return a.head_dim == 64 ? launch_decode_t<uint16_t, 64>(a, stream)
                             : launch_decode_t<uint16_t, 128>(a, stream);

@@ -318,8 +318,11 @@ size_t gqa_decode_paged_workspace(int32_t rows, int32_t pages, int32_t heads,
  * in a device array the library holds, GQA_DECODE_SCRATCH_BYTES per GPU,
  * until the process ends; the call allocates and frees nothing. A call whose
  * partials would exceed that array returns GQA_ERR_WORKSPACE before touching
- * the device (bf16 with Heads / KvHeads <= 16 needs at most rows * heads *
- * ceil(pages * 64 / 1024) * (D + 2) * 4 bytes, often none). Every call on a
+ * the device. The split rules keep every call far below it: a row is split
+ * only while the grid has fewer than 512 workgroups (bf16 on matrix cores) or
+ * 1024 (the vector-ALU kernel), so at most 16384 (query head, split) partials
+ * of D + 2 floats (8.5 MB) are written, and none when each row takes one
+ * split. Every call on a
  * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
  * other threads) race and must be serialized by the caller. The array needs
  * no clearing: a call reads only partials it wrote itself. Checked mode does

@@ -71,6 +71,49 @@ def test_decode_rows_gpt2_f32():
     assert_close(f64(out), ref, "f32", "gpt2 decode_rows f32")
 
 
+# --- one workgroup per (row, head chunk), launched longest row first ---------------
+# With at most 64 rows and at least 256 (row, head chunk) units the vector-ALU
+# kernel takes each row whole and ranks the rows by attended keys on the
+# device. Ties, empty rows, positions past the cache, windows and sinks all
+# change the ranking; 64 rows is the largest ranked batch, 65 falls back to
+# split rows with a merge.
+@pytest.mark.parametrize("batch,heads", [(24, 16), (64, 4), (65, 4)])
+def test_decode_rows_sorted_dispatch(batch, heads):
+    kvh, d, dtype, max_seq = heads, 64, "f32", 300
+    print(f"[case] decode_rows sorted dispatch B={batch} H={heads} f32", flush=True)
+    g = W.streams(300 + batch)
+    pos = g["extra"].integers(0, max_seq, batch).astype(np.int32)
+    pos[:4] = [-1, max_seq + 50, 17, 17]
+    pos[4:7] = pos[7]                      # ties
+    dv, hv, gg = contiguous_case(300 + batch, batch, heads, kvh, d, max_seq, pos, dtype)
+    sinks_t, sinks64 = host_values(W.normal(gg["sinks"], (heads,)), dtype)
+    o = oracle.default()
+    for window, sk in ((0, None), (100, sinks_t), (1, None)):
+        out = run_decode_rows(*dv, pos, heads, kvh, d, dtype, window=window,
+                              sinks=None if sk is None else dev(sk))
+        ref = o.decode_rows(*hv, pos, window=window, sinks=None if sk is None else sinks64)
+        got = f64(out)
+        assert np.all(got[0] == 0.0)
+        assert_close(got, ref, dtype, f"sorted decode_rows B={batch} W={window}")
+
+
+def test_decode_paged_sorted_dispatch():
+    heads, kvh, d, dtype = 12, 12, 64, "f32"
+    lengths = np.array([700, 1, 64, 65, 300, 300, 1024, 2, 128, 500] * 3, dtype=np.int64)
+    rows = len(lengths)
+    print(f"[case] decode_paged sorted dispatch rows={rows} f32", flush=True)
+    dv, hv, pos, table, otable, g = paged_case(301, rows, heads, kvh, d, lengths, 16, 260, dtype)
+    table = table.copy()
+    otable = otable.copy()
+    table[4, 2] = -1                       # an invalid page inside a row
+    otable[4, 2] = -1
+    o = oracle.default()
+    for window in (0, 200):
+        out = run_decode_paged(*dv, pos, table, heads, kvh, d, dtype, window=window)
+        ref = o.decode_paged(hv[0], hv[1], hv[2], pos, otable, window=window)
+        assert_close(f64(out), ref, dtype, f"sorted decode_paged W={window}")
+
+
 # --- small and edge cases -------------------------------------------------------
 # bf16 with up to 16 query heads per KV head runs on the matrix-core kernel;
 # f32 and larger groups (32 here) on the vector-ALU kernel.

@@ -1,8 +1,8 @@
 """GPU: the paged decode entry point that allocates nothing
 (gqa_decode_paged_noalloc) against gqa_decode_paged with a caller workspace,
 through the C ABI: identical bits on two calls in a row, the second with a
-smaller input, on plans with and without split partials; an oversized plan is
-refused before anything runs."""
+smaller input, on plans with and without split partials, and on the plan with
+the most partials the split rules allow."""
 import numpy as np
 import pytest
 import torch
@@ -27,7 +27,7 @@ def noalloc(q, pk, pv, pos, table, heads, kvh, d, dtype, window=0, sinks=None):
     (32, 8, 128, "bf16", 2, 3000, 8000, 128),   # few rows, long contexts: several splits per row
     (64, 8, 64, "bf16", 1, 4100, 4352, 68),     # gpt-oss-shaped single row: split partials + merge
     (32, 8, 128, "bf16", 64, 512, 2048, 32),    # many rows: one split each, no partials
-    (12, 12, 64, "f32", 3, 500, 1024, 16),      # vector-ALU path (f32): 256-key splits
+    (12, 12, 64, "f32", 3, 500, 1024, 16),      # vector-ALU path (f32): split partials + merge
 ])
 def test_noalloc_matches_workspace_entry(heads, kvh, d, dtype, rows, lo, hi, pages):
     print(f"[case] decode_paged_noalloc H={heads} KvH={kvh} D={d} {dtype} rows={rows}", flush=True)
@@ -47,16 +47,20 @@ def test_noalloc_matches_workspace_entry(heads, kvh, d, dtype, rows, lo, hi, pag
     assert np.array_equal(bits(got2), bits(ref2)), "second (smaller) call differs"
 
 
-def test_noalloc_rejects_oversized_plan():
-    """f32, 64 rows x 32 heads x 8192 keys needs ~34 MB of partials: refused
-    on the host before any launch (the buffers below are never read)."""
-    rows, pages, heads, kvh, d = 64, 128, 32, 8, 128
-    q = torch.zeros((rows, heads, d), dtype=torch.float32, device=DEV)
-    pool = torch.zeros((1, kvh, 64, d), dtype=torch.float32, device=DEV)
-    pos = np.zeros(rows, np.int32)
-    table = np.full((rows, pages), -1, np.int32)
-    out = torch.zeros_like(q)
-    with pytest.raises(gqa.GQAError) as e:
-        gqa.gqa_decode_paged_noalloc(rows, pages, heads, kvh, d, gqa.GQA_F32, 0.0, 0, None, q, pool, pool,
-                                     1, i32(pos), i32(table), out)
-    assert e.value.status == gqa.GQA_ERR_WORKSPACE
+def test_noalloc_largest_plan():
+    """The plan with the most split partials the split rules allow: 511
+    (row, KV head) units of 16 query heads with D 128 take two splits each,
+    1022 x 16 partials of 130 floats (8.5 MB), inside the 16 MB array. Rows
+    share a small pool through the table; bits equal to the workspace entry."""
+    rows, pages, heads, kvh, d, num_pages = 511, 32, 16, 1, 128, 8
+    print(f"[case] decode_paged_noalloc largest plan rows={rows} H={heads} KvH={kvh} D={d}", flush=True)
+    g = np.random.default_rng(515)
+    q = torch.from_numpy(g.standard_normal((rows, heads, d), dtype=np.float32)).to(DEV, torch.bfloat16)
+    pk = torch.from_numpy(g.standard_normal((num_pages, kvh, 64, d), dtype=np.float32)).to(DEV, torch.bfloat16)
+    pv = torch.from_numpy(g.standard_normal((num_pages, kvh, 64, d), dtype=np.float32)).to(DEV, torch.bfloat16)
+    pos = g.integers(1100, pages * 64, rows).astype(np.int32)
+    table = ((np.arange(rows)[:, None] + np.arange(pages)[None, :]) % num_pages).astype(np.int32)
+    ref = run_decode_paged(q, pk, pv, pos, table, heads, kvh, d, "bf16")
+    got = noalloc(q, pk, pv, pos, table, heads, kvh, d, "bf16")
+    assert np.array_equal(bits(got), bits(ref)), "largest plan differs from the workspace entry"
+    assert torch.isfinite(got.float()).all()
