@@ -158,4 +158,29 @@ __device__ __forceinline__ void decode_key_range(int pos, int cap, int window, i
   lo = (int)(l < (long long)cap ? l : (long long)cap);
 }
 
+// Largest batch the decode kernels rank on the device (one row per lane).
+constexpr int kSortMaxRows = 64;
+
+// Row of rank k when rows (at most 64) are ordered by the number of keys they
+// attend, longest first (ties by row index). Every wavefront of the caller
+// computes it on its own: lane l holds row l's key count and counts the rows
+// ahead of it.
+__device__ __forceinline__ int row_of_rank(const int32_t* positions, int rows, int cap, int window,
+                                           int k) {
+  const int lane = threadIdx.x & 63;
+  int n = -1;  // lanes past the last row never match
+  if (lane < rows) {
+    int lo, hi;
+    decode_key_range(positions[lane], cap, window, lo, hi);
+    n = hi >= lo ? hi - lo + 1 : 0;
+  }
+  int rank = 0;
+  for (int j = 0; j < rows; ++j) {
+    const int nj = __builtin_amdgcn_readlane(n, j);
+    rank += (nj > n) | ((nj == n) & (j < lane));
+  }
+  const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < rows && rank == k);
+  return (int)__builtin_ctzll(hit);
+}
+
 }  // namespace gqa

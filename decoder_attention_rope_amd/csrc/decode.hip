@@ -80,28 +80,6 @@ __device__ __forceinline__ float slot_sum(float v) {
 constexpr int kVecLoads = GQA_DECODE_VEC_LOADS;  // K (and V) loads per lane per chunk, at most
 constexpr int kVecWaves = 8;         // wavefronts per workgroup with split rows
 constexpr int kVecWavesSorted = 16;  // ... with one workgroup per row and head chunk
-constexpr int kSortMaxRows = 64;     // rows one wavefront can rank
-
-// Row of rank k when rows (at most 64) are ordered by the number of keys they
-// attend, longest first (ties by row index). Every wavefront of the caller
-// computes it on its own: lane l holds row l's key count and counts the rows
-// ahead of it.
-__device__ __forceinline__ int row_of_rank(const DecodeArgs& a, int k) {
-  const int lane = threadIdx.x & 63;
-  int n = -1;  // lanes past the last row never match
-  if (lane < a.rows) {
-    int lo, hi;
-    decode_key_range(a.positions[lane], a.cap, a.window, lo, hi);
-    n = hi >= lo ? hi - lo + 1 : 0;
-  }
-  int rank = 0;
-  for (int j = 0; j < a.rows; ++j) {
-    const int nj = __builtin_amdgcn_readlane(n, j);
-    rank += (nj > n) | ((nj == n) & (j < lane));
-  }
-  const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < a.rows && rank == k);
-  return (int)__builtin_ctzll(hit);
-}
 
 template <typename T, int D, int GC, bool PAGED, int NW, bool SORTED>
 __global__ __launch_bounds__(64 * NW) void decode_vec_kernel(DecodeArgs a) {
@@ -116,7 +94,7 @@ __global__ __launch_bounds__(64 * NW) void decode_vec_kernel(DecodeArgs a) {
   const int split = blockIdx.x;
   // Sorted dispatch (one split): workgroups are launched in blockIdx order,
   // so the longest rows start first and shorter ones fill in behind them.
-  const int r = SORTED ? __builtin_amdgcn_readfirstlane(row_of_rank(a, blockIdx.z)) : blockIdx.z;
+  const int r = SORTED ? __builtin_amdgcn_readfirstlane(row_of_rank(a.positions, a.rows, a.cap, a.window, blockIdx.z)) : blockIdx.z;
   const int G = a.heads / a.kv_heads;
   const int nchunks = G / GC;
   const int kh = blockIdx.y / nchunks;

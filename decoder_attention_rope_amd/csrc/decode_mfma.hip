@@ -32,6 +32,10 @@
 // * The split length is chosen per call: as long as possible while the grid
 //   still fills the chip. With a single split per (row, KV head) the kernel
 //   also normalizes (and adds the sink) and writes the output directly.
+// * With one split and at most 64 rows the workgroups take the rows in order
+//   of decreasing key count, ranked on the device from the positions: only
+//   one workgroup fits a CU at D = 128, so the grid runs in rounds, and
+//   starting the longest rows first keeps the last round short.
 // * A chunk whose page id is out of range contributes nothing.
 // The merge of the split partials (and the sink term) is shared with the
 // vector-ALU path in decode.hip.
@@ -66,9 +70,13 @@ __device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3;
 __device__ __forceinline__ int kt_swz(int k) { return (k & 3) | ((k >> 1) & 4); }
 }  // namespace
 
-template <int D, bool PAGED>
-__global__ __launch_bounds__(64 * kWaves, GQA_DECODE_MIN_WAVES_PER_SIMD) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int NW = kWaves;
+#ifndef GQA_DECODE_SORTED_WAVES
+#define GQA_DECODE_SORTED_WAVES 8
+#endif
+constexpr int kWavesSorted = GQA_DECODE_SORTED_WAVES;  // ... with sorted dispatch
+
+template <int D, bool PAGED, int NW, bool SORTED>
+__global__ __launch_bounds__(64 * NW, NW == kWaves ? GQA_DECODE_MIN_WAVES_PER_SIMD : 1) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KK = D / 32;               // 32-wide k-steps of QK over the head dim
   constexpr int NB = D / 16;               // 16-wide d-blocks of O
   constexpr int VROWS = D == 128 ? 8 : 4;  // V rows loaded per lane per chunk
@@ -84,7 +92,11 @@ __global__ __launch_bounds__(64 * kWaves, GQA_DECODE_MIN_WAVES_PER_SIMD) void de
 
   const int split = blockIdx.x;
   const int kh = blockIdx.y;
-  const int r = blockIdx.z;
+  // Sorted dispatch (one split, at most 64 rows): workgroups start in
+  // blockIdx order, so ranking the rows by attended keys makes the longest
+  // start first.
+  const int r = SORTED ? __builtin_amdgcn_readfirstlane(row_of_rank(a.positions, a.rows, a.cap, a.window, blockIdx.z))
+                       : blockIdx.z;
   const int G = a.heads / a.kv_heads;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,7 +115,7 @@ __global__ __launch_bounds__(64 * kWaves, GQA_DECODE_MIN_WAVES_PER_SIMD) void de
     // with a single split this workgroup owns the output, which is 0.
     if (a.nsplit == 1) {
       uint16_t* out = static_cast<uint16_t*>(a.out) + ((long long)r * a.heads + kh * G) * D;
-      for (int x = tid; x < G * D; x += 64 * kWaves) out[x] = 0;
+      for (int x = tid; x < G * D; x += 64 * NW) out[x] = 0;
     }
     return;
   }
@@ -337,15 +349,22 @@ int decode_mfma_split_len(int rows, int kv_heads, int cap) {
   return (int)len;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
+template <int D, bool PAGED>
+static void launch_mfma_t(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.nsplit, a.kv_heads, a.rows);
-  dim3 block(64 * kWaves);
+  if (a.nsplit == 1 && a.rows <= kSortMaxRows)
+    decode_mfma_kernel<D, PAGED, kWavesSorted, true><<<grid, dim3(64 * kWavesSorted), 0, stream>>>(a);
+  else
+    decode_mfma_kernel<D, PAGED, kWaves, false><<<grid, dim3(64 * kWaves), 0, stream>>>(a);
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   if (a.head_dim == 128) {
-    if (a.paged) decode_mfma_kernel<128, true><<<grid, block, 0, stream>>>(a);
-    else decode_mfma_kernel<128, false><<<grid, block, 0, stream>>>(a);
+    if (a.paged) launch_mfma_t<128, true>(a, stream);
+    else launch_mfma_t<128, false>(a, stream);
   } else {
-    if (a.paged) decode_mfma_kernel<64, true><<<grid, block, 0, stream>>>(a);
-    else decode_mfma_kernel<64, false><<<grid, block, 0, stream>>>(a);
+    if (a.paged) launch_mfma_t<64, true>(a, stream);
+    else launch_mfma_t<64, false>(a, stream);
   }
   return hipGetLastError();
 }
