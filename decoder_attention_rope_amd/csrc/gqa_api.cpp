@@ -376,7 +376,8 @@ static int prefill_cached_impl(int32_t n, int32_t heads, int32_t kv_heads, int32
                                int32_t cache_dim0, int32_t cache_seq, const int32_t* table,
                                int32_t table_rows, int32_t table_pages, void* out,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               bool launch, bool check) {
+                               bool launch, bool check,
+                               const gqa::DecodeArgs* with_decode = nullptr) {
   if (n < 0 || window < 0) return GQA_ERR_INVALID_ARG;
   int st = check_heads(heads, kv_heads, head_dim, dtype);
   if (st != GQA_OK) return st;
@@ -443,6 +444,8 @@ static int prefill_cached_impl(int32_t n, int32_t heads, int32_t kv_heads, int32
     a.table_pages = table_pages;
     a.num_pages = cache_dim0;
   }
+  if (with_decode != nullptr)
+    return hip_status(gqa::launch_prefill_step(a, *with_decode, static_cast<hipStream_t>(stream)));
   return hip_status(gqa::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -543,6 +546,34 @@ int gqa_decode_rows(int32_t batch, int32_t heads, int32_t kv_heads, int32_t head
                           !g_dry_run, g_checked != 0);
 }
 
+static gqa::DecodeArgs paged_decode_args(int32_t rows, int32_t pages, int32_t heads,
+                                         int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                                         float scale, int32_t window, const void* sinks,
+                                         const void* q, const void* pool_k, const void* pool_v,
+                                         int32_t num_pages, const int32_t* positions,
+                                         const int32_t* table, void* out) {
+  gqa::DecodeArgs a{};
+  a.rows = rows;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.head_dim = head_dim;
+  a.dtype = dtype;
+  a.scale_log2 = effective_scale_log2(scale, head_dim);
+  a.window = window;
+  a.sinks = sinks;
+  a.q = q;
+  a.k = pool_k;
+  a.v = pool_v;
+  a.positions = positions;
+  a.table = table;
+  a.paged = 1;
+  a.cap = pages * GQA_PAGE_SIZE;
+  a.pages = pages;
+  a.num_pages = num_pages;
+  a.out = out;
+  return a;
+}
+
 static int decode_paged_impl(int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
                      int32_t head_dim, int32_t dtype, float scale, int32_t window,
                      const void* sinks, const void* q, const void* pool_k, const void* pool_v,
@@ -564,25 +595,8 @@ static int decode_paged_impl(int32_t rows, int32_t pages, int32_t heads, int32_t
     st = run_checks(&c, 1, stream);
     if (st != GQA_OK) return st;
   }
-  gqa::DecodeArgs a{};
-  a.rows = rows;
-  a.heads = heads;
-  a.kv_heads = kv_heads;
-  a.head_dim = head_dim;
-  a.dtype = dtype;
-  a.scale_log2 = effective_scale_log2(scale, head_dim);
-  a.window = window;
-  a.sinks = sinks;
-  a.q = q;
-  a.k = pool_k;
-  a.v = pool_v;
-  a.positions = positions;
-  a.table = table;
-  a.paged = 1;
-  a.cap = pages * GQA_PAGE_SIZE;
-  a.pages = pages;
-  a.num_pages = num_pages;
-  a.out = out;
+  gqa::DecodeArgs a = paged_decode_args(rows, pages, heads, kv_heads, head_dim, dtype, scale, window,
+                                        sinks, q, pool_k, pool_v, num_pages, positions, table, out);
   if (noalloc) {
     // The split partials go to the library's own device array.
     if (gqa::decode_partials_bytes(a) > gqa::kDecodeScratchBytes) return GQA_ERR_WORKSPACE;
@@ -736,6 +750,19 @@ int gqa_step_paged(int32_t p, int32_t rows, int32_t pages, int32_t heads, int32_
                                  window);
     st = run_checks(c, nc, stream);
     if (st != GQA_OK) return st;
+  }
+  if (p > 0 && rows > 0) {
+    // Decode tokens and chunk tokens in one grid when the decode runs on
+    // matrix cores: its workgroups stream the cache beside the prefill tiles.
+    const gqa::DecodeArgs d = paged_decode_args(
+        rows, pages, heads, kv_heads, head_dim, dtype, scale, window, sinks,
+        static_cast<const char*>(q) + p * row, pool_k, pool_v, num_pages, step_positions, table,
+        static_cast<char*>(out) + p * row);
+    if (gqa::decode_mfma_supported(d))
+      return prefill_cached_impl(p, heads, kv_heads, head_dim, dtype, scale, window, sinks, q,
+                                 token_rows, positions, GQA_CACHE_PAGED_TABLE, pool_k, pool_v,
+                                 num_pages, GQA_PAGE_SIZE, table, rows, pages, out, ws, pre_ws,
+                                 stream, true, false, &d);
   }
   if (rows > 0) {
     s2 = decode_paged_impl(rows, pages, heads, kv_heads, head_dim, dtype, scale, window, sinks,

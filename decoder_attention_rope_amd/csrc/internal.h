@@ -121,6 +121,9 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 
 size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// A cached paged prefill and a one-split matrix-core paged decode (bf16,
+// G <= 16, same head dim) in one grid; `d` needs no workspace.
+hipError_t launch_prefill_step(const PrefillArgs& a, DecodeArgs d, hipStream_t stream);
 
 // Backward of the packed prefill (bf16): dq [p, heads, D], dk / dv
 // [p, kv_heads, D] from q, k, v, the forward's out and lse, and dout.

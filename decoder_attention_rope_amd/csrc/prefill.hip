@@ -39,6 +39,7 @@
 
 #include "attn_tiles.h"
 #include "common.h"
+#include "decode_mfma.h"
 #include "internal.h"
 
 namespace gqa {
@@ -284,8 +285,11 @@ constexpr int prefill_waves() { return 4; }
 template <int GW>
 constexpr int prefill_ahead() { return 1; }
 
+// One workgroup of the prefill: the query tile and head group of the bid-th
+// work record, in `smem_raw` (Lds<...>::total bytes, 16-byte aligned).
 template <int D, int GW, int SRC>
-__global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) void prefill_kernel(PrefillArgs a, Plan pl) {
+__device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Plan& pl, int bid,
+                                             char* smem_raw) {
   constexpr int NW = prefill_waves<GW>();
   constexpr int AHEAD = prefill_ahead<GW>();
   constexpr int NKB = AHEAD + 1;  // K (and V) buffers
@@ -298,13 +302,12 @@ __global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) 
   static_assert(TQ <= 128, "cache-row leaders fit a 128-bit mask");
   using L = Lds<D, NKB, NPB>;
 
-  __shared__ __attribute__((aligned(16))) char smem_raw[L::total];
   LdsByte* smem = (LdsByte*)smem_raw;
 
   const int G = a.heads / a.kv_heads;
   const int n_groups = a.kv_heads * pl.head_groups;
-  const int wi = blockIdx.x / n_groups;
-  const int grp = blockIdx.x % n_groups;
+  const int wi = bid / n_groups;
+  const int grp = bid % n_groups;
   const int kh = grp / pl.head_groups;
   const int hg = grp % pl.head_groups;
   // Tile indices are workgroup-uniform: keep them (and the summary loads that
@@ -994,9 +997,34 @@ __global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) 
   }
 }
 
+template <int D, int GW, int SRC>
+__global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) void prefill_kernel(PrefillArgs a, Plan pl) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[Lds<D, prefill_ahead<GW>() + 1, 4>::total];
+  prefill_body<D, GW, SRC>(a, pl, blockIdx.x, smem_raw);
+}
 
-// ---------------------------------------------------------------------------
-// Host side.
+// One step of step_paged in a single grid: the first n_dec workgroups each
+// decode one (decode row, KV head) over its whole key range -- one split, so
+// they write the output themselves -- and the rest are the chunk's prefill
+// workgroups in their usual order. The decode shares start first and stream
+// the cache (each wavefront loading its next chunk while it computes the
+// current one) while the prefill tiles keep the matrix cores busy. Measured
+// alternatives were slower: the decode shares last in the grid, and rows
+// split into 1024- or 2048-key pieces (more workgroups plus a merge pass).
+template <int D, int GW>
+__global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) void step_paged_kernel(PrefillArgs a, Plan pl, DecodeArgs d, int n_dec) {
+  constexpr int NW = prefill_waves<GW>();
+  constexpr int kPre = Lds<D, prefill_ahead<GW>() + 1, 4>::total;
+  constexpr int kDec = decode_mfma_lds_bytes<D, NW>();
+  __shared__ __attribute__((aligned(16))) char smem_raw[kPre > kDec ? kPre : kDec];
+  const int bid = blockIdx.x;
+  if (bid < n_dec) {
+    decode_mfma_body<D, true, NW, false, true>(d, 0, bid % d.kv_heads, bid / d.kv_heads, smem_raw);
+    return;
+  }
+  prefill_body<D, GW, kSrcPaged>(a, pl, bid - n_dec, smem_raw);
+}
+
 // ---------------------------------------------------------------------------
 static int group_width(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
 
@@ -1077,6 +1105,34 @@ hipError_t prefill_order(const Plan& pl, hipStream_t stream) {
 hipError_t prefill_summarize(const PrefillArgs& a, const Plan& pl, hipStream_t stream) {
   const int n_tiles = pl.n_kt + pl.n_qt;
   prefill_summarize_kernel<<<dim3((n_tiles + 3) / 4), dim3(256), 0, stream>>>(a, pl);
+  return hipGetLastError();
+}
+
+template <int D, int GW>
+static void launch_step(const PrefillArgs& a, const Plan& pl, const DecodeArgs& d,
+                        hipStream_t stream) {
+  const int n_groups = a.kv_heads * pl.head_groups;
+  const int n_dec = d.rows * d.kv_heads;
+  const dim3 grid(n_dec + pl.n_qt * n_groups), block(64 * prefill_waves<GW>());
+  step_paged_kernel<D, GW><<<grid, block, 0, stream>>>(a, pl, d, n_dec);
+}
+
+hipError_t launch_prefill_step(const PrefillArgs& a, DecodeArgs d, hipStream_t stream) {
+  d.split_len = d.cap;
+  d.nsplit = 1;
+  d.ws = nullptr;
+  Plan pl;
+  const hipError_t e = prefill_prepare(a, pl, stream);
+  if (e != hipSuccess) return e;
+  if (a.head_dim == 64) {
+    if (pl.gw == 4) launch_step<64, 4>(a, pl, d, stream);
+    else if (pl.gw == 2) launch_step<64, 2>(a, pl, d, stream);
+    else launch_step<64, 1>(a, pl, d, stream);
+  } else {
+    if (pl.gw == 4) launch_step<128, 4>(a, pl, d, stream);
+    else if (pl.gw == 2) launch_step<128, 2>(a, pl, d, stream);
+    else launch_step<128, 1>(a, pl, d, stream);
+  }
   return hipGetLastError();
 }
 

@@ -52,9 +52,15 @@ def test_step_packed(heads, kvh, d, window, use_sinks):
     assert_close(got[batch:], ref_pre, "bf16", "step_packed packed part")
 
 
-@pytest.mark.parametrize("heads,kvh,d", [(32, 8, 128), (64, 8, 64)])
-def test_step_paged(heads, kvh, d):
-    print(f"[case] step_paged H={heads} KvH={kvh} D={d}", flush=True)
+# Up to 16 query heads per KV head the decode tokens run in the same grid as
+# the chunk (matrix-core decode workgroups first); with more (G = 32 here) the
+# decode runs as its own vector-ALU pass before the chunk.
+@pytest.mark.parametrize("heads,kvh,d,window,use_sinks,bad_page", [
+    (32, 8, 128, 0, False, False), (64, 8, 64, 0, False, False),
+    (64, 8, 64, 128, True, True), (32, 2, 128, 300, False, True), (32, 1, 64, 0, True, False)])
+def test_step_paged(heads, kvh, d, window, use_sinks, bad_page):
+    print(f"[case] step_paged H={heads} KvH={kvh} D={d} W={window} sinks={use_sinks} "
+          f"bad_page={bad_page}", flush=True)
     g = W.streams(2500 + heads + d)
     rows, num_pages = 12, 200
     lengths, dec_pos, table = W.paged_layout(rows, 40, 900, num_pages, 64, g["index"], max_len=1024)
@@ -71,16 +77,28 @@ def test_step_paged(heads, kvh, d):
     crow = np.asarray(crow, np.int32)
     cpos = np.asarray(cpos, np.int32)
     p = len(cpos)
+    if bad_page:
+        # a page outside the pool in a decode-only row and one in a chunk row:
+        # both contribute no keys; row 11 attends nothing
+        table = table.copy()
+        table[2, 0] = num_pages
+        table[5, 0] = -3
+        dec_pos = dec_pos.copy()
+        dec_pos[11] = -1
     q_t, q64 = host_values(W.normal(g["q"], (p + rows, heads, d)), "bf16")
+    sk_t, sk64 = host_values(W.normal(g["sinks"], (heads,)), "bf16")
+    sinks, sk = (dev(sk_t), sk64) if use_sinks else (None, None)
     out = torch.full((p + rows, heads, d), float("nan"), dtype=torch.bfloat16, device=DEV)
     ws, nb = workspace(gqa.gqa_step_paged_workspace(p, rows, table.shape[1], heads, kvh, d))
-    gqa.gqa_step_paged(p, rows, table.shape[1], heads, kvh, d, CODE["bf16"], 0.0, 0, None,
+    gqa.gqa_step_paged(p, rows, table.shape[1], heads, kvh, d, CODE["bf16"], 0.0, window, sinks,
                        dev(q_t), i32(crow), i32(cpos), dev(pk_t), dev(pv_t), num_pages, i32(table),
                        i32(dec_pos), out, ws, nb)
     torch.cuda.synchronize()
     o = oracle.default()
-    ref_pre = o.prefill_paged(q64[:p], crow, cpos, pk64, pv64, table)
-    ref_dec = o.decode_paged(q64[p:], pk64, pv64, dec_pos, table)
+    ref_pre = o.prefill_paged(q64[:p], crow, cpos, pk64, pv64, table, window=window, sinks=sk)
+    ref_dec = o.decode_paged(q64[p:], pk64, pv64, dec_pos, table, window=window, sinks=sk)
     got = f64(out)
     assert_close(got[:p], ref_pre, "bf16", "step_paged chunk part")
     assert_close(got[p:], ref_dec, "bf16", "step_paged decode part")
+    if bad_page:
+        assert np.all(got[p + 11] == 0.0)
