@@ -11,8 +11,7 @@
 // The pass is HBM-bound: one thread owns one 16-byte chunk of the low half of
 // a head and the matching chunk of the high half, so every load and store is
 // a full 16-byte vector and the rotation needs no cross-lane traffic. The
-// rotation is evaluated in fp64 (the bf16 x bf16 and f32 x f32 products are
-// exact there) and rounded once to T.
+// rotation is the exact value rounded once to T (rope_common.h).
 #include "common.h"
 #include "internal.h"
 #include "rope_common.h"

@@ -3,8 +3,9 @@
 //
 // `rope` of the Linnet "examples/01-llama" page (src/attention.linnet) pairs
 // dimension i with i + D/2 (rotate-half); the rotation of T values by T table
-// entries is evaluated in fp64, where the bf16 x bf16 and f32 x f32 products
-// are exact, and rounded once to T. write_at ("a masked select", section Key
+// entries is the exact value rounded once to T (bf16: an f32 fma of exact
+// products, fp64 for the rare f32 results on a bf16 midpoint; f32: fp64,
+// where the f32 x f32 products are exact). write_at ("a masked select", section Key
 // ideas) drops a write whose target is outside the cache; the serving entries
 // of the Nest llama-3.1-8b-instruct card address the cache by row and
 // position, by table page, or by physical slot.
@@ -19,7 +20,19 @@ template <typename T>
 __device__ __forceinline__ void rotate_chunk(u32x4& lo, u32x4& hi, const u32x4& cw,
                                              const u32x4& sw);
 
-// bf16: 8 elements per 16-byte chunk.
+// bf16: 8 elements per 16-byte chunk. A product of two bf16 values is exact
+// in f32, so fma(a, b, c * d) is the exact a b + c d rounded once to f32.
+// Rounding that f32 to bf16 (nearest-even) gives the correctly rounded
+// result unless the f32 value sits exactly on a bf16 midpoint (low 16 bits
+// 0x8000): a bf16 midpoint is itself an f32 value, so the first rounding can
+// land on one but never cross one. Only then is the value recomputed in fp64
+// and rounded once.
+__device__ __forceinline__ uint16_t rot_bf16(float a, float b, float c, float d) {
+  const float y = __builtin_fmaf(a, b, c * d);
+  if ((__float_as_uint(y) & 0xffffu) != 0x8000u) return f32_to_bf16(y);
+  return f64_to_bf16((double)a * (double)b + (double)c * (double)d);
+}
+
 template <>
 __device__ __forceinline__ void rotate_chunk<uint16_t>(u32x4& lo, u32x4& hi, const u32x4& cw,
                                                        const u32x4& sw) {
@@ -31,10 +44,8 @@ __device__ __forceinline__ void rotate_chunk<uint16_t>(u32x4& lo, u32x4& hi, con
   uint16_t yl[8], yh[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const double ylo = (double)xl[e] * (double)c[e] - (double)xh[e] * (double)s[e];
-    const double yhi = (double)xh[e] * (double)c[e] + (double)xl[e] * (double)s[e];
-    yl[e] = f64_to_bf16(ylo);
-    yh[e] = f64_to_bf16(yhi);
+    yl[e] = rot_bf16(xl[e], c[e], -xh[e], s[e]);
+    yh[e] = rot_bf16(xh[e], c[e], xl[e], s[e]);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

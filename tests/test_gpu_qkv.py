@@ -53,7 +53,7 @@ def run_case(n, hidden, heads, kvh, d, bias, rope, cache, seed, k_out=True, sel=
     wk_t, wk64 = host_values(W.normal(g["v"], (kvh * d, hidden)) * xs, "bf16")
     wv_t, wv64 = host_values(W.normal(g["extra"], (kvh * d, hidden)) * xs, "bf16")
     b = [host_values(W.normal(g["sinks"], (f,)), "bf16") for f in (heads * d, kvh * d, kvh * d)]
-    max_pos, theta = 4096, 500000.0
+    max_pos, theta = max(4096, n), 500000.0
     # distinct positions: two tokens with one cache target would race
     pos = g["index"].permutation(max(n, 700))[:n].astype(np.int32)
     tab = torch.empty((2, max_pos, d // 2), dtype=torch.bfloat16, device=DEV)
@@ -125,6 +125,7 @@ def run_case(n, hidden, heads, kvh, d, bias, rope, cache, seed, k_out=True, sel=
     (300, 1024, 8, 2, 128, False, True, "paged"),
     (150, 2880, 64, 8, 64, True, False, "slots"),
     (129, 768, 4, 4, 64, False, True, "none"),
+    (130, 512, 4, 1, 128, True, True, "contiguous"),   # kv features not a multiple of 256
 ])
 def test_qkv_rope_write(n, hidden, heads, kvh, d, bias, rope, cache):
     print(f"[case] qkv n={n} H={hidden} heads={heads} kvh={kvh} D={d} bias={bias} rope={rope} "
@@ -137,10 +138,12 @@ def test_qkv_rope_write_no_k_out():
     run_case(100, 512, 8, 2, 128, True, True, "contiguous", seed=2700, k_out=False)
 
 
-def test_qkv_llama8b_sampled():
-    """Llama-3.1-8B projections (hidden 4096, 32 / 8 heads, D 128) over 2048
-    tokens; 24 sampled tokens checked against the oracle."""
+@pytest.mark.parametrize("n", [2048, 16384])
+def test_qkv_llama8b_sampled(n):
+    """Llama-3.1-8B projections (hidden 4096, 32 / 8 heads, D 128); 24 sampled
+    tokens checked against the oracle. 16384 tokens is the full prefill batch
+    (64 token tiles: the XCD-banded tile order)."""
     g = W.streams(2800)
-    sel = np.sort(W.sample_indices(2048, 24, g["index"]))
-    print("[case] qkv llama8b n=2048 sampled", flush=True)
-    run_case(2048, 4096, 32, 8, 128, False, True, "none", seed=2800, sel=sel)
+    sel = np.sort(W.sample_indices(n, 24, g["index"]))
+    print(f"[case] qkv llama8b n={n} sampled", flush=True)
+    run_case(n, 4096, 32, 8, 128, False, True, "none", seed=2800, sel=sel)
