@@ -436,6 +436,14 @@ def source_sha(*names):
     return h.hexdigest()[:16]
 
 
+# Sources each measured kernel is built from: a committed traffic figure is
+# used only while they hash as they did when the counters were taken.
+DECODE_SOURCES = ["decode.hip", "decode_mfma.hip", "decode_mfma.h", "common.h"]
+PREFILL_SOURCES = ["prefill.hip", "attn_tiles.h", "common.h"]
+STEP_SOURCES = ["prefill.hip", "decode_mfma.h", "attn_tiles.h", "common.h"]
+QKV_SOURCES = ["qkv.hip", "rope_common.h", "attn_tiles.h", "common.h"]
+
+
 def traffic_for(kernel, sources):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
@@ -625,7 +633,7 @@ def main():
     c_tflops = c_flops / c_s / 1e12
     chunk_roof = {"bound": "mfma", "achieved": c_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                   "unit": "TFLOP/s", "frac": c_tflops / MFMA_BF16_PEAK_TFLOPS,
-                  "traffic": traffic_for("prefill_cached_paged", ["prefill.hip", "attn_tiles.h", "common.h"]),
+                  "traffic": traffic_for("prefill_cached_paged", PREFILL_SOURCES),
                   "algorithmic_flops": c_flops, "avg_us": c_s * 1e6,
                   "workload": f"{ec['rows']} rows, prefixes U[{ec['pre_lo']}, {ec['pre_hi']}] "
                               f"({int(c_pre.sum())} keys), chunk {ec['chunk']}, paged"}
@@ -659,7 +667,8 @@ def main():
     s_flops = c_flops + 4 * D * H * int(np.sum(s_pos.astype(np.int64) + 1))
     s_tflops = s_flops / s_s / 1e12
     step_roof = {"bound": "mfma", "achieved": s_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-                 "unit": "TFLOP/s", "frac": s_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                 "unit": "TFLOP/s", "frac": s_tflops / MFMA_BF16_PEAK_TFLOPS,
+                 "traffic": traffic_for("step_paged", STEP_SOURCES),
                  "algorithmic_flops": s_flops, "avg_us": s_s * 1e6,
                  "workload": f"step_paged: the {cn} chunk tokens above + {s_rows} decode tokens"}
 
@@ -700,7 +709,7 @@ def main():
     q_flops = 2 * P * hid * (H + 2 * KVH) * D
     qkv_roof = {"bound": "mfma", "achieved": q_flops / q_s / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": q_flops / q_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                "traffic": traffic_for("qkv_rope_write", ["qkv.hip", "rope_common.h", "common.h"]),
+                "traffic": traffic_for("qkv_rope_write", QKV_SOURCES),
                 "algorithmic_flops": q_flops, "avg_us": q_s * 1e6,
                 "hipblaslt_gemm_only_us": mm_s * 1e6,
                 "workload": f"{P} tokens x hidden {hid} -> (32 + 8 + 8) x 128, rope, contiguous cache"}
@@ -755,11 +764,11 @@ def main():
 
     dec_roof = {"bound": "hbm", "achieved": decode_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": decode_gbs / HBM_PEAK_GBS,
-                "traffic": traffic_for("decode_paged", ["decode.hip", "decode_mfma.hip", "common.h"]),
+                "traffic": traffic_for("decode_paged", DECODE_SOURCES),
                 "algorithmic_bytes": decode_bytes, "avg_us": dec_s * 1e6}
     pre_roof = {"bound": "mfma", "achieved": prefill_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": prefill_tflops / MFMA_BF16_PEAK_TFLOPS,
-                "traffic": traffic_for("prefill_packed", ["prefill.hip", "attn_tiles.h", "common.h"]),
+                "traffic": traffic_for("prefill_packed", PREFILL_SOURCES),
                 "algorithmic_flops": prefill_flops, "avg_us": pre_s * 1e6}
     dominant = "prefill_packed" if pre_s >= dec_s else "decode_paged"
     roof = dict(pre_roof if dominant == "prefill_packed" else dec_roof)
