@@ -25,19 +25,21 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// f32 -> bf16, round to nearest, ties to even, computed on the integer
-// pattern (select, no branch); NaN stays a quiet NaN. Used wherever the
-// result is compared bit for bit.
+// f32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN. One
+// v_cvt_pk_bf16_f32: the hardware converter rounds every finite and infinite
+// f32 exactly as the integer nearest-even formula
+// (u + 0x7fff + ((u >> 16) & 1)) >> 16 does (checked over all 2^32 patterns),
+// so results compared bit for bit are unchanged. The empty asm keeps the f32
+// value opaque: otherwise the compiler folds a preceding fp64 -> f32
+// conversion into one fp64 -> bf16 rounding, which differs from rounding
+// through f32 (the rotary tables depend on the two steps).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t q = (u >> 16) | 0x0040u;
-  return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? q : r);
+  asm("" : "+v"(f));
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// Two f32 -> packed bf16 with the hardware converter (v_cvt_pk_bf16_f32), for
-// matrix-core operands where the last-bit rounding choice on exact ties does
-// not matter.
+// Two f32 -> packed bf16 with one v_cvt_pk_bf16_f32 (nearest-even, as
+// f32_to_bf16).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2_t r;
