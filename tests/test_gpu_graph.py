@@ -172,3 +172,72 @@ def test_graph_replay_training_pair_matches_eager():
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(results(), ref)):
             assert _same(a, b), f"replay {rep}: result {i} differs from the eager run"
+
+
+def test_graph_replay_sorted_decode_and_step_paged():
+    """The launches whose dispatch order is ranked on the device (sorted decode:
+    matrix-core bf16 paged rows and vector-ALU f32 contiguous rows) and the
+    single-grid step_paged (decode and chunk workgroups in one launch)."""
+    print("[case] graph capture: sorted paged/rows decode + step_paged", flush=True)
+    g = W.streams(779)
+    bf = torch.bfloat16
+    # bf16 paged decode, 64 rows x 8 KV heads: one split, ranked rows.
+    heads, kvh, d, num_pages = 32, 8, 128, 700
+    lengths, dpos, table = W.paged_layout(64, 1, 600, num_pages, 64, g["index"], max_len=640)
+    dpos = dpos.copy()
+    dpos[3] = -1                                     # a row that attends nothing
+    pk = dev(host_values(W.normal(g["pool_k"], (num_pages, kvh, 64, d)), "bf16")[0])
+    pv = dev(host_values(W.normal(g["pool_v"], (num_pages, kvh, 64, d)), "bf16")[0])
+    qd = dev(host_values(W.normal(g["q"], (64, heads, d)), "bf16")[0])
+    dpos_t, table_t = i32(dpos), i32(table)
+    pages = table.shape[1]
+    out_d = torch.empty((64, heads, d), dtype=bf, device=DEV)
+    wsd, nbd = workspace(gqa.gqa_decode_paged_workspace(64, pages, heads, kvh, d))
+    # f32 contiguous decode, 32 rows x 12 heads (one head per KV head): ranked rows.
+    fh, fd, fmax = 12, 64, 400
+    fpos = i32(g["extra"].integers(0, fmax, 32).astype(np.int32))
+    fk = dev(host_values(W.normal(g["k"], (32, fh, fmax, fd)), "f32")[0])
+    fv = dev(host_values(W.normal(g["v"], (32, fh, fmax, fd)), "f32")[0])
+    fq = dev(host_values(W.normal(g["q"], (32, fh, fd)), "f32")[0])
+    out_f = torch.empty((32, fh, fd), dtype=torch.float32, device=DEV)
+    wsf, nbf = workspace(gqa.gqa_decode_rows_workspace(32, fh, fh, fd, fmax))
+    # step_paged: the last 48 positions of rows 0, 5, 9 as the chunk, all 64 rows decode.
+    crow, cpos = [], []
+    for r in (0, 5, 9):
+        c = min(int(lengths[r]), 48)
+        crow += [r] * c
+        cpos += list(range(int(lengths[r]) - c, int(lengths[r])))
+    p = len(cpos)
+    qs = dev(host_values(W.normal(g["sinks"], (p + 64, heads, d)), "bf16")[0])
+    crow_t, cpos_t = i32(np.asarray(crow, np.int32)), i32(np.asarray(cpos, np.int32))
+    out_s = torch.empty((p + 64, heads, d), dtype=bf, device=DEV)
+    wss, nbs = workspace(gqa.gqa_step_paged_workspace(p, 64, pages, heads, kvh, d))
+
+    def work():
+        gqa.gqa_decode_paged(64, pages, heads, kvh, d, gqa.GQA_BF16, 0.0, 0, None, qd, pk, pv,
+                             num_pages, dpos_t, table_t, out_d, wsd, nbd)
+        gqa.gqa_decode_rows(32, fh, fh, fd, gqa.GQA_F32, 0.0, 0, None, fq, fk, fv, fmax, fpos,
+                            out_f, wsf, nbf)
+        gqa.gqa_step_paged(p, 64, pages, heads, kvh, d, gqa.GQA_BF16, 0.0, 0, None, qs, crow_t,
+                           cpos_t, pk, pv, num_pages, table_t, dpos_t, out_s, wss, nbs)
+
+    outs = (out_d, out_f, out_s)
+    work()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in outs]
+    assert all(torch.isfinite(x.float()).all() for x in ref)
+    assert bool((ref[0][3] == 0).all())
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in outs:
+            x.fill_(float("nan"))
+        _ = torch.randn(4096, device=DEV).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert _same(a, b), f"replay {rep}: result {i} differs from the eager run"
