@@ -54,6 +54,7 @@ struct Plan {
   int* nfull;      // [n_qt] fully allowed tiles in each visit list
   int n_kt, n_qt, n_kg, tq, head_groups, gw;
   int max_cost;    // costs are clamped to [0, max_cost] for the ordering
+  int resident;    // forward workgroups resident at once on the device (0: unknown)
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

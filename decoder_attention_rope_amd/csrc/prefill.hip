@@ -34,6 +34,7 @@
 //   tile's visited key-tile range and cost (one wavefront per tile), then
 //   order the query tiles costliest first (a counting sort); workgroup index i * n_groups + g maps KV head g to the
 //   round-robin XCD g % 8, keeping one head's K/V in one XCD's L2.
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -177,6 +178,7 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(PrefillArgs a, Plan p
 // affects scheduling, never results.
 // ---------------------------------------------------------------------------
 constexpr int kMaxCostBins = 4096;
+constexpr int kTouchMinTiles = 8;  // see touch_next in prefill_body
 
 __global__ __launch_bounds__(kPrepThreads) void prefill_order_kernel(Plan pl) {
   __shared__ int start[kMaxCostBins + 1];
@@ -265,7 +267,8 @@ struct Lds {
   static constexpr int kOff(int buf) { return buf * kBytes; }
   static constexpr int vOff(int buf) { return NKB * kBytes + buf * vBytes; }
   static constexpr int posOff(int buf) { return NKB * (kBytes + vBytes) + buf * 2 * kBK * 4; }
-  static constexpr int total = posOff(NPB);
+  static constexpr int touchOff = posOff(NPB);  // 256 bytes nobody reads (see touch_next)
+  static constexpr int total = touchOff + 256;
 };
 // Chunk swizzle of V row r (see above).
 template <int D>
@@ -314,6 +317,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Plan& p
   // depend on them) on the scalar unit.
   const int* rec = pl.rec + (long long)wi * kRecInts;
   const int qt = __builtin_amdgcn_readfirstlane(ld_const(rec, 0));
+  // Query tile of the workgroup pl.resident indices later (-1: none).
+  const int bid_next = bid + pl.resident;
+  const int qt_next = pl.resident > 0 && bid_next < pl.n_qt * n_groups
+                          ? __builtin_amdgcn_readfirstlane(ld_const(pl.rec + (long long)(bid_next / n_groups) * kRecInts, 0))
+                          : -1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -507,6 +515,37 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Plan& p
   // first; the online softmax does not depend on the order of the key
   // tiles). The first kRecVis entries come with the start record.
   const int v_n = __builtin_amdgcn_readfirstlane(ld_const(rec, 1)) + __builtin_amdgcn_readfirstlane(ld_const(rec, 2));
+
+  // Packed keys: the workgroup pl.resident indices later will most likely
+  // start when one of the workgroups running now ends. Its queries are
+  // fetched into the caches by this workgroup, one 128-byte line per lane
+  // (the data lands in an LDS area nobody reads), so that its start does not
+  // wait on a cold read. The fetch is the first slot's last load and that
+  // slot's closing wait leaves it in flight: it has two slots to land. Walks
+  // shorter than kTouchMinTiles skip it (the wait would show in them).
+  const int tok_next = qt_next * TQ + st * 32;
+  const bool touch = SRC == kSrcPacked && AHEAD == 1 && qt_next >= 0 && tok_next < P && v_n >= kTouchMinTiles;
+  auto touch_next = [&]() {
+    if (touch) {
+      const int grp2 = bid_next % n_groups;
+      const int h2 = (grp2 / pl.head_groups) * G + (grp2 % pl.head_groups) * GW + hl;
+      // Lane l: token tok_next + l % 32, line l / 32 of its 2 D-byte row;
+      // the range ends at the end of q (lanes past it read nothing).
+      const long long row = (long long)a.heads * D * 2;
+      const long long left = (long long)(P - tok_next) * row - (long long)h2 * D * 2;
+      const i32x4 rq = raw_rsrc(static_cast<const char*>(a.q) + (tok_next * (long long)a.heads + h2) * D * 2,
+                                (int)(left < (1ll << 30) ? left : (1ll << 30)));
+      constexpr int kLine2 = D * 2 > 128 ? 128 : 0;
+      lds_dma<4>(rq, (uint32_t)(uintptr_t)smem + L::touchOff, (int)((lane & 31) * row + (lane >> 5) * kLine2));
+    }
+  };
+  // The first slot's closing wait: the same, less the query fetch issued
+  // last (loads complete in issue order, so the next slot's wait covers it).
+  auto wait_loads_first = [&](bool extra) {
+    static_assert(AHEAD == 1, "one load left in flight");
+    if (touch) __builtin_amdgcn_s_waitcnt(0xF70 | 1);
+    else wait_loads(extra);
+  };
   const int* visq = pl.vis + (long long)qt * pl.n_kt;
   int v_i = 0;
 
@@ -663,7 +702,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Plan& p
   constexpr int HS = 2 * C;        // matrix steps per half-slot
   constexpr int NSOFT = 14;        // softmax slices per half
   constexpr int NLOAD = KU + 1 + VU;  // load steps at the start of a slot
-  static_assert(NLOAD <= HS, "loads fit the first half-slot");
+  static_assert(NLOAD < HS, "loads (and the query fetch after them) fit the first half-slot");
   u32x4 pw[4];                     // P of the halves of parity 0 and 1 (bf16)
   f32x16 s[2];                     // S^T of the halves of parity 0 and 1
   bf16x8 ring[4];
@@ -892,6 +931,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Plan& p
         if constexpr (i <= KU) k_load(ks, (Tu + AHEAD) % NKB, (Tu + AHEAD) % NPB, AHEAD >= 2 || kn.mode != 0, std::integral_constant<int, i>{});
         else v_load(rv, (Tu + AHEAD - 1) % NKB, std::integral_constant<int, i - KU - 1>{});
       }
+      if constexpr (SRC == kSrcPacked && DO_S && !DO_PREV && h == 0 && i == NLOAD) touch_next();
       if constexpr (DO_S && h == 1 && i == 0) t_gen = gen();
       // Half-slot 0 runs the softmax of tile tp's second half, half-slot 1
       // that of tile t's first half; slice c sits at step 2 + c (HS - 2) / NSOFT,
@@ -910,7 +950,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const Plan& p
     });
     if constexpr (DO_S) {
       // The loads of the previous slot have landed (this slot's may fly on).
-      wait_loads(extra_load);
+      if constexpr (SRC == kSrcPacked && !DO_PREV) wait_loads_first(extra_load);
+      else wait_loads(extra_load);
       barrier();
     }
   };
@@ -1054,6 +1095,23 @@ static void launch_main(const PrefillArgs& a, const Plan& pl, hipStream_t stream
   else prefill_kernel<D, GW, kSrcPacked><<<grid, block, 0, stream>>>(a, pl);
 }
 
+// Compute units of the current device (queried once per device; 0 if the
+// query fails).
+static int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int cus[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream, int waves) {
   const int G = a.heads / a.kv_heads;
   pl.gw = group_width(G);
@@ -1064,6 +1122,7 @@ hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream, i
   pl.n_kt = a.src == kSrcPacked ? (a.p + kBK - 1) / kBK : 0;
   pl.n_qt = (a.p + pl.tq - 1) / pl.tq;
   pl.max_cost = a.src == kSrcPacked ? pl.n_kt : min(kMaxCostBins - 1, a.cap / kBK + 1);
+  pl.resident = 2 * device_cu_count();  // two forward workgroups per CU
   const size_t n_kt_b = align256((size_t)pl.n_kt * sizeof(TileSum));
   const size_t n_qt_max = (size_t)(a.p + 31) / 32;
   const size_t q_b = align256(n_qt_max * sizeof(TileSum));
