@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   for (int j = 0; j < DPL; ++j) Elem<T>::store1(out + lane + 64 * j, den > 0.f ? num[j] / den : 0.f);
 }
 
-hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
+static hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
   const int waves = a.rows * a.heads;
   dim3 grid((waves + 3) / 4);
   if (a.dtype == kDtypeBf16) {
@@ -450,7 +450,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     e = a.paged ? launch_vec_t<T, D, true, false>(a, gc, stream)
                 : launch_vec_t<T, D, false, false>(a, gc, stream);
   if (e != hipSuccess || a.nsplit == 1) return e;  // one split: the output is written
-  return launch_decode_merge(a, stream);
+  return launch_merge(a, stream);
 }
 
 // Bytes of split partials the launch below will write for `a` (0 when each
@@ -498,7 +498,7 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
     hipError_t e = launch_decode_mfma(a, stream);
     if (e != hipSuccess) return e;
     if (a.nsplit == 1) return hipSuccess;  // the split kernel wrote the output
-    return launch_decode_merge(a, stream);
+    return launch_merge(a, stream);
   }
   a.split_len = decode_vec_split_len(a);
   a.nsplit = (a.cap + a.split_len - 1) / a.split_len;

@@ -702,12 +702,7 @@ size_t gqa_step_paged_workspace(int32_t p, int32_t rows, int32_t pages, int32_t 
                                 int32_t kv_heads, int32_t head_dim) {
   if (p < 0 || rows < 0) return 0;
   const size_t a = p > 0 ? align_up_256(gqa_prefill_cached_workspace(p, heads, kv_heads, head_dim)) : 0;
-  size_t b = rows > 0 ? gqa_decode_paged_workspace(rows, pages, heads, kv_heads, head_dim) : 0;
-  // The one-grid path's decode pieces (partials of kStepSplitLen keys).
-  if (p > 0 && rows > 0 && pages > 0 && heads > 0 && head_dim > 0) {
-    const size_t c = gqa::step_decode_bytes(rows, heads, head_dim, pages);
-    if (c > b) b = c;
-  }
+  const size_t b = rows > 0 ? gqa_decode_paged_workspace(rows, pages, heads, kv_heads, head_dim) : 0;
   return a + b;
 }
 
@@ -759,11 +754,10 @@ int gqa_step_paged(int32_t p, int32_t rows, int32_t pages, int32_t heads, int32_
   if (p > 0 && rows > 0) {
     // Decode tokens and chunk tokens in one grid when the decode runs on
     // matrix cores: its workgroups stream the cache beside the prefill tiles.
-    gqa::DecodeArgs d = paged_decode_args(
+    const gqa::DecodeArgs d = paged_decode_args(
         rows, pages, heads, kv_heads, head_dim, dtype, scale, window, sinks,
         static_cast<const char*>(q) + p * row, pool_k, pool_v, num_pages, step_positions, table,
         static_cast<char*>(out) + p * row);
-    d.ws = reinterpret_cast<float*>(ws + pre_ws);
     if (gqa::decode_mfma_supported(d))
       return prefill_cached_impl(p, heads, kv_heads, head_dim, dtype, scale, window, sinks, q,
                                  token_rows, positions, GQA_CACHE_PAGED_TABLE, pool_k, pool_v,

@@ -115,20 +115,14 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t stream);
 constexpr size_t kDecodeScratchBytes = 16u << 20;
 size_t decode_partials_bytes(const DecodeArgs& a);
 hipError_t decode_scratch(float** ptr);
-// The split-K merge of a.nsplit partials per (row, query head) in a.ws.
-hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 bool decode_mfma_supported(const DecodeArgs& a);
 int decode_mfma_split_len(int rows, int kv_heads, int cap);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 
 size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
-// A cached paged prefill and a matrix-core paged decode (bf16, G <= 16, same
-// head dim) in one grid, then the decode's merge. The decode runs as pieces
-// of kStepSplitLen keys after the prefill tiles; d.ws holds their partials,
-// step_decode_bytes(...) bytes.
-constexpr int kStepSplitLen = 512;
-size_t step_decode_bytes(int rows, int heads, int head_dim, int pages);
+// A cached paged prefill and a one-split matrix-core paged decode (bf16,
+// G <= 16, same head dim) in one grid; `d` needs no workspace.
 hipError_t launch_prefill_step(const PrefillArgs& a, DecodeArgs d, hipStream_t stream);
 
 // Backward of the packed prefill (bf16): dq [p, heads, D], dk / dv

@@ -1052,38 +1052,18 @@ __global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) 
 // current one) while the prefill tiles keep the matrix cores busy. Measured
 // alternatives were slower: the decode shares last in the grid, and rows
 // split into 1024- or 2048-key pieces (more workgroups plus a merge pass).
-// One decode piece of the step: keys [split * L, (split + 1) * L) of row r
-// for the query heads of KV head kh (L = d.split_len), written as a partial
-// (max, denominator, unnormalized output) to d.ws for the merge that follows
-// the step grid (which also writes the zeros of rows that attend nothing).
-template <int D, int NW>
-__device__ __forceinline__ void step_decode_piece(const DecodeArgs& d, int r, int kh, int split, char* smem) {
-  int lo, hi;
-  decode_key_range(d.positions[r], d.cap, d.window, lo, hi);
-  if (hi < lo || split < lo / d.split_len || split > hi / d.split_len) return;
-  decode_mfma_body<D, true, NW, false, true>(d, split, kh, r, smem);
-}
-
-// The step grid: the prefill's n_pre workgroups first (its plan and order),
-// then the decode pieces (row, split) x KV head, KV head fastest so that a
-// head's pieces share an XCD with its prefill tiles. Placed last, the short
-// pieces fill the workgroup slots the prefill's last tiles leave idle, and
-// they do not stream the cache through L2 while the prefill's tiles share
-// it (decode workgroups placed first doubled the grid's memory fetch).
 template <int D, int GW>
-__global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) void step_paged_kernel(PrefillArgs a, Plan pl, DecodeArgs d, int n_pre) {
+__global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) void step_paged_kernel(PrefillArgs a, Plan pl, DecodeArgs d, int n_dec) {
   constexpr int NW = prefill_waves<GW>();
   constexpr int kPre = Lds<D, prefill_ahead<GW>() + 1, 4>::total;
   constexpr int kDec = decode_mfma_lds_bytes<D, NW>();
   __shared__ __attribute__((aligned(16))) char smem_raw[kPre > kDec ? kPre : kDec];
   const int bid = blockIdx.x;
-  if (bid >= n_pre) {
-    const int x = bid - n_pre;
-    const int rs = x / d.kv_heads;
-    step_decode_piece<D, NW>(d, rs / d.nsplit, x % d.kv_heads, rs % d.nsplit, smem_raw);
+  if (bid < n_dec) {
+    decode_mfma_body<D, true, NW, false, true>(d, 0, bid % d.kv_heads, bid / d.kv_heads, smem_raw);
     return;
   }
-  prefill_body<D, GW, kSrcPaged>(a, pl, bid, smem_raw);
+  prefill_body<D, GW, kSrcPaged>(a, pl, bid - n_dec, smem_raw);
 }
 
 // ---------------------------------------------------------------------------
@@ -1188,25 +1168,20 @@ hipError_t prefill_summarize(const PrefillArgs& a, const Plan& pl, hipStream_t s
 }
 
 template <int D, int GW>
-static void launch_step(const PrefillArgs& a, const Plan& pl, const DecodeArgs& d, hipStream_t stream) {
+static void launch_step(const PrefillArgs& a, const Plan& pl, const DecodeArgs& d,
+                        hipStream_t stream) {
   const int n_groups = a.kv_heads * pl.head_groups;
-  const int n_pre = pl.n_qt * n_groups;
-  const long long n_dec = (long long)d.rows * d.nsplit * d.kv_heads;
-  const dim3 grid((unsigned)(n_pre + n_dec)), block(64 * prefill_waves<GW>());
-  step_paged_kernel<D, GW><<<grid, block, 0, stream>>>(a, pl, d, n_pre);
-}
-
-size_t step_decode_bytes(int rows, int heads, int head_dim, int pages) {
-  const long long cap = (long long)pages * kPageSize;
-  const long long nsplit = cap > 0 ? (cap + kStepSplitLen - 1) / kStepSplitLen : 1;
-  return (size_t)rows * heads * nsplit * (head_dim + 2) * sizeof(float);
+  const int n_dec = d.rows * d.kv_heads;
+  const dim3 grid(n_dec + pl.n_qt * n_groups), block(64 * prefill_waves<GW>());
+  step_paged_kernel<D, GW><<<grid, block, 0, stream>>>(a, pl, d, n_dec);
 }
 
 hipError_t launch_prefill_step(const PrefillArgs& a, DecodeArgs d, hipStream_t stream) {
-  d.split_len = kStepSplitLen;
-  d.nsplit = d.cap > 0 ? (d.cap + kStepSplitLen - 1) / kStepSplitLen : 1;
+  d.split_len = d.cap;
+  d.nsplit = 1;
+  d.ws = nullptr;
   Plan pl;
-  hipError_t e = prefill_prepare(a, pl, stream);
+  const hipError_t e = prefill_prepare(a, pl, stream);
   if (e != hipSuccess) return e;
   if (a.head_dim == 64) {
     if (pl.gw == 4) launch_step<64, 4>(a, pl, d, stream);
@@ -1217,9 +1192,7 @@ hipError_t launch_prefill_step(const PrefillArgs& a, DecodeArgs d, hipStream_t s
     else if (pl.gw == 2) launch_step<128, 2>(a, pl, d, stream);
     else launch_step<128, 1>(a, pl, d, stream);
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_decode_merge(d, stream);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {

@@ -375,11 +375,9 @@ size_t gqa_step_packed_workspace(int32_t batch, int32_t p, int32_t heads, int32_
  *   [num_pages, kv_heads, 64, D]; table [rows, pages]; step_positions
  *   [rows]. bf16 only. workspace: gqa_step_paged_workspace(...) bytes,
  *   256-byte aligned.
- * With up to 16 query heads per KV head the chunk and the decode tokens run
- * as one grid: the chunk's tiles first, then the decode as pieces of 512
- * keys that fill the slots the chunk's last tiles leave idle, followed by a
- * small merge of the pieces (partials in the workspace); otherwise the
- * decode runs first, then the chunk.
+ * With up to 16 query heads per KV head the decode tokens and the chunk run
+ * as one grid (decode workgroups first), so the decode's cache reads overlap
+ * the chunk's matrix work; otherwise the decode runs first, then the chunk.
  */
 int gqa_step_paged(int32_t p, int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
                    int32_t head_dim, int32_t dtype, float scale, int32_t window, const void* sinks,
