@@ -116,26 +116,53 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(PrefillArgs a, Plan p
   }
   int first = pl.n_kt, last = -1, cnt = 0, nm = 0;
   int* vis = pl.vis + (size_t)qt * pl.n_kt;
+  // Whether key tile g * 64 + lane can meet this query tile, is fully
+  // allowed, and lies in its one segment.
+  auto classify = [&](int g, const TileSum& k, bool& meet, bool& full, bool& one) {
+    const int kt = g * 64 + lane;
+    meet = full = one = false;
+    if (kt < pl.n_kt) {
+      meet = tiles_meet(q, k, a.window);
+      full = meet && tiles_full(q, k, kt, a.p, a.window);
+      one = meet && tiles_oneseg(q, k, kt, a.p);
+    }
+  };
+  // The first kScanKept groups of 64 key tiles: every summary is loaded at
+  // once (one memory round trip instead of one per group and pass), and the
+  // classification is kept as 3 bits per group for the second pass.
+  constexpr int kScanKept = 8;
+  TileSum kc[kScanKept];
+#pragma unroll
+  for (int g = 0; g < kScanKept; ++g)
+    if (g < pl.n_kg) kc[g] = pl.ksum[min(g * 64 + lane, pl.n_kt - 1)];
+  uint32_t kept = 0;
   // The visit list holds the fully allowed tiles first: count them first.
   int nf = 0;
-  for (int g = 0; g < pl.n_kg; ++g) {
-    const int kt = g * 64 + lane;
-    bool full = false;
-    if (kt < pl.n_kt) {
-      const TileSum k = pl.ksum[kt];
-      full = tiles_meet(q, k, a.window) && tiles_full(q, k, kt, a.p, a.window);
+#pragma unroll
+  for (int g = 0; g < kScanKept; ++g) {
+    if (g < pl.n_kg) {
+      bool meet, full, one;
+      classify(g, kc[g], meet, full, one);
+      kept |= ((meet ? 1u : 0u) | (full ? 2u : 0u) | (one ? 4u : 0u)) << (3 * g);
+      nf += __builtin_popcountll(__builtin_amdgcn_ballot_w64(full));
     }
+  }
+  for (int g = kScanKept; g < pl.n_kg; ++g) {
+    bool meet, full, one;
+    classify(g, pl.ksum[min(g * 64 + lane, pl.n_kt - 1)], meet, full, one);
     nf += __builtin_popcountll(__builtin_amdgcn_ballot_w64(full));
   }
   int rank_f = 0;
   for (int g = 0; g < pl.n_kg; ++g) {
     const int kt = g * 64 + lane;
-    bool meet = false, full = false, one = false;
-    if (kt < pl.n_kt) {
-      const TileSum k = pl.ksum[kt];
-      meet = tiles_meet(q, k, a.window);
-      full = meet && tiles_full(q, k, kt, a.p, a.window);
-      one = meet && tiles_oneseg(q, k, kt, a.p);
+    bool meet, full, one;
+    if (g < kScanKept) {
+      const uint32_t b = kept >> (3 * g);
+      meet = b & 1u;
+      full = b & 2u;
+      one = b & 4u;
+    } else {
+      classify(g, pl.ksum[min(kt, pl.n_kt - 1)], meet, full, one);
     }
     if (meet) {
       first = min(first, kt);
@@ -183,10 +210,15 @@ constexpr int kTouchMinTiles = 8;  // see touch_next in prefill_body
 __global__ __launch_bounds__(kPrepThreads) void prefill_order_kernel(Plan pl) {
   __shared__ int start[kMaxCostBins + 1];
   __shared__ int part[kPrepThreads];
+  __shared__ int s_order[kMaxCostBins];  // the order again, for the records (n_qt <= kMaxCostBins)
   const int tid = threadIdx.x;
+  const bool keep = pl.n_qt <= kMaxCostBins;
   const int nb = pl.max_cost + 1;  // costs 0 .. max_cost
   if (nb > kMaxCostBins) {
-    for (int i = tid; i < pl.n_qt; i += kPrepThreads) pl.order[i] = i;
+    for (int i = tid; i < pl.n_qt; i += kPrepThreads) {
+      pl.order[i] = i;
+      if (keep) s_order[i] = i;
+    }
   } else {
   for (int i = tid; i < nb; i += kPrepThreads) start[i] = 0;
   __syncthreads();
@@ -214,26 +246,37 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_order_kernel(Plan pl) {
     run += c;
   }
   __syncthreads();
-  for (int i = tid; i < pl.n_qt; i += kPrepThreads)
-    pl.order[atomicAdd(&start[pl.max_cost - pl.cost[i]], 1)] = i;
+  for (int i = tid; i < pl.n_qt; i += kPrepThreads) {
+    const int at = atomicAdd(&start[pl.max_cost - pl.cost[i]], 1);
+    pl.order[at] = i;
+    if (keep) s_order[at] = i;
+  }
   }
   if (pl.rec == nullptr) return;
   // Start records: the walk's first scalar loads, in one place per slot.
   __syncthreads();
+  static_assert(kRecInts == 16 && kRecVis == 12, "record layout");
   for (int i = tid; i < pl.n_qt; i += kPrepThreads) {
-    const int qt = pl.order[i];
-    int* rec = pl.rec + (size_t)i * kRecInts;
-    rec[0] = qt;
+    const int qt = keep ? s_order[i] : pl.order[i];
+    int4* rec = reinterpret_cast<int4*>(pl.rec + (size_t)i * kRecInts);
     if (pl.vis != nullptr) {
       // Packed keys: the list's counts and its first entries in walk order.
+      // All loads are issued before any is used (indices clamped into the
+      // list, entries past its length replaced by zeros).
       const int nf = pl.nfull[qt], n = pl.cost[qt];
       const int* vis = pl.vis + (size_t)qt * pl.n_kt;
-      rec[1] = nf;
-      rec[2] = n - nf;
-      rec[3] = 0;
-      for (int w = 0; w < kRecVis; ++w) rec[4 + w] = w < n ? vis[w] : 0;
+      int e[kRecVis];
+#pragma unroll
+      for (int w = 0; w < kRecVis; ++w) e[w] = vis[min(w, pl.n_kt - 1)];
+#pragma unroll
+      for (int w = 0; w < kRecVis; ++w) e[w] = w < n ? e[w] : 0;
+      rec[0] = make_int4(qt, nf, n - nf, 0);
+      rec[1] = make_int4(e[0], e[1], e[2], e[3]);
+      rec[2] = make_int4(e[4], e[5], e[6], e[7]);
+      rec[3] = make_int4(e[8], e[9], e[10], e[11]);
     } else {
-      for (int w = 1; w < kRecInts; ++w) rec[w] = 0;
+      rec[0] = make_int4(qt, 0, 0, 0);
+      rec[1] = rec[2] = rec[3] = make_int4(0, 0, 0, 0);
     }
   }
 }
