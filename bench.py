@@ -582,6 +582,39 @@ def main():
                       for p_ in (10, 50, 90)] for i, n in enumerate(names)}
     step_ms = float(np.mean([ev[0].elapsed_time(ev[5]) for ev in evs]))
 
+    # Measured ceilings beside the published peaks: one streaming read of the
+    # decode's key pool (1.18 GB) by the library's diagnostic read kernel, and
+    # a large bf16 GEMM through torch.matmul (hipBLASLt); medians, measured
+    # right after the timed steps.
+    xor_word = torch.zeros(gqa.GQA_DIAG_READ_BLOCKS, dtype=torch.int32, device=dev)
+    pool_bytes = pool_k.numel() * pool_k.element_size()
+
+    def timed_median(fn, n=30):
+        for _ in range(5):
+            fn()
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(n)]
+        for e0, e1 in pairs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in pairs])) * 1e-3
+
+    rd_s = timed_median(lambda: gqa.gqa_diag_stream_read(pool_k, pool_bytes, xor_word))
+    mm_n = 8192
+    ma = W.device_normal((mm_n, mm_n), SEED_QKV, "q", bf16)
+    mb = W.device_normal((mm_n, mm_n), SEED_QKV, "k", bf16)
+    mmb_s = timed_median(lambda: ma @ mb, 10)
+    ceilings = {"stream_read_gbs": pool_bytes / rd_s / 1e9, "stream_read_bytes": pool_bytes,
+                "stream_read_us": rd_s * 1e6,
+                "bf16_matmul_tflops": 2 * mm_n ** 3 / mmb_s / 1e12, "bf16_matmul_shape": [mm_n] * 3,
+                "bf16_matmul_us": mmb_s * 1e6,
+                "note": "streaming read: gqa_diag_stream_read (nontemporal 16-byte loads, grid-stride) "
+                        "over the paged decode's key pool; matmul: torch.matmul of two seeded N(0,1) "
+                        "bf16 matrices"}
+    del ma, mb, xor_word
+
     def prefill_only():
         gqa.gqa_prefill_packed(P, H, KVH, D, gqa.GQA_BF16, 0.0, 0, None, pq, pk, pv, p_pos, p_seg,
                                p_out, p_ws, pws_n)
@@ -714,6 +747,7 @@ def main():
                 "hipblaslt_gemm_only_us": mm_s * 1e6,
                 "workload": f"{P} tokens x hidden {hid} -> (32 + 8 + 8) x 128, rope, contiguous cache"}
     del gx, gwq, gwk, gwv, gwcat, g_q
+
 
     # Training pair on the packed prefill batch: the forward with log-sum-exp,
     # then the backward (dq, dk, dv) against a seeded dout. Algorithmic work
@@ -854,6 +888,9 @@ def main():
         "prefill_tflops": prefill_tflops,
         "decode_frac_of_hbm_peak": decode_gbs / HBM_PEAK_GBS,
         "prefill_frac_of_mfma_peak": prefill_tflops / MFMA_BF16_PEAK_TFLOPS,
+        "measured_ceilings": ceilings,
+        "decode_frac_of_stream_read": decode_gbs / ceilings["stream_read_gbs"],
+        "prefill_frac_of_bf16_matmul": prefill_tflops / ceilings["bf16_matmul_tflops"],
         "roofline": roof,
         "rooflines": {"decode_paged": dec_roof, "prefill_packed": pre_roof},
         "next_rows": {"prefill_cached_paged": chunk_roof, "step_paged": step_roof,

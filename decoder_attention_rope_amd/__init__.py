@@ -27,13 +27,15 @@ __all__ = [
     "gqa_decode_rows", "gqa_decode_rows_workspace", "gqa_decode_paged",
     "gqa_decode_paged_workspace", "gqa_decode_paged_noalloc", "GQA_DECODE_SCRATCH_BYTES",
     "gqa_status_string", "gqa_status_str", "gqa_workspace_bytes",
-    "gqa_set_dry_run", "gqa_set_checked", "gqa_abi_version",
+    "gqa_set_dry_run", "gqa_set_checked", "gqa_abi_version", "gqa_diag_stream_read",
+    "GQA_DIAG_READ_BLOCKS",
     "dtype_code",
 ]
 
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = 0, 1, 2, 3, 4
 GQA_ERR_INDEX = 5
 GQA_DECODE_SCRATCH_BYTES = 16 << 20
+GQA_DIAG_READ_BLOCKS = 2048
 (GQA_OP_PREFILL_PACKED, GQA_OP_PREFILL_CACHED, GQA_OP_PREFILL_BACKWARD, GQA_OP_DECODE_ROWS,
  GQA_OP_DECODE_PAGED, GQA_OP_STEP_PACKED, GQA_OP_STEP_PAGED) = range(7)
 GQA_BF16, GQA_F32 = 0, 1
@@ -108,6 +110,7 @@ _workspace_bytes = _sig("gqa_workspace_bytes", _sz, [_i32] * 7)
 _set_dry_run = _sig("gqa_set_dry_run", _i32, [_i32])
 _set_checked = _sig("gqa_set_checked", _i32, [_i32])
 _abi_version = _sig("gqa_abi_version", _i32, [])
+_diag_stream_read = _sig("gqa_diag_stream_read", ctypes.c_int, [_vp, _sz, _vp, _vp])
 
 
 class GQAError(RuntimeError):
@@ -175,6 +178,13 @@ def gqa_set_checked(on):
 
 def gqa_abi_version():
     return _abi_version()
+
+
+def gqa_diag_stream_read(buffer, nbytes, out, stream=None):
+    """Diagnostic outside the attention path: one streaming read of nbytes at
+    buffer; out holds GQA_DIAG_READ_BLOCKS 32-bit words, workgroup b's XOR of
+    the words it read in out[b]."""
+    _check(_diag_stream_read(_ptr(buffer), nbytes, _ptr(out), _stream(stream)), "gqa_diag_stream_read")
 
 
 def gqa_rope_table(head_dim, max_pos, theta, dtype, table, stream=None):

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libgqa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["gqa_api.cpp", "rope.hip", "decode.hip", "decode_mfma.hip", "prefill.hip", "prefill_bwd.hip", "qkv.hip",
-           "check.hip"]
+           "check.hip", "diag.hip"]
 
 COMMON_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -423,6 +423,21 @@ int32_t gqa_set_checked(int32_t on);
 /* ABI version of this header. */
 int32_t gqa_abi_version(void);
 
+/*
+ * gqa_diag_stream_read -- a diagnostic outside the attention path: reads
+ * `bytes` of device memory at `buffer` once, in a streaming pattern
+ * (nontemporal 16-byte loads, a grid-stride loop over at most
+ * GQA_DIAG_READ_BLOCKS workgroups). Workgroup b stores the XOR of the 32-bit
+ * words it read to out[b] (device memory, GQA_DIAG_READ_BLOCKS words; words
+ * of workgroups not launched are left as they are, so a caller that zeroes
+ * `out` first gets the XOR of the whole buffer by XOR-ing the words).
+ * bench.py times it as the measured HBM read ceiling the decode is compared
+ * with. buffer 16-byte aligned, bytes a multiple of 16 (else
+ * GQA_ERR_INVALID_ARG); enqueued on `stream`, nothing allocated.
+ */
+#define GQA_DIAG_READ_BLOCKS 2048
+int gqa_diag_stream_read(const void* buffer, size_t bytes, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

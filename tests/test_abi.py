@@ -324,3 +324,17 @@ def test_checked_mode_from_environment():
                              text=True, timeout=120)
         assert out.returncode == 0, out.stderr
         assert out.stdout.strip() == want, out.stdout
+
+
+def test_diag_stream_read_rejects_bad_buffers(g):
+    """Null pointers and sizes or addresses that are not 16-byte multiples are
+    rejected before anything is enqueued."""
+    cdll = ctypes.CDLL(g.library_path)
+    f = cdll.gqa_diag_stream_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, 16, 64, None) == g.GQA_ERR_INVALID_ARG
+    assert f(64, 16, None, None) == g.GQA_ERR_INVALID_ARG
+    assert f(64, 24, 64, None) == g.GQA_ERR_INVALID_ARG
+    assert f(72, 16, 64, None) == g.GQA_ERR_INVALID_ARG
+    assert f(64, 0, 64, None) == g.GQA_OK
