@@ -212,72 +212,112 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_order_kernel(Plan pl) {
   __shared__ int part[kPrepThreads];
   __shared__ int s_order[kMaxCostBins];  // the order again, for the records (n_qt <= kMaxCostBins)
   const int tid = threadIdx.x;
-  const bool keep = pl.n_qt <= kMaxCostBins;
   const int nb = pl.max_cost + 1;  // costs 0 .. max_cost
+  static_assert(kRecInts == 16 && kRecVis == 12, "record layout");
+  // Exclusive scan over the bins (bin b = cost max_cost - b, so costly tiles
+  // first): each thread sums a run of bins, a block scan of the run sums,
+  // then the runs are rewritten as exclusive offsets.
+  auto scan_bins = [&]() {
+    const int per = (nb + kPrepThreads - 1) / kPrepThreads;
+    const int b0 = tid * per;
+    int sum = 0;
+    for (int b = b0; b < min(nb, b0 + per); ++b) sum += start[b];
+    part[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < kPrepThreads; off <<= 1) {
+      const int v = tid >= off ? part[tid - off] : 0;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
+    }
+    int run = part[tid] - sum;
+    for (int b = b0; b < min(nb, b0 + per); ++b) {
+      const int c = start[b];
+      start[b] = run;
+      run += c;
+    }
+    __syncthreads();
+  };
+  // Start record of query tile qt at slot i: its index, for packed keys the
+  // numbers of fully allowed and masked tiles it visits and its first
+  // kRecVis visit-list entries (zeros past the list).
+  auto write_rec = [&](int i, int qt, int nf, int n, const int* e) {
+    int4* rec = reinterpret_cast<int4*>(pl.rec + (size_t)i * kRecInts);
+    if (pl.vis != nullptr) {
+      int f[kRecVis];
+#pragma unroll
+      for (int w = 0; w < kRecVis; ++w) f[w] = w < n ? e[w] : 0;
+      rec[0] = make_int4(qt, nf, n - nf, 0);
+      rec[1] = make_int4(f[0], f[1], f[2], f[3]);
+      rec[2] = make_int4(f[4], f[5], f[6], f[7]);
+      rec[3] = make_int4(f[8], f[9], f[10], f[11]);
+    } else {
+      rec[0] = make_int4(qt, 0, 0, 0);
+      rec[1] = rec[2] = rec[3] = make_int4(0, 0, 0, 0);
+    }
+  };
+  // The list entries of query tile qt a record needs, all loads issued before
+  // any is used (indices clamped into the list).
+  auto load_vis = [&](int qt, int* e) {
+    const int* vis = pl.vis + (size_t)qt * pl.n_kt;
+#pragma unroll
+    for (int w = 0; w < kRecVis; ++w) e[w] = vis[min(w, pl.n_kt - 1)];
+  };
+
+  if (pl.n_qt <= kPrepThreads && nb <= kMaxCostBins) {
+    // One query tile per thread: its cost (and what its record needs) is
+    // loaded once, before the sort, and the thread writes its tile's order
+    // entry and record at the tile's sorted place; nothing waits on memory
+    // after the sort.
+    const bool mine = tid < pl.n_qt;
+    const bool recs = mine && pl.rec != nullptr && pl.vis != nullptr;
+    const int c = mine ? pl.cost[tid] : 0;
+    const int nf = recs ? pl.nfull[tid] : 0;
+    int e[kRecVis];
+#pragma unroll
+    for (int w = 0; w < kRecVis; ++w) e[w] = 0;
+    if (recs) load_vis(tid, e);
+    for (int i = tid; i < nb; i += kPrepThreads) start[i] = 0;
+    __syncthreads();
+    if (mine) atomicAdd(&start[pl.max_cost - c], 1);
+    __syncthreads();
+    scan_bins();
+    if (mine) {
+      const int at = atomicAdd(&start[pl.max_cost - c], 1);
+      pl.order[at] = tid;
+      if (pl.rec != nullptr) write_rec(at, tid, nf, c, e);
+    }
+    return;
+  }
+
+  const bool keep = pl.n_qt <= kMaxCostBins;
   if (nb > kMaxCostBins) {
     for (int i = tid; i < pl.n_qt; i += kPrepThreads) {
       pl.order[i] = i;
       if (keep) s_order[i] = i;
     }
   } else {
-  for (int i = tid; i < nb; i += kPrepThreads) start[i] = 0;
-  __syncthreads();
-  for (int i = tid; i < pl.n_qt; i += kPrepThreads) atomicAdd(&start[pl.max_cost - pl.cost[i]], 1);
-  __syncthreads();
-  // Exclusive scan over bins (bin b = cost max_cost - b, so costly tiles first):
-  // each thread sums a run of bins, a block scan of the run sums, then the
-  // runs are rewritten as exclusive offsets.
-  const int per = (nb + kPrepThreads - 1) / kPrepThreads;
-  const int b0 = tid * per;
-  int sum = 0;
-  for (int b = b0; b < min(nb, b0 + per); ++b) sum += start[b];
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < kPrepThreads; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
+    for (int i = tid; i < nb; i += kPrepThreads) start[i] = 0;
     __syncthreads();
-    part[tid] += v;
+    for (int i = tid; i < pl.n_qt; i += kPrepThreads) atomicAdd(&start[pl.max_cost - pl.cost[i]], 1);
     __syncthreads();
-  }
-  int run = part[tid] - sum;
-  for (int b = b0; b < min(nb, b0 + per); ++b) {
-    const int c = start[b];
-    start[b] = run;
-    run += c;
-  }
-  __syncthreads();
-  for (int i = tid; i < pl.n_qt; i += kPrepThreads) {
-    const int at = atomicAdd(&start[pl.max_cost - pl.cost[i]], 1);
-    pl.order[at] = i;
-    if (keep) s_order[at] = i;
-  }
+    scan_bins();
+    for (int i = tid; i < pl.n_qt; i += kPrepThreads) {
+      const int at = atomicAdd(&start[pl.max_cost - pl.cost[i]], 1);
+      pl.order[at] = i;
+      if (keep) s_order[at] = i;
+    }
   }
   if (pl.rec == nullptr) return;
   // Start records: the walk's first scalar loads, in one place per slot.
   __syncthreads();
-  static_assert(kRecInts == 16 && kRecVis == 12, "record layout");
   for (int i = tid; i < pl.n_qt; i += kPrepThreads) {
     const int qt = keep ? s_order[i] : pl.order[i];
-    int4* rec = reinterpret_cast<int4*>(pl.rec + (size_t)i * kRecInts);
-    if (pl.vis != nullptr) {
-      // Packed keys: the list's counts and its first entries in walk order.
-      // All loads are issued before any is used (indices clamped into the
-      // list, entries past its length replaced by zeros).
-      const int nf = pl.nfull[qt], n = pl.cost[qt];
-      const int* vis = pl.vis + (size_t)qt * pl.n_kt;
-      int e[kRecVis];
-#pragma unroll
-      for (int w = 0; w < kRecVis; ++w) e[w] = vis[min(w, pl.n_kt - 1)];
-#pragma unroll
-      for (int w = 0; w < kRecVis; ++w) e[w] = w < n ? e[w] : 0;
-      rec[0] = make_int4(qt, nf, n - nf, 0);
-      rec[1] = make_int4(e[0], e[1], e[2], e[3]);
-      rec[2] = make_int4(e[4], e[5], e[6], e[7]);
-      rec[3] = make_int4(e[8], e[9], e[10], e[11]);
-    } else {
-      rec[0] = make_int4(qt, 0, 0, 0);
-      rec[1] = rec[2] = rec[3] = make_int4(0, 0, 0, 0);
-    }
+    int e[kRecVis];
+    const bool packed = pl.vis != nullptr;
+    const int nf = packed ? pl.nfull[qt] : 0, n = packed ? pl.cost[qt] : 0;
+    if (packed) load_vis(qt, e);
+    write_rec(i, qt, nf, n, e);
   }
 }
 
