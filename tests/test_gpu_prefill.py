@@ -147,6 +147,26 @@ def test_prefill_llama8b_packed_full_sampled():
     assert_close(f64(out)[sel], ref, "bf16", f"llama8b packed prefill, {len(sel)} sampled queries")
 
 
+def test_prefill_long_batch_sampled():
+    """40,960 packed tokens (1,280 query tiles, 640 key tiles): the prepared
+    walk's paths for more query tiles than one workgroup has threads and for
+    more than 8 groups of 64 key tiles."""
+    heads, kvh, d, p = 8, 2, 64, 40960
+    print(f"[case] prefill long batch P={p}", flush=True)
+    g = W.streams(4096)
+    lengths, pos, seg = W.segment_layout(p, 64, 4096, g["index"])
+    dv, hv, (sk, sk64), g2 = make_inputs(4096, p, heads, kvh, d)
+    o = oracle.default()
+    starts = np.concatenate([[0], np.cumsum(lengths)[:-1]])
+    ends = np.cumsum(lengths) - 1
+    sel = np.unique(np.concatenate([starts, ends, W.sample_indices(p, 160, g2["extra"]),
+                                    np.arange(0, p, 211), [p - 1]])).astype(np.int32)
+    for window, sinks in ((0, None), (700, sk)):
+        out = run_prefill(*dv, pos, seg, heads, kvh, d, window, sinks)
+        ref = o.packed(*hv, pos, seg, window=window, sinks=None if sinks is None else sk64, sel=sel)
+        assert_close(f64(out)[sel], ref, "bf16", f"long packed batch W={window}, {len(sel)} sampled queries")
+
+
 @pytest.mark.parametrize("window", [128, 0])
 def test_prefill_gpt_oss_sampled(window):
     wl = W.GPT_OSS_SINK
