@@ -356,8 +356,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
 // LDS. Its consumer (w - 4, on the same SIMD) takes them one step later and
 // accumulates dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
 // transposed from that step's stage. Pairs are visited two at a time, both
-// staged in LDS (a ring of three stages).
+// staged in LDS (a ring of three stages). The consumers also stage the
+// pairs (each one its parity's pair and half of its tiles) and classify
+// them, so a producer's step holds only its matrix and softmax work.
 // ---------------------------------------------------------------------------
+// How a producer forms P for a staged pair: no element allowed (P = dS = 0),
+// every element allowed, one segment and non-negative positions (one unsigned
+// compare of the position difference per element), or the full mask.
+enum : int { kPairSkip = 0, kPairFull = 1, kPairOneSeg = 2, kPairMasked = 3 };
+
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, const TileSum* ksum,
                                                          const int2* krange, const int* korder,
@@ -365,6 +372,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
   constexpr int KS = D / 16, MD = D / 32;
   using SQT = ST<D>;
   constexpr int qTile = SQT::bytes(32);            // one Q or dout tile (32 queries, swizzled)
+  constexpr int NLD = SQT::loads(32) / 2;          // 16-byte loads of a tile per consumer half
   // Q, dout, then lse, delta, positions, segments (256 bytes each: a 64-lane
   // load writes its 32 values and 32 zeros).
   constexpr int pairBytes = 2 * qTile + 4 * 256;
@@ -372,11 +380,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
   // After three stages, P and dS of the producers: two buffers of 4 slots
   // (key half, pair parity) of 4 x 64 lanes x 16 bytes (P halves, then dS
   // halves; piece c of lane l at 1024 c + 16 l, so each access covers the
-  // banks once).
+  // banks once); then one code word per (stage, slot).
   constexpr int pOff = 3 * stageBytes;
   constexpr int pBufBytes = 4 * 64 * 64;
+  constexpr int codeOff = pOff + 2 * pBufBytes;
   constexpr int combineBytes = 2 * 2 * MD * 16 * 64 * 4;
-  constexpr int ldsBytes = pOff + 2 * pBufBytes > combineBytes ? pOff + 2 * pBufBytes : combineBytes;
+  constexpr int ldsBytes = codeOff + 32 > combineBytes ? codeOff + 32 : combineBytes;
   __shared__ __attribute__((aligned(16))) char smem_raw[ldsBytes];
   LdsByte* smem = (LdsByte*)smem_raw;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
@@ -397,47 +406,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
   const int2 rng = make_int2(__builtin_amdgcn_readfirstlane(krange[kt].x), __builtin_amdgcn_readfirstlane(krange[kt].y));
   const int n_pairs = rng.y >= rng.x ? (rng.y - rng.x + 1) * G : 0;
   const int n_steps = (n_pairs + 1) / 2;
-  const int row_bytes = a.heads * D * 2;
   // This lane's first piece of P and dS in slot (kb, hp) of buffer pbuf.
   auto p_slot = [&](int pbuf) { return pOff + pbuf * pBufBytes + (2 * hp + kb) * 4096 + lane * 16; };
-
-  // Stage the pair `pair` (query tile, head) into slot `slot` of buffer b:
-  // Q and dout rows, lse and delta of the head, positions and segments.
-  auto load_pair = [&](int pair, int slot, int b) {
-    const int qt = rng.x + pair / G, h = kh * G + pair % G;
-    const int n_rows = min(32, P - qt * 32);
-    const long long e0 = ((long long)qt * 32 * a.heads + h) * D;
-    const int nrec = (n_rows - 1) * row_bytes + 2 * D;
-    const i32x4 rq = raw_rsrc(static_cast<const uint16_t*>(a.q) + e0, nrec);
-    const i32x4 rg = raw_rsrc(static_cast<const uint16_t*>(a.dout) + e0, nrec);
-    const uint32_t base = lds0 + b * stageBytes + slot * pairBytes;
-    for (int i = wave; i < SQT::loads(32); i += 8) {
-      const int off = swz_off<D>(64 * i + lane, n_rows, row_bytes);
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(base + 1024 * i);
-      lds_dma<16>(rq, dst, off);
-      lds_dma<16>(rg, dst + qTile, off);
-    }
-    // Waves 4..7: lse, delta (stride heads floats), positions, segments.
-    const int mw = wave - 4;
-    const uint32_t mdst = __builtin_amdgcn_readfirstlane(base + 2 * qTile + 256 * (mw & 3));
-    if (mw == 0 || mw == 1) {
-      const float* src = mw == 0 ? lse2 : delta;
-      const i32x4 r = raw_rsrc(src + (long long)qt * 32 * a.heads + h, 4 * ((n_rows - 1) * a.heads + 1));
-      lds_dma<4>(r, mdst, lane < 32 ? lane * a.heads * 4 : 0x40000000);
-    } else if (mw == 2 || mw == 3) {
-      const int32_t* src = mw == 2 ? a.positions : a.segments;
-      const i32x4 r = raw_rsrc(src + (long long)qt * 32, 4 * n_rows);
-      lds_dma<4>(r, mdst, lane < 32 ? lane * 4 : 0x40000000);
-    }
-  };
+  auto code_at = [&](int b, int slot) { return codeOff + 4 * (2 * b + slot); };
 
   // Producer: this lane's key as the B operand of S and dP (K^T and V^T
   // columns, dimensions 16 ks + 8 hf ..).
   auto produce = [&]() {
     const int pos_k = a.positions[key_ld], seg_k = a.segments[key_ld];
     const uint32_t wlast = a.window > 0 ? (uint32_t)a.window - 1u : 0xffffffffu;
+    // One-segment pairs: positions are non-negative, so an unsigned
+    // difference at most this bound means order and window both hold.
+    const uint32_t wl_one = a.window > 0 ? (uint32_t)a.window - 1u : 0x7fffffffu;
     const float scale_log2 = a.scale * kLog2eB;
-    const TileSum ks_sum = ld_const(ksum, kt);
     const uint16_t* kg = static_cast<const uint16_t*>(a.k) + ((long long)key_ld * a.kv_heads + kh) * D;
     const uint16_t* vg = static_cast<const uint16_t*>(a.v) + ((long long)key_ld * a.kv_heads + kh) * D;
     u32x4 kf[KS], vf[KS];
@@ -451,26 +432,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
     const int q_row = qn * SQT::kStride;
     const int q_xc = hf ^ SQT::swz(qn);
 
-    if (n_steps > 0) {
-      load_pair(0, 0, 0);
-      load_pair(min(1, n_pairs - 1), 1, 0);
-      wait_all_loads();
-      wg_barrier();
-    }
+    if (n_steps > 0) wg_barrier();  // the first stage
     int b = 0;  // stage of this step
     for (int step = 0; step < n_steps; ++step) {
       const int bn = b == 2 ? 0 : b + 1;
-      if (step + 1 < n_steps) {
-        load_pair(2 * step + 2, 0, bn);
-        load_pair(min(2 * step + 3, n_pairs - 1), 1, bn);
-      }
-      const int pair = 2 * step + hp;
-      const int qt = rng.x + min(pair, n_pairs - 1) / G;
-      const TileSum q_sum = ld_const(qp.qsum, qt);
-      // A pair that cannot meet the key tile (or lies past the last pair)
-      // contributes zeros.
-      const bool meet = pair < n_pairs && tiles_meet(q_sum, ks_sum, a.window);
-      const bool full = meet && tiles_full(q_sum, ks_sum, kt, P, a.window) && (qt + 1) * 32 <= P;
+      const int code = __builtin_amdgcn_readfirstlane(lds_ld<int>(smem + code_at(b, hp)));
       const LdsByte* pbase = smem + b * stageBytes + hp * pairBytes;
       const LdsByte* qb = pbase;
       const LdsByte* gb = pbase + qTile;
@@ -498,7 +464,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
       // Register r of this lane holds query iq = 16 (r / 8) + 8 hf + r % 8
       // of the tile and this lane's key; lse and delta of those queries
       // come as four 16-byte reads each.
-      const int n_q = P - qt * 32;
       float lse_r[16], dl_r[16];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -510,19 +475,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
           dl_r[4 * c + e] = __uint_as_float(dw[e]);
         }
       }
-      // P and dS in bf16, two 16-query halves each, to LDS. One copy of this
-      // code for fully-allowed pairs and one for masked pairs (their query
-      // positions and segments read 16 bytes at a time), so the branch on
-      // `full` is taken once per pair rather than once per element.
-      const int po = p_slot(step & 1);
-      auto p_ds = [&](auto full_c) {
-        constexpr bool FULL = decltype(full_c)::value;
+      // P and dS in bf16, two 16-query halves each, to LDS; one copy of this
+      // code per pair class, chosen once per pair. Rows past the end of a
+      // partial query tile were staged as zeros (q, dout, lse, delta), so
+      // their P is finite and their dout and q columns add nothing; keys
+      // past the end only feed their own (unwritten) columns of dK and dV.
+      u32x4 pp[2] = {}, pds[2] = {};
+      auto p_ds = [&](auto mode_c) {
+        constexpr int MODE = decltype(mode_c)::value;
         int qpos_r[16], qseg_r[16];
-        if constexpr (!FULL) {
+        if constexpr (MODE != kPairFull) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int iq0 = 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
-            const u32x4 pw = lds_ld<u32x4>(misc + 512 + iq0 * 4), sw = lds_ld<u32x4>(misc + 768 + iq0 * 4);
+            const u32x4 pw = lds_ld<u32x4>(misc + 512 + iq0 * 4);
+            u32x4 sw = {};
+            if constexpr (MODE == kPairMasked) sw = lds_ld<u32x4>(misc + 768 + iq0 * 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               qpos_r[4 * c + e] = (int)pw[e];
@@ -530,33 +498,55 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
             }
           }
         }
-        u32x4 pp[2], pds[2];
+        // In phases of 16 independent operations each (fenced, so the
+        // compiler does not fold them back into per-element chains that
+        // wait out each result's latency): P from S, whose MFMAs were issued
+        // first, then dS, which needs dP.
+        float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float p2[2], d2[2];
+        for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], scale_log2, -lse_r[r]);  // lse * log2(e)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int iq = 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
-            const float l2 = lse_r[r + e];  // lse * log2(e), staged as such
-            bool ok = k_valid & meet;
-            if constexpr (!FULL)
-              ok = ok & (qseg_r[r + e] == seg_k) & (pos_k <= qpos_r[r + e]) &
-                   ((uint32_t)qpos_r[r + e] - (uint32_t)pos_k <= wlast) & (iq < n_q);
-            const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -l2)) : 0.f;
-            p2[e] = p;
-            d2[e] = p * (dp[r + e] - dl_r[r + e]);  // p is 0 where masked; dP, delta finite
+        for (int r = 0; r < 16; ++r) x[r] = fast_exp2(x[r]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MODE == kPairOneSeg) {
+          // Allowed iff 0 <= d <= wl_one for d = qpos - pos_k (both
+          // non-negative, so neither d nor wl_one - d overflows when d >= 0):
+          // the sign of d | (wl_one - d) is the mask.
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int d = qpos_r[r] - pos_k;
+            const int m = (d | ((int)wl_one - d)) >> 31;
+            x[r] = __int_as_float(__float_as_int(x[r]) & ~m);
           }
-          pp[r >> 3][(r & 7) >> 1] = pack_bf16x2(p2[0], p2[1]);
-          pds[r >> 3][(r & 7) >> 1] = pack_bf16x2(d2[0], d2[1]);
+        } else if constexpr (MODE == kPairMasked) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            x[r] = (qseg_r[r] == seg_k) & (pos_k <= qpos_r[r]) & ((uint32_t)qpos_r[r] - (uint32_t)pos_k <= wlast)
+                       ? x[r]
+                       : 0.f;
         }
-        lds_st(smem + po, pp[0]);
-        lds_st(smem + po + 1024, pp[1]);
-        lds_st(smem + po + 2048, pds[0]);
-        lds_st(smem + po + 3072, pds[1]);
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) pp[r >> 3][(r & 7) >> 1] = pack_bf16x2(x[r], x[r + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] = dp[r] - dl_r[r];
+        __builtin_amdgcn_sched_barrier(0);
+        // p is 0 where masked; dP and delta are finite
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] *= x[r];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) pds[r >> 3][(r & 7) >> 1] = pack_bf16x2(t[r], t[r + 1]);
       };
-      if (full) p_ds(std::true_type{});
-      else p_ds(std::false_type{});
-      wait_all_loads();
+      if (code == kPairFull) p_ds(std::integral_constant<int, kPairFull>{});
+      else if (code == kPairOneSeg) p_ds(std::integral_constant<int, kPairOneSeg>{});
+      else if (code == kPairMasked) p_ds(std::integral_constant<int, kPairMasked>{});
+      const int po = p_slot(step & 1);
+      lds_st(smem + po, pp[0]);
+      lds_st(smem + po + 1024, pp[1]);
+      lds_st(smem + po + 2048, pds[0]);
+      lds_st(smem + po + 3072, pds[1]);
       wg_barrier();
       b = bn;
     }
@@ -565,7 +555,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
     wg_barrier();  // the consumers' sums
   };
 
-  // Consumer: one step behind its producer.
+  // Consumer: stages the pairs one step ahead and accumulates one step
+  // behind its producer.
   auto consume = [&]() {
     f32x16 dk[MD], dv[MD];
 #pragma unroll
@@ -607,26 +598,104 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, Plan qp, co
       });
     };
 
+    // Staging: this wave loads half kb of the pair of parity hp (Q and dout
+    // loads kb NLD .. +NLD - 1 of each tile; lse and delta for half 0,
+    // positions and segments for half 1); half 0 also writes the pair's
+    // code (classify).
+    // Lane offsets of the tile loads: row r of the LDS tile holds query
+    // kappa(r); rows past a partial tile's end lie past the descriptor's
+    // range and load zeros.
+    const int row_bytes = a.heads * D * 2;
+    int voff[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int p = 64 * (kb * NLD + j) + lane;
+      const int row = p / SQT::kChunks, pc = p % SQT::kChunks;
+      voff[j] = kappa(row) * row_bytes + ((pc ^ SQT::swz(row)) << 4);
+    }
+    const int moff = lane >= 32 ? 0x40000000 : kb == 0 ? lane * a.heads * 4 : lane * 4;
+    const TileSum ks_sum = ld_const(ksum, kt);
+    // The pair of this parity for the step being staged: index np, query
+    // tile rng.x + lq, head kh G + lh (lq = np / G, lh = np % G, advanced
+    // two pairs at a time).
+    int np = hp, lq = G == 1 ? hp : 0, lh = G == 1 ? 0 : hp;
+    int st_qt = 0;
+    bool st_valid = false;
+    auto stage = [&](int b) {
+      // A slot past the last pair stages the last pair again (its code
+      // makes the producer's P zero), so every step has the same body.
+      const bool valid = np < n_pairs;
+      int sq = lq, sh = lh;
+      if (!valid) {
+        if (sh == 0) {
+          sq -= 1;
+          sh = G - 1;
+        } else {
+          sh -= 1;
+        }
+      }
+      const int qt = rng.x + sq, h = kh * G + sh;
+      const int n_rows = min(32, P - qt * 32);
+      const uint32_t base = lds0 + b * stageBytes + hp * pairBytes;
+      const long long r0 = (long long)qt * 32 * a.heads + h;
+      const int nrec = (n_rows - 1) * row_bytes + 2 * D;
+      const i32x4 rq = raw_rsrc(static_cast<const uint16_t*>(a.q) + r0 * D, nrec);
+      const i32x4 rg = raw_rsrc(static_cast<const uint16_t*>(a.dout) + r0 * D, nrec);
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const uint32_t dst = base + 1024 * (kb * NLD + j);
+        lds_dma<16>(rq, dst, voff[j]);
+        lds_dma<16>(rg, dst + qTile, voff[j]);
+      }
+      const uint32_t mdst = base + 2 * qTile + 512 * kb;
+      if (kb == 0) {
+        const int nm = 4 * ((n_rows - 1) * a.heads + 1);
+        lds_dma<4>(raw_rsrc(lse2 + r0, nm), mdst, moff);
+        lds_dma<4>(raw_rsrc(delta + r0, nm), mdst + 256, moff);
+      } else {
+        lds_dma<4>(raw_rsrc(a.positions + (long long)qt * 32, 4 * n_rows), mdst, moff);
+        lds_dma<4>(raw_rsrc(a.segments + (long long)qt * 32, 4 * n_rows), mdst + 256, moff);
+      }
+      st_qt = qt;
+      st_valid = valid;
+      np += 2;
+      lh += 2;
+      while (lh >= G) {
+        lh -= G;
+        ++lq;
+      }
+    };
+    // The code of the pair staged last (half-0 waves; after this wave's
+    // matrix work, so the scalar load's wait holds up no LDS reads).
+    auto classify = [&](int b) {
+      if (kb != 0) return;
+      int code = kPairSkip;
+      if (st_valid) {
+        const TileSum q_sum = ld_const(qp.qsum, st_qt);
+        if (tiles_meet(q_sum, ks_sum, a.window))
+          code = tiles_full(q_sum, ks_sum, kt, P, a.window) && (st_qt + 1) * 32 <= P ? kPairFull
+                 : tiles_oneseg(q_sum, ks_sum, kt, P)                                ? kPairOneSeg
+                                                                                     : kPairMasked;
+      }
+      lds_st(smem + code_at(b, hp), code);
+    };
+
     // Stages form a ring of three: step s of the producers reads stage
     // s % 3 and this wave stage (s - 1) % 3, while the pairs of step s + 1
     // load into stage (s + 1) % 3, last read in step s - 1. P and dS of step
-    // s sit in P buffer s % 2. A step's second slot past the last pair
-    // stages that last pair again (its products are masked to zero), so
-    // every step runs the same straight-line body.
+    // s sit in P buffer s % 2.
     if (n_steps > 0) {
-      load_pair(0, 0, 0);
-      load_pair(min(1, n_pairs - 1), 1, 0);
+      stage(0);
+      classify(0);
       wait_all_loads();
       wg_barrier();
     }
     int b = 0;
     for (int step = 0; step < n_steps; ++step) {
       const int bn = b == 2 ? 0 : b + 1, bp = b == 0 ? 2 : b - 1;
-      if (step + 1 < n_steps) {
-        load_pair(2 * step + 2, 0, bn);
-        load_pair(min(2 * step + 3, n_pairs - 1), 1, bn);
-      }
+      if (step + 1 < n_steps) stage(bn);
       if (step > 0) accumulate(smem + bp * stageBytes + hp * pairBytes, (step - 1) & 1);
+      if (step + 1 < n_steps) classify(bn);
       wait_all_loads();
       wg_barrier();
       b = bn;
