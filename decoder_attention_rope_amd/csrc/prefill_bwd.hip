@@ -287,33 +287,45 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, Plan pl, cons
       // 16 bytes at a time (a masked tile only). One copy of this code for
       // fully-allowed tiles and one for masked tiles, so the branch on
       // `full` is taken once per half tile rather than once per element.
+      // The element work runs in fenced phases of 16 independent
+      // operations (the compiler otherwise chains it element by element and
+      // waits out each result's latency).
       u32x4 dsw[2];
       auto ds_of = [&](auto full_c) {
         constexpr bool FULL = decltype(full_c)::value;
+        u32x4 kpw[4] = {}, ksw[4] = {};
+        if constexpr (!FULL) {
 #pragma unroll
-        for (int r4 = 0; r4 < 16; r4 += 4) {
-          const int j0 = 32 * hb + 16 * (r4 >> 3) + 8 * hf + (r4 & 7);
-          u32x4 kpw = {}, ksw = {};
-          if constexpr (!FULL) {
-            kpw = lds_ld<u32x4>(pb + j0 * 4);
-            ksw = lds_ld<u32x4>(pb + 256 + j0 * 4);
-          }
-#pragma unroll
-          for (int r = r4; r < r4 + 4; r += 2) {
-            float ds2[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int j = j0 + (r + e - r4);
-              bool ok = true;
-              if constexpr (!FULL)
-                ok = ((int)ksw[r + e - r4] == my_seg) & ((int)kpw[r + e - r4] <= my_pos) &
-                     ((uint32_t)my_pos - kpw[r + e - r4] <= wlast) & (j < n_j);
-              const float p = ok ? fast_exp2(__builtin_fmaf(s[r + e], scale_log2, -lse2)) : 0.f;
-              ds2[e] = p * (dp[r + e] - dlt);
-            }
-            dsw[r >> 3][(r & 7) >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+          for (int c = 0; c < 4; ++c) {
+            const int j0 = 32 * hb + 16 * (c >> 1) + 8 * hf + 4 * (c & 1);
+            kpw[c] = lds_ld<u32x4>(pb + j0 * 4);
+            ksw[c] = lds_ld<u32x4>(pb + 256 + j0 * 4);
           }
         }
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], scale_log2, -lse2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = fast_exp2(x[r]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!FULL) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = 32 * hb + 16 * (r >> 3) + 8 * hf + (r & 7);
+            const uint32_t kp = kpw[r >> 2][r & 3], kq = ksw[r >> 2][r & 3];
+            const bool ok = ((int)kq == my_seg) & ((int)kp <= my_pos) & ((uint32_t)my_pos - kp <= wlast) & (j < n_j);
+            x[r] = ok ? x[r] : 0.f;
+          }
+        }
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] = dp[r] - dlt;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] *= x[r];  // x is 0 where masked; dP and delta are finite
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) dsw[r >> 3][(r & 7) >> 1] = pack_bf16x2(t[r], t[r + 1]);
       };
       if (full) ds_of(std::true_type{});
       else ds_of(std::false_type{});
