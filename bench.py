@@ -10,7 +10,10 @@ workloads, with all inputs resident in HBM:
   3. gqa_decode_paged   paged decode, 64 rows, context lengths U[512, 8192]
   4. gqa_rope_write_kv  rope + KV write of 16384 packed tokens (cache row =
                         segment)
-  5. gqa_prefill_packed packed prefill, 16384 tokens, segments U[64, 4096]
+  5. gqa_prefill_packed packed prefill, 16384 tokens, segments U[64, 4096]:
+                        its plan (gqa_prefill_packed_plan, from positions and
+                        segments only) on a second stream during stages 1-4,
+                        then gqa_prefill_packed_planned
 
 Each stage is bracketed by HIP events on the stream it is launched on. The
 JSON line reports the paged-decode KV bandwidth as `value` (GB/s), the
@@ -545,8 +548,22 @@ def main():
     names = ["rope_table", "rope_write_decode", "decode_paged", "rope_write_prefill",
              "prefill_packed"]
 
-    def step(ev):
+    # The packed prefill's plan depends only on the prefill tokens' positions
+    # and segments: each step builds it on a second stream (default priority)
+    # while the decode runs, after the previous step's prefill has read it,
+    # and the prefill waits for it.
+    side = torch.cuda.Stream()
+    plan_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    plan_ms = []
+
+    def step(ev, timing=False):
         ev[0].record(stream)
+        side.wait_event(ev[0])
+        with torch.cuda.stream(side):
+            if timing:
+                ev[6].record(side)
+            gqa.gqa_prefill_packed_plan(P, H, KVH, D, 0, p_pos, p_seg, p_ws, pws_n)
+            ev[7].record(side)
         gqa.gqa_rope_table(D, max_pos, theta, gqa.GQA_BF16, rope_tab)
         ev[1].record(stream)
         gqa.gqa_rope_write_kv(rows, H, KVH, D, gqa.GQA_BF16, dq, dk, dv, d_pos, rope_tab, max_pos,
@@ -560,12 +577,13 @@ def main():
                               gqa.GQA_CACHE_CONTIGUOUS, p_cache_k, p_cache_v, nseg, cache_len,
                               p_seg, None, None, 0, 0)
         ev[4].record(stream)
-        gqa.gqa_prefill_packed(P, H, KVH, D, gqa.GQA_BF16, 0.0, 0, None, pq, pk, pv, p_pos, p_seg,
-                               p_out, p_ws, pws_n)
+        stream.wait_event(ev[7])
+        gqa.gqa_prefill_packed_planned(P, H, KVH, D, gqa.GQA_BF16, 0.0, 0, None, pq, pk, pv, p_pos,
+                                       p_seg, p_out, p_ws, pws_n)
         ev[5].record(stream)
 
     def new_events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        return [torch.cuda.Event(enable_timing=True) for _ in range(8)]
 
     for _ in range(args.warmup):
         step(new_events())
@@ -573,8 +591,9 @@ def main():
     evs = [new_events() for _ in range(args.steps)]
     t0 = time.perf_counter()
     for ev in evs:
-        step(ev)
+        step(ev, timing=True)
     torch.cuda.synchronize()
+    plan_us = float(np.mean([ev[6].elapsed_time(ev[7]) for ev in evs])) * 1e3
     wall = time.perf_counter() - t0
     per_op_ms = {n: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in evs]))
                  for i, n in enumerate(names)}
@@ -615,9 +634,15 @@ def main():
                         "bf16 matrices"}
     del ma, mb, xor_word
 
-    def prefill_only():
+    def prefill_entry():
         gqa.gqa_prefill_packed(P, H, KVH, D, gqa.GQA_BF16, 0.0, 0, None, pq, pk, pv, p_pos, p_seg,
                                p_out, p_ws, pws_n)
+
+    # The one-call entry (plan and attention on one stream), for comparison.
+    entry_s = timed_median(prefill_entry, 20)
+
+    def prefill_only():
+        prefill_entry()
         torch.cuda.synchronize()
     clocks_prefill = clocks_under_load(prefill_only)
 
@@ -803,7 +828,12 @@ def main():
     pre_roof = {"bound": "mfma", "achieved": prefill_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": prefill_tflops / MFMA_BF16_PEAK_TFLOPS,
                 "traffic": traffic_for("prefill_packed", PREFILL_SOURCES),
-                "algorithmic_flops": prefill_flops, "avg_us": pre_s * 1e6}
+                "algorithmic_flops": prefill_flops, "avg_us": pre_s * 1e6,
+                "plan_us_on_second_stream": plan_us, "entry_call_us": entry_s * 1e6,
+                "entry_call_frac": prefill_flops / entry_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                "note": "avg_us: gqa_prefill_packed_planned in the step (its plan built on a second "
+                        "stream during the decode, plan_us_on_second_stream); entry_call_us: the "
+                        "one-call gqa_prefill_packed (plan + attention) timed alone"}
     dominant = "prefill_packed" if pre_s >= dec_s else "decode_paged"
     roof = dict(pre_roof if dominant == "prefill_packed" else dec_roof)
     roof["kernel"] = dominant

@@ -20,6 +20,7 @@ __all__ = [
     "GQA_BF16", "GQA_F32", "GQA_CACHE_NONE", "GQA_CACHE_CONTIGUOUS", "GQA_CACHE_PAGED_TABLE",
     "GQA_CACHE_PAGED_SLOTS", "GQA_PAGE_SIZE",
     "gqa_rope_table", "gqa_rope_write_kv", "gqa_prefill_packed", "gqa_prefill_packed_workspace",
+    "gqa_prefill_packed_plan", "gqa_prefill_packed_planned",
     "gqa_prefill_cached", "gqa_prefill_cached_workspace", "gqa_step_packed",
     "gqa_step_packed_workspace", "gqa_step_paged", "gqa_step_paged_workspace",
     "gqa_qkv_rope_write", "gqa_prefill_packed_lse", "gqa_prefill_packed_backward",
@@ -71,6 +72,11 @@ _prefill_packed = _sig("gqa_prefill_packed", ctypes.c_int,
                        [_i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                         _vp, _vp, _sz, _vp])
 _prefill_ws = _sig("gqa_prefill_packed_workspace", _sz, [_i32, _i32, _i32, _i32])
+_prefill_plan = _sig("gqa_prefill_packed_plan", ctypes.c_int,
+                     [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
+_prefill_planned = _sig("gqa_prefill_packed_planned", ctypes.c_int,
+                        [_i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                         _vp, _vp, _sz, _vp])
 _prefill_lse = _sig("gqa_prefill_packed_lse", ctypes.c_int,
                     [_i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32] + [_vp] * 7 +
                     [_vp, _sz, _vp])
@@ -212,6 +218,21 @@ def gqa_prefill_packed(p, heads, kv_heads, head_dim, dtype, scale, window, sinks
                            _ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(segments), _ptr(out),
                            _ptr(workspace), workspace_bytes, _stream(stream)),
            "gqa_prefill_packed")
+
+
+def gqa_prefill_packed_plan(p, heads, kv_heads, head_dim, window, positions, segments, workspace,
+                            workspace_bytes, stream=None):
+    _check(_prefill_plan(p, heads, kv_heads, head_dim, window, _ptr(positions), _ptr(segments),
+                         _ptr(workspace), workspace_bytes, _stream(stream)),
+           "gqa_prefill_packed_plan")
+
+
+def gqa_prefill_packed_planned(p, heads, kv_heads, head_dim, dtype, scale, window, sinks, q, k, v,
+                               positions, segments, out, workspace, workspace_bytes, stream=None):
+    _check(_prefill_planned(p, heads, kv_heads, head_dim, dtype, scale, window, _ptr(sinks),
+                            _ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(segments), _ptr(out),
+                            _ptr(workspace), workspace_bytes, _stream(stream)),
+           "gqa_prefill_packed_planned")
 
 
 def gqa_prefill_packed_lse(p, heads, kv_heads, head_dim, dtype, scale, window, q, k, v,

@@ -230,17 +230,22 @@ size_t gqa_prefill_packed_workspace(int32_t p, int32_t heads, int32_t kv_heads,
   return gqa::prefill_workspace_bytes(p, heads, kv_heads, head_dim);
 }
 
+// What a packed prefill call launches: plan and attention, the plan alone,
+// or the attention alone on a plan already in the workspace.
+enum class PackedPart { kAll, kPlan, kPlanned };
+
 static int prefill_packed_impl(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
                                int32_t dtype, float scale, int32_t window, const void* sinks,
                                const void* q, const void* k, const void* v,
                                const int32_t* positions, const int32_t* segments, void* out,
-                               void* workspace, size_t workspace_bytes, void* stream, bool launch) {
+                               void* workspace, size_t workspace_bytes, void* stream, bool launch,
+                               PackedPart part = PackedPart::kAll) {
   if (p < 0 || window < 0) return GQA_ERR_INVALID_ARG;
   int st = check_heads(heads, kv_heads, head_dim, dtype);
   if (st != GQA_OK) return st;
   if (!std::isfinite(scale) || scale < 0.0f) return GQA_ERR_INVALID_ARG;
-  if (q == nullptr || k == nullptr || v == nullptr || positions == nullptr ||
-      segments == nullptr || out == nullptr)
+  if (positions == nullptr || segments == nullptr) return GQA_ERR_INVALID_ARG;
+  if (part != PackedPart::kPlan && (q == nullptr || k == nullptr || v == nullptr || out == nullptr))
     return GQA_ERR_INVALID_ARG;
   if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
   // Each KV head's K (and V) is addressed through one 32-bit buffer range.
@@ -268,7 +273,26 @@ static int prefill_packed_impl(int32_t p, int32_t heads, int32_t kv_heads, int32
   a.ws = workspace;
   a.ws_bytes = workspace_bytes;
   a.src = gqa::kSrcPacked;
-  return hip_status(gqa::launch_prefill(a, static_cast<hipStream_t>(stream)));
+  if (part == PackedPart::kPlan) return hip_status(gqa::launch_prefill_plan(a, static_cast<hipStream_t>(stream)));
+  return hip_status(gqa::launch_prefill(a, static_cast<hipStream_t>(stream), part == PackedPart::kPlanned));
+}
+
+int gqa_prefill_packed_plan(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                            int32_t window, const int32_t* positions, const int32_t* segments,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_packed_impl(p, heads, kv_heads, head_dim, GQA_BF16, 0.0f, window, nullptr, nullptr,
+                             nullptr, nullptr, positions, segments, nullptr, workspace, workspace_bytes,
+                             stream, !g_dry_run, PackedPart::kPlan);
+}
+
+int gqa_prefill_packed_planned(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                               int32_t dtype, float scale, int32_t window, const void* sinks,
+                               const void* q, const void* k, const void* v,
+                               const int32_t* positions, const int32_t* segments, void* out,
+                               const void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_packed_impl(p, heads, kv_heads, head_dim, dtype, scale, window, sinks, q, k, v,
+                             positions, segments, out, const_cast<void*>(workspace), workspace_bytes,
+                             stream, !g_dry_run, PackedPart::kPlanned);
 }
 
 int gqa_prefill_packed(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,

@@ -120,7 +120,11 @@ int decode_mfma_split_len(int rows, int kv_heads, int cap);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 
 size_t prefill_workspace_bytes(int p, int heads, int kv_heads, int head_dim);
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// The prefill (plan, then attention; with `planned` the attention alone, on
+// the plan a launch_prefill_plan of the same p, heads, kv_heads, window,
+// positions and segments left in a.ws).
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, bool planned = false);
+hipError_t launch_prefill_plan(const PrefillArgs& a, hipStream_t stream);
 // A cached paged prefill and a one-split matrix-core paged decode (bf16,
 // G <= 16, same head dim) in one grid; `d` needs no workspace.
 hipError_t launch_prefill_step(const PrefillArgs& a, DecodeArgs d, hipStream_t stream);

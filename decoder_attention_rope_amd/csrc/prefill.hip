@@ -1195,7 +1195,8 @@ static int device_cu_count() {
   return cus[dev];
 }
 
-hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream, int waves) {
+// The plan's shape and its arrays' places in the workspace (host only).
+static void prefill_layout(const PrefillArgs& a, Plan& pl, int waves) {
   const int G = a.heads / a.kv_heads;
   pl.gw = group_width(G);
   pl.head_groups = G / pl.gw;
@@ -1227,7 +1228,10 @@ hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream, i
                ? reinterpret_cast<int*>(reinterpret_cast<char*>(pl.nfull) + align256(n_qt_max * sizeof(int)))
                : nullptr;
   (void)n_kt_max;
+}
 
+hipError_t prefill_prepare(const PrefillArgs& a, Plan& pl, hipStream_t stream, int waves) {
+  prefill_layout(a, pl, waves);
   const int n_tiles = pl.n_kt + pl.n_qt;
   prefill_summarize_kernel<<<dim3((n_tiles + 3) / 4), dim3(256), 0, stream>>>(a, pl);
   hipError_t e = hipGetLastError();
@@ -1278,10 +1282,19 @@ hipError_t launch_prefill_step(const PrefillArgs& a, DecodeArgs d, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_prefill_plan(const PrefillArgs& a, hipStream_t stream) {
   Plan pl;
-  const hipError_t e = prefill_prepare(a, pl, stream);
-  if (e != hipSuccess) return e;
+  return prefill_prepare(a, pl, stream);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream, bool planned) {
+  Plan pl;
+  if (planned) {
+    prefill_layout(a, pl, 0);
+  } else {
+    const hipError_t e = prefill_prepare(a, pl, stream);
+    if (e != hipSuccess) return e;
+  }
   if (a.head_dim == 64) {
     if (pl.gw == 4) launch_main<64, 4>(a, pl, stream);
     else if (pl.gw == 2) launch_main<64, 2>(a, pl, stream);

@@ -196,6 +196,36 @@ size_t gqa_prefill_packed_workspace(int32_t p, int32_t heads, int32_t kv_heads,
                                     int32_t head_dim);
 
 /*
+ * gqa_prefill_packed_plan / gqa_prefill_packed_planned -- gqa_prefill_packed
+ * in two calls. Which key tiles each query tile visits follows from the
+ * `own` mask of `packed<P>` (the Linnet "examples/01-llama" page,
+ * src/attention.linnet `packed`) alone, i.e. from positions, segments and the
+ * window, which every layer of a model shares; so the plan can be built
+ * once per batch, or on another stream while earlier work runs.
+ *   gqa_prefill_packed_plan writes the plan (tile summaries, visit lists,
+ *   costliest-first schedule) into the workspace (at least
+ *   gqa_prefill_packed_workspace(p, heads, kv_heads, head_dim) bytes,
+ *   256-byte aligned). It reads positions and segments [p] only.
+ *   gqa_prefill_packed_planned takes the arguments of gqa_prefill_packed and
+ *   only reads the workspace: it computes the same out, bit for bit, as
+ *   gqa_prefill_packed, provided the workspace holds a plan built for the
+ *   same p, heads, kv_heads, head_dim, window and the same positions and
+ *   segments contents, and that build has finished on the device (same
+ *   stream, or an event between streams). Any number of planned calls, on
+ *   any q, k, v, may share one plan; nothing checks that a plan matches.
+ *   Errors as gqa_prefill_packed (positions, segments, workspace checked by
+ *   both calls; q, k, v, out by the planned call).
+ */
+int gqa_prefill_packed_plan(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                            int32_t window, const int32_t* positions, const int32_t* segments,
+                            void* workspace, size_t workspace_bytes, void* stream);
+int gqa_prefill_packed_planned(int32_t p, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                               int32_t dtype, float scale, int32_t window, const void* sinks,
+                               const void* q, const void* k, const void* v,
+                               const int32_t* positions, const int32_t* segments, void* out,
+                               const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gqa_prefill_packed_lse -- gqa_prefill_packed for training: the same
  * attention (no sinks), and also each (token, head)'s natural-log softmax
  * denominator lse = ln sum_j exp(scale <q_i, k_j>) over the keys the `own`

@@ -166,6 +166,28 @@ def test_entry_point_argument_checks(g):
             8, 8, 256, 10 ** 12)
 
 
+def test_prefill_plan_argument_checks(g):
+    bad_arg, unsup, ws_err = _codes(g)
+    # the plan needs positions, segments and a workspace; q, k, v, out are not read
+    _expect(g, g.GQA_OK, g.gqa_prefill_packed_plan, 10, 8, 8, 64, 0, 8, 8, 256, 10 ** 6)
+    _expect(g, bad_arg, g.gqa_prefill_packed_plan, 10, 8, 8, 64, 0, None, 8, 256, 10 ** 6)
+    _expect(g, bad_arg, g.gqa_prefill_packed_plan, 10, 8, 8, 64, -1, 8, 8, 256, 10 ** 6)
+    _expect(g, ws_err, g.gqa_prefill_packed_plan, 10, 8, 8, 64, 0, 8, 8, 256, 16)
+    _expect(g, ws_err, g.gqa_prefill_packed_plan, 10, 8, 8, 64, 0, 8, 8, 257, 10 ** 6)
+    _expect(g, unsup, g.gqa_prefill_packed_plan, 10, 8, 8, 96, 0, 8, 8, 256, 10 ** 6)
+    # the planned call checks what gqa_prefill_packed checks
+    _expect(g, g.GQA_OK, g.gqa_prefill_packed_planned, 10, 8, 8, 64, 0, 0.0, 0, None, 8, 8, 8, 8, 8,
+            8, 256, 10 ** 6)
+    _expect(g, bad_arg, g.gqa_prefill_packed_planned, 10, 8, 8, 64, 0, 0.0, 0, None, 8, 8, 8, 8, 8,
+            None, 256, 10 ** 6)
+    _expect(g, unsup, g.gqa_prefill_packed_planned, 10, 8, 8, 64, 1, 0.0, 0, None, 8, 8, 8, 8, 8,
+            8, 256, 10 ** 6)
+    _expect(g, ws_err, g.gqa_prefill_packed_planned, 10, 8, 8, 64, 0, 0.0, 0, None, 8, 8, 8, 8, 8,
+            8, None, 0)
+    _expect(g, g.GQA_OK, g.gqa_prefill_packed_planned, 0, 8, 8, 64, 0, 0.0, 0, None, 8, 8, 8, 8, 8,
+            8, None, 0)
+
+
 def test_prefill_cached_argument_checks(g):
     bad_arg, unsup, ws_err = _codes(g)
     cont, paged = g.GQA_CACHE_CONTIGUOUS, g.GQA_CACHE_PAGED_TABLE

@@ -47,6 +47,39 @@ def test_prefill_packed_ragged(heads, kvh, d, window, use_sinks):
     assert_close(f64(out), ref, "bf16", f"prefill ragged P={len(pos)}")
 
 
+@pytest.mark.parametrize("heads,kvh,d,window,use_sinks", [(32, 8, 128, 0, False), (8, 8, 64, 37, True),
+                                                          (16, 2, 64, 0, True)])
+def test_prefill_plan_once_run_twice(heads, kvh, d, window, use_sinks):
+    """One plan (built on a second stream, handed over by an event) serves two
+    layers' q, k, v; each planned output equals gqa_prefill_packed bit for bit,
+    and the first also the oracle."""
+    print(f"[case] prefill plan reuse H={heads} KvH={kvh} D={d} W={window} sinks={use_sinks}", flush=True)
+    g0 = W.streams(2100 + heads + d)
+    lengths, pos, seg = W.segment_layout(700, 1, 300, g0["index"])
+    p = len(pos)
+    layers = [make_inputs(2100 + heads + d + 17 * i, p, heads, kvh, d) for i in range(2)]
+    ws, nb = workspace(gqa.gqa_prefill_packed_workspace(p, heads, kvh, d))
+    pos_d, seg_d = i32(pos), i32(seg)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        gqa.gqa_prefill_packed_plan(p, heads, kvh, d, window, pos_d, seg_d, ws, nb)
+        built = torch.cuda.Event()
+        built.record(side)
+    torch.cuda.current_stream().wait_event(built)
+    for i, (dv_, hv, (sk, sk64), _) in enumerate(layers):
+        sinks = sk if use_sinks else None
+        out = torch.full((p, heads, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+        gqa.gqa_prefill_packed_planned(p, heads, kvh, d, gqa.GQA_BF16, 0.0, window, sinks, *dv_, pos_d,
+                                       seg_d, out, ws, nb)
+        torch.cuda.synchronize()
+        fused = run_prefill(*dv_, pos, seg, heads, kvh, d, window, sinks)
+        assert np.array_equal(bits(out), bits(fused)), f"layer {i}: planned != fused"
+        if i == 0:
+            ref = oracle.default().packed(*hv, pos, seg, window=window, sinks=sk64 if use_sinks else None)
+            assert_close(f64(out), ref, "bf16", f"planned prefill P={p}")
+
+
 def test_prefill_tiny_llama_example():
     wl = W.TINY_LLAMA
     s = wl.extra["prefill"]
