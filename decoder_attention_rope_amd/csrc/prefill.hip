@@ -1130,23 +1130,27 @@ __global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) 
 // One step of step_paged in a single grid: the first n_dec workgroups each
 // decode one (decode row, KV head) over its whole key range -- one split, so
 // they write the output themselves -- and the rest are the chunk's prefill
-// workgroups in their usual order. The decode shares start first and stream
-// the cache (each wavefront loading its next chunk while it computes the
-// current one) while the prefill tiles keep the matrix cores busy. Measured
-// alternatives were slower: the decode shares last in the grid, and rows
-// split into 1024- or 2048-key pieces (more workgroups plus a merge pass).
+// workgroups in their usual order. The decode shares take workgroup ids
+// [dec0, dec0 + n_dec): the costliest prefill tiles (the first in their
+// order) start before them, and they stream the cache (each wavefront loading
+// its next chunk while it computes the current one) while the remaining
+// prefill tiles keep the matrix cores busy, finishing long before the grid's
+// tail. Measured alternatives were slower: the decode shares first or last in
+// the grid, and rows split into 1024- or 2048-key pieces (more workgroups
+// plus a merge pass).
 template <int D, int GW>
-__global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) void step_paged_kernel(PrefillArgs a, Plan pl, DecodeArgs d, int n_dec) {
+__global__ __launch_bounds__(64 * prefill_waves<GW>(), 8 / prefill_waves<GW>()) void step_paged_kernel(PrefillArgs a, Plan pl, DecodeArgs d, int n_dec, int dec0) {
   constexpr int NW = prefill_waves<GW>();
   constexpr int kPre = Lds<D, prefill_ahead<GW>() + 1, 4>::total;
   constexpr int kDec = decode_mfma_lds_bytes<D, NW>();
   __shared__ __attribute__((aligned(16))) char smem_raw[kPre > kDec ? kPre : kDec];
   const int bid = blockIdx.x;
-  if (bid < n_dec) {
-    decode_mfma_body<D, true, NW, false, true>(d, 0, bid % d.kv_heads, bid / d.kv_heads, smem_raw);
+  if (bid >= dec0 && bid < dec0 + n_dec) {
+    const int db = bid - dec0;
+    decode_mfma_body<D, true, NW, false, true>(d, 0, db % d.kv_heads, db / d.kv_heads, smem_raw);
     return;
   }
-  prefill_body<D, GW, kSrcPaged>(a, pl, bid - n_dec, smem_raw);
+  prefill_body<D, GW, kSrcPaged>(a, pl, bid < dec0 ? bid : bid - n_dec, smem_raw);
 }
 
 // ---------------------------------------------------------------------------
@@ -1259,8 +1263,14 @@ static void launch_step(const PrefillArgs& a, const Plan& pl, const DecodeArgs& 
                         hipStream_t stream) {
   const int n_groups = a.kv_heads * pl.head_groups;
   const int n_dec = d.rows * d.kv_heads;
-  const dim3 grid(n_dec + pl.n_qt * n_groups), block(64 * prefill_waves<GW>());
-  step_paged_kernel<D, GW><<<grid, block, 0, stream>>>(a, pl, d, n_dec);
+  const int n_pre = pl.n_qt * n_groups;
+  // The decode shares follow half the prefill tiles, at most three
+  // workgroups per compute unit of them (1.5 residencies of two per CU).
+  const int cus = device_cu_count();
+  const int cap = 3 * (cus > 0 ? cus : 256);
+  const int dec0 = n_pre / 2 < cap ? n_pre / 2 : cap;
+  const dim3 grid(n_dec + n_pre), block(64 * prefill_waves<GW>());
+  step_paged_kernel<D, GW><<<grid, block, 0, stream>>>(a, pl, d, n_dec, dec0);
 }
 
 hipError_t launch_prefill_step(const PrefillArgs& a, DecodeArgs d, hipStream_t stream) {
