@@ -406,8 +406,9 @@ size_t gqa_step_packed_workspace(int32_t batch, int32_t p, int32_t heads, int32_
  *   [rows]. bf16 only. workspace: gqa_step_paged_workspace(...) bytes,
  *   256-byte aligned.
  * With up to 16 query heads per KV head the decode tokens and the chunk run
- * as one grid (decode workgroups first), so the decode's cache reads overlap
- * the chunk's matrix work; otherwise the decode runs first, then the chunk.
+ * as one grid (decode workgroups after the first half of the prefill tiles),
+ * so the decode's cache reads overlap the chunk's matrix work; otherwise the
+ * decode runs first, then the chunk.
  */
 int gqa_step_paged(int32_t p, int32_t rows, int32_t pages, int32_t heads, int32_t kv_heads,
                    int32_t head_dim, int32_t dtype, float scale, int32_t window, const void* sinks,

@@ -53,8 +53,9 @@ def test_step_packed(heads, kvh, d, window, use_sinks):
 
 
 # Up to 16 query heads per KV head the decode tokens run in the same grid as
-# the chunk (matrix-core decode workgroups first); with more (G = 32 here) the
-# decode runs as its own vector-ALU pass before the chunk.
+# the chunk (matrix-core decode workgroups placed after the first half of the
+# prefill tiles); with more (G = 32 here) the decode runs as its own
+# vector-ALU pass before the chunk.
 @pytest.mark.parametrize("heads,kvh,d,window,use_sinks,bad_page", [
     (32, 8, 128, 0, False, False), (64, 8, 64, 0, False, False),
     (64, 8, 64, 128, True, True), (32, 2, 128, 300, False, True), (32, 1, 64, 0, True, False)])
